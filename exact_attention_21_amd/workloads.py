@@ -1,0 +1,110 @@
+"""Seeded synthetic workloads: shapes, value distributions and rounding to fp16/bf16.
+
+This module holds no attention arithmetic.  It only draws the random inputs and
+rounds them to the storage dtype; both the GPU path and the CPU oracle consume
+what it returns.  It imports numpy only.
+
+The five workloads are the attention-forward shapes the method is measured on:
+a tiny correctness case, the 8-head N=8192 d=64 fp16 headline shape, a causal
+training-style d=128 bf16 shape, a long-context causal N=32768 shape and a
+d=256 bf16 shape with a ragged length and a wide score range.
+
+Draw recipe (one generator per call): ``numpy.random.default_rng(seed)``
+(PCG64); Q, then K, then V, each drawn as one float64 array of shape
+[B, H, N, d] in C order.  "normal" is ``standard_normal() * sigma``;
+"uniform" is ``uniform(-1, 1)``.  fp16 rounding is numpy's float64 -> float16
+cast (round to nearest even).  bf16 rounding is float64 -> float32 (numpy, round
+to nearest even) followed by round-to-nearest-even of the float32 bit pattern to
+its upper 16 bits.  Upcasting the rounded values to float64 is exact.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+FP16 = "fp16"
+BF16 = "bf16"
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str
+    causal: bool
+    q_dist: tuple = ("normal", 1.0)
+    k_dist: tuple = ("normal", 1.0)
+    v_dist: tuple = ("normal", 1.0)
+    scale: float = field(default=None)
+
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / float(np.sqrt(self.d))
+
+    def flops(self) -> float:
+        """Nominal forward FLOPs of the metric: 4*B*H*N^2*d, halved when causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2.0 if self.causal else f
+
+    def describe(self) -> dict:
+        return {"B": self.B, "H": self.H, "N": self.N, "d": self.d, "dtype": self.dtype,
+                "causal": self.causal, "scale": self.softmax_scale()}
+
+
+TINY = Workload("tiny_b1h1n128d64_fp16", 1, 1, 128, 64, FP16, False)
+HEADLINE = Workload("headline_b1h8n8192d64_fp16", 1, 8, 8192, 64, FP16, False)
+CAUSAL_TRAIN = Workload("causal_b2h16n4096d128_bf16", 2, 16, 4096, 128, BF16, True)
+LONG_CAUSAL = Workload("longctx_causal_b1h4n32768d64_fp16", 1, 4, 32768, 64, FP16, True)
+WIDE_RAGGED = Workload("wide_ragged_b4h8n2047d256_bf16", 4, 8, 2047, 256, BF16, False,
+                       q_dist=("normal", 3.0), k_dist=("normal", 3.0), v_dist=("uniform", 1.0))
+
+WORKLOADS = [TINY, HEADLINE, CAUSAL_TRAIN, LONG_CAUSAL, WIDE_RAGGED]
+
+
+def _draw(rng: np.random.Generator, shape, dist) -> np.ndarray:
+    kind, width = dist
+    if kind == "normal":
+        return rng.standard_normal(shape) * width
+    if kind == "uniform":
+        return rng.uniform(-width, width, shape)
+    raise ValueError(f"unknown distribution {kind!r}")
+
+
+def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values to the storage dtype.
+
+    Returns float16 values for fp16 and uint16 bf16 bit patterns for bf16.
+    """
+    if dtype == FP16:
+        return np.asarray(x, dtype=np.float64).astype(np.float16)
+    if dtype == BF16:
+        bits = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32)
+        bias = np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))
+        return ((bits + bias) >> np.uint32(16)).astype(np.uint16)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def to_float64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact upcast of storage values (float16, or uint16 bf16 bits) to float64."""
+    if dtype == FP16:
+        return np.asarray(x, dtype=np.float16).astype(np.float64)
+    if dtype == BF16:
+        return (np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_inputs(w: Workload, seed: int = 0, N: int | None = None, B: int | None = None,
+                H: int | None = None):
+    """Draw Q, K, V for a workload (optionally with B, H or N overridden).
+
+    Returns three storage arrays (float16, or uint16 bf16 bits) of shape [B, H, N, d].
+    """
+    shape = (B or w.B, H or w.H, N or w.N, w.d)
+    rng = np.random.default_rng(seed)
+    q = round_to_storage(_draw(rng, shape, w.q_dist), w.dtype)
+    k = round_to_storage(_draw(rng, shape, w.k_dist), w.dtype)
+    v = round_to_storage(_draw(rng, shape, w.v_dist), w.dtype)
+    return q, k, v

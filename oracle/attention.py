@@ -1,0 +1,148 @@
+"""fp64 CPU oracle for the FlashAttention-2 forward pass (test infrastructure).
+
+This module is test infrastructure.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import it.  It shares no code,
+constants or helpers with the HIP library.
+
+Sources (page title, then the part of the page followed):
+
+* "FlashAttention-2 MMA 代码学习" (chuoer47.github.io, leetCUDA study notes),
+  step 0: attention is O = softmax(Q K^T * scale) V; step 1: the online (m, l)
+  merge over key blocks.
+* "第 15 章 FA2 前向：Tiling 与 Online Softmax" (yangyitao.com), §15.1 change 4:
+  the statistic kept per row is the log-sum-exp L = m + log l; §15.3 kernel
+  skeleton: Q, K, V, O are [B, H, N, d], LSE is [B, H, N] fp32, the scale is
+  applied to the scores before the row max, the causal mask hides key j from
+  query i when j > i, a row with no visible key gives O = 0 and LSE = +inf;
+  §15.4.3: masking happens before the softmax.
+
+Precision: every step is fp64.  Inputs are the already-rounded fp16/bf16 values,
+upcast exactly by the caller.  ``scale`` is rounded to fp32 first, because that
+is the value a caller passing a C ``float`` hands to the GPU library.
+
+Every function here is pinned by tests that do not re-use its own formulas
+(tests/test_oracle.py): a pure-Python brute force on tiny shapes, closed forms
+derived by hand (tests/golden/closed_forms.json), invariants (key shift,
+key/value permutation), special cases (one key, identical keys, scale 0) and a
+library routine (torch scaled_dot_product_attention in fp64 on the CPU).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Rows of one (batch, head) handled per matmul.  This only bounds memory: every
+# block computes complete softmax rows, so the result is the plain definition.
+_ROW_BLOCK = 256
+
+
+def _visible_count(i: int, n: int, causal: bool) -> int:
+    """Number of keys visible to query row ``i``.
+
+    Causal reading (yangyitao.com ch.15 §15.3 skeleton, mask step): key j is
+    visible to query i iff j <= i, with queries and keys indexed from 0 in the
+    same sequence (square, top-left aligned).
+    """
+    return i + 1 if causal else n
+
+
+def attention_ref(q, k, v, scale: float, causal: bool, rows=None):
+    """O = softmax(scale * Q K^T [+ causal mask]) V and LSE, straight from the definition.
+
+    Args:
+      q, k, v: float arrays of shape [B, H, N, d]; converted to fp64.
+      scale: softmax scale (a C float on the GPU side, so rounded to fp32 here).
+      causal: hide key j from query i when j > i.
+      rows: optional 1-D integer array of query rows to evaluate (the same rows
+        for every batch and head).  ``None`` means all rows.
+
+    Returns:
+      (O, LSE): O is fp64 [B, H, R, d] and LSE is fp64 [B, H, R], where R is N or
+      len(rows).  LSE is the natural log of the sum over visible keys of
+      exp(scale * q.k) (yangyitao.com ch.15 §15.1 change 4 and §15.3 LSE store).
+      A row with no visible key gets O = 0 and LSE = +inf (§15.3, final
+      normalisation and LSE store); with N >= 1 every row sees at least key 0.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if q.ndim != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    b_, h_, n, d = q.shape
+    c = float(np.float32(scale))
+    if rows is None:
+        rows = np.arange(n)
+    rows = np.asarray(rows, dtype=np.int64)
+    if rows.ndim != 1 or (rows.size and (rows.min() < 0 or rows.max() >= n)):
+        raise ValueError("rows must be a 1-D array of indices in [0, N)")
+    r_ = rows.size
+    out = np.zeros((b_, h_, r_, d), dtype=np.float64)
+    lse = np.full((b_, h_, r_), np.inf, dtype=np.float64)
+    for b in range(b_):
+        for h in range(h_):
+            for r0 in range(0, r_, _ROW_BLOCK):
+                idx = rows[r0:r0 + _ROW_BLOCK]
+                # Keys any row in this block can see.
+                kmax = max(_visible_count(int(i), n, causal) for i in idx)
+                # Scores, with the scale applied before the row max.
+                s = (q[b, h, idx, :] @ k[b, h, :kmax, :].T) * c
+                if causal:
+                    j = np.arange(kmax)[None, :]
+                    s = np.where(j <= idx[:, None], s, -np.inf)
+                m = s.max(axis=1)
+                p = np.exp(s - m[:, None])
+                l = p.sum(axis=1)
+                out[b, h, r0:r0 + idx.size, :] = (p @ v[b, h, :kmax, :]) / l[:, None]
+                lse[b, h, r0:r0 + idx.size] = m + np.log(l)
+    return out, lse
+
+
+def attention_online_merge(q, k, v, scale: float, causal: bool, block: int, reverse: bool = False):
+    """The same result through the pages' online (m, l) merge over key blocks, in fp64.
+
+    Follows "FlashAttention-2 MMA 代码学习" (chuoer47.github.io) step 1: for
+    every key block, take the block's row max, m = max(m_old, m_block),
+    P = exp(S*scale - m), l = exp(m_old - m) * l_old + rowsum(P),
+    O = exp(m_old - m) * O_old + P V; and yangyitao.com ch.15 §15.1 change 4 /
+    §15.3: divide O by l once after the last block, LSE = m + log l, and while a
+    row has seen only masked keys use 0 as the exponent base so that
+    exp(-inf - (-inf)) is never formed.
+
+    ``block`` is the number of keys per block; ``reverse`` walks the blocks from
+    the last to the first.  The result must not depend on either: the tests use
+    that to pin the algebra against ``attention_ref``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b_, h_, n, d = q.shape
+    c = float(np.float32(scale))
+    out = np.zeros_like(q)
+    lse = np.zeros(q.shape[:3], dtype=np.float64)
+    starts = list(range(0, n, block))
+    if reverse:
+        starts = starts[::-1]
+    qi = np.arange(n)[:, None]
+    for b in range(b_):
+        for h in range(h_):
+            m_run = np.full(n, -np.inf)
+            l_run = np.zeros(n)
+            o_run = np.zeros((n, d))
+            for k0 in starts:
+                k1 = min(n, k0 + block)
+                s = (q[b, h] @ k[b, h, k0:k1].T) * c
+                if causal:
+                    kj = np.arange(k0, k1)[None, :]
+                    s = np.where(kj <= qi, s, -np.inf)
+                m_blk = s.max(axis=1)
+                m_new = np.maximum(m_run, m_blk)
+                base = np.where(np.isneginf(m_new), 0.0, m_new)
+                alpha = np.exp(m_run - base)
+                p = np.exp(s - base[:, None])
+                l_run = alpha * l_run + p.sum(axis=1)
+                o_run = alpha[:, None] * o_run + p @ v[b, h, k0:k1]
+                m_run = m_new
+            safe_l = np.where(l_run == 0.0, 1.0, l_run)
+            out[b, h] = o_run / safe_l[:, None]
+            with np.errstate(divide="ignore"):
+                lse[b, h] = np.where(l_run == 0.0, np.inf, m_run + np.log(safe_l))
+    return out, lse

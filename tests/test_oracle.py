@@ -1,0 +1,255 @@
+"""Pins for the fp64 oracle, checked against things other than itself.
+
+* brute force: the literal textbook softmax (exp(s_ij) / sum_k exp(s_ik), no
+  max shift) in pure Python with math.fsum, on tiny shapes;
+* closed forms derived by hand (tests/golden/closed_forms.json);
+* special cases: one key, identical keys, causal row 0, scale 0;
+* invariants: shifting every key by u shifts LSE_i by scale * q_i . u and
+  leaves O unchanged; permuting keys and values together changes nothing;
+* library routines: torch scaled_dot_product_attention in fp64 on the CPU for
+  O, scipy.special.logsumexp for LSE;
+* the method's own algebra: the online (m, l) merge over key blocks of any
+  size, in either order, reaches the same result;
+* planted mistakes in the oracle are caught by the brute-force and
+  closed-form pins.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import attention_online_merge, attention_ref
+import oracle.attention as oracle_mod
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def brute_force(q, k, v, scale, causal):
+    """Pure-Python definition: P_ij = exp(s_ij) / sum_k exp(s_ik) (inputs kept small)."""
+    c = float(np.float32(scale))
+    B, H, N, d = q.shape
+    O = np.zeros((B, H, N, d))
+    L = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                js = range(i + 1) if causal else range(N)
+                e = {j: math.exp(c * math.fsum(float(q[b, h, i, t]) * float(k[b, h, j, t])
+                                              for t in range(d))) for j in js}
+                z = math.fsum(e.values())
+                for t in range(d):
+                    O[b, h, i, t] = math.fsum(e[j] * float(v[b, h, j, t]) for j in js) / z
+                L[b, h, i] = math.log(z)
+    return O, L
+
+
+def _rand(shape, seed, width=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * width
+
+
+TINY_SHAPES = [(1, 1, 1, 1), (1, 1, 2, 4), (2, 1, 3, 8), (1, 2, 17, 4), (2, 2, 5, 1), (1, 1, 17, 8)]
+
+
+def check_brute_force(fn, tol=1e-12):
+    for n_case, shape in enumerate(TINY_SHAPES):
+        for causal in (False, True):
+            q, k, v = (_rand(shape, 10 * n_case + t) for t in range(3))
+            scale = 1.0 / math.sqrt(shape[-1])
+            O, L = fn(q, k, v, scale, causal)
+            Ob, Lb = brute_force(q, k, v, scale, causal)
+            assert np.max(np.abs(O - Ob)) <= tol, (shape, causal)
+            assert np.max(np.abs(L - Lb)) <= tol, (shape, causal)
+
+
+def check_closed_forms(fn, tol=1e-12):
+    cases = json.load(open(GOLDEN))["cases"]
+    for case in cases:
+        q = np.array(case["q"], dtype=np.float64)[None, None]
+        k = np.array(case["k"], dtype=np.float64)[None, None]
+        v = np.array(case["v"], dtype=np.float64)[None, None]
+        for causal, key in ((False, "noncausal"), (True, "causal")):
+            O, L = fn(q, k, v, case["scale"], causal)
+            assert np.max(np.abs(O[0, 0] - np.array(case[key]["O"]))) <= tol, (case["name"], key)
+            assert np.max(np.abs(L[0, 0] - np.array(case[key]["LSE"]))) <= tol, (case["name"], key)
+
+
+def test_brute_force():
+    check_brute_force(attention_ref)
+
+
+def test_closed_forms():
+    check_closed_forms(attention_ref)
+
+
+def test_single_key():
+    q, k, v = (_rand((2, 3, 1, 8), s) for s in range(3))
+    for causal in (False, True):
+        O, L = attention_ref(q, k, v, 0.3, causal)
+        np.testing.assert_array_equal(O, v)
+        c = float(np.float32(0.3))
+        np.testing.assert_allclose(L, c * np.einsum("bhnd,bhnd->bhn", q, k), rtol=0, atol=1e-14)
+
+
+def test_identical_keys_give_mean_of_values():
+    B, H, N, d = 1, 2, 33, 8
+    q = _rand((B, H, N, d), 1)
+    k = np.broadcast_to(_rand((B, H, 1, d), 2), (B, H, N, d)).copy()
+    v = _rand((B, H, N, d), 3)
+    c = float(np.float32(0.25))
+    s = c * np.einsum("bhnd,bhd->bhn", q, k[:, :, 0])
+    O, L = attention_ref(q, k, v, 0.25, False)
+    np.testing.assert_allclose(O, np.broadcast_to(v.mean(axis=2, keepdims=True), O.shape), atol=1e-12)
+    np.testing.assert_allclose(L, s + math.log(N), atol=1e-12)
+    Oc, Lc = attention_ref(q, k, v, 0.25, True)
+    prefix_mean = np.cumsum(v, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+    np.testing.assert_allclose(Oc, prefix_mean, atol=1e-12)
+    np.testing.assert_allclose(Lc, s + np.log(np.arange(1, N + 1))[None, None], atol=1e-12)
+
+
+def test_causal_row_zero_is_first_value():
+    q, k, v = (_rand((2, 2, 9, 4), s) for s in range(3))
+    O, _ = attention_ref(q, k, v, 1.7, True)
+    np.testing.assert_array_equal(O[:, :, 0], v[:, :, 0])
+
+
+def test_scale_zero_is_uniform():
+    B, H, N, d = 1, 2, 20, 4
+    q, k, v = (_rand((B, H, N, d), s, 5.0) for s in range(3))
+    O, L = attention_ref(q, k, v, 0.0, False)
+    np.testing.assert_allclose(O, np.broadcast_to(v.mean(axis=2, keepdims=True), O.shape), atol=1e-12)
+    np.testing.assert_allclose(L, np.full((B, H, N), math.log(N)), atol=1e-13)
+    Oc, Lc = attention_ref(q, k, v, 0.0, True)
+    np.testing.assert_allclose(Oc, np.cumsum(v, axis=2) / np.arange(1, N + 1)[None, None, :, None],
+                               atol=1e-12)
+    np.testing.assert_allclose(Lc, np.broadcast_to(np.log(np.arange(1, N + 1)), Lc.shape), atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_invariance(causal):
+    # Shift every key by u: scores of row i move by c * q_i.u, softmax unchanged.
+    # A large negative shift (c * q.u << 0) is the case where a running max
+    # started at 0 instead of -inf underflows every exponential.
+    B, H, N, d = 1, 2, 40, 16
+    q, k, v = (_rand((B, H, N, d), s) for s in range(3))
+    q = np.abs(q) + 0.5
+    c = float(np.float32(0.125))
+    O, L = attention_ref(q, k, v, 0.125, causal)
+    for shift in (3.0, -200.0):
+        u = np.full(d, shift)
+        O2, L2 = attention_ref(q, k + u, v, 0.125, causal)
+        np.testing.assert_allclose(O2, O, atol=1e-10)
+        np.testing.assert_allclose(L2, L + c * (q @ u), rtol=1e-13, atol=1e-9)
+        assert np.all(np.isfinite(O2)) and np.all(np.isfinite(L2))
+
+
+def test_key_value_permutation_invariance():
+    B, H, N, d = 2, 1, 31, 8
+    q, k, v = (_rand((B, H, N, d), s) for s in range(3))
+    perm = np.random.default_rng(7).permutation(N)
+    O, L = attention_ref(q, k, v, 0.4, False)
+    O2, L2 = attention_ref(q, k[:, :, perm], v[:, :, perm], 0.4, False)
+    np.testing.assert_allclose(O2, O, atol=1e-13)
+    np.testing.assert_allclose(L2, L, atol=1e-13)
+
+
+def test_probabilities_sum_to_one():
+    # P_ij = exp(s_ij - LSE_i) must sum to one over the visible keys.
+    B, H, N, d = 1, 2, 50, 8
+    q, k, v = (_rand((B, H, N, d), s, 2.0) for s in range(3))
+    c = float(np.float32(0.35))
+    for causal in (False, True):
+        _, L = attention_ref(q, k, v, 0.35, causal)
+        s = c * np.einsum("bhid,bhjd->bhij", q, k)
+        if causal:
+            s = np.where(np.tril(np.ones((N, N), bool)), s, -np.inf)
+        psum = np.exp(s - L[..., None]).sum(axis=-1)
+        np.testing.assert_allclose(psum, 1.0, atol=1e-12)
+
+
+def test_lse_against_scipy_logsumexp():
+    from scipy.special import logsumexp
+    B, H, N, d = 2, 2, 37, 8
+    q, k, v = (_rand((B, H, N, d), s, 3.0) for s in range(3))
+    c = float(np.float32(0.2))
+    for causal in (False, True):
+        _, L = attention_ref(q, k, v, 0.2, causal)
+        s = c * np.einsum("bhid,bhjd->bhij", q, k)
+        if causal:
+            s = np.where(np.tril(np.ones((N, N), bool)), s, -np.inf)
+        np.testing.assert_allclose(L, logsumexp(s, axis=-1), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_against_torch_sdpa_fp64(causal):
+    torch = pytest.importorskip("torch")
+    B, H, N, d = 2, 3, 45, 16
+    q, k, v = (_rand((B, H, N, d), s) for s in range(3))
+    scale = 0.3
+    O, _ = attention_ref(q, k, v, scale, causal)
+    t = [torch.from_numpy(x) for x in (q, k, v)]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *t, is_causal=causal, scale=float(np.float32(scale))).numpy()
+    np.testing.assert_allclose(O, ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("block", [1, 7, 64])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_merge_reaches_definition(block, reverse, causal):
+    B, H, N, d = 1, 2, 70, 8
+    q, k, v = (_rand((B, H, N, d), s, 2.0) for s in range(3))
+    O, L = attention_ref(q, k, v, 0.5, causal)
+    O2, L2 = attention_online_merge(q, k, v, 0.5, causal, block, reverse)
+    np.testing.assert_allclose(O2, O, atol=1e-12)
+    np.testing.assert_allclose(L2, L, atol=1e-12)
+
+
+def test_online_merge_brute_force_and_closed_forms():
+    check_brute_force(lambda q, k, v, s, c: attention_online_merge(q, k, v, s, c, 3))
+    check_closed_forms(lambda q, k, v, s, c: attention_online_merge(q, k, v, s, c, 1, True))
+
+
+def test_rows_subset_matches_full():
+    B, H, N, d = 2, 2, 600, 8
+    q, k, v = (_rand((B, H, N, d), s) for s in range(3))
+    rows = np.array([0, 1, 255, 256, 257, 599, 300])
+    for causal in (False, True):
+        O, L = attention_ref(q, k, v, 0.3, causal)
+        Os, Ls = attention_ref(q, k, v, 0.3, causal, rows=rows)
+        # Equal up to BLAS summation order.
+        np.testing.assert_allclose(Os, O[:, :, rows], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(Ls, L[:, :, rows], rtol=0, atol=1e-13)
+
+
+class _NumpyWith:
+    """numpy with one attribute replaced: plants a mistake in the oracle."""
+
+    def __init__(self, **over):
+        self._over = over
+
+    def __getattr__(self, name):
+        return self._over[name] if name in self._over else getattr(np, name)
+
+
+MUTANTS = {
+    "lse_in_log2": {"np": _NumpyWith(log=np.log2)},
+    "exp_off_by_ulp_scale": {"np": _NumpyWith(exp=lambda x: np.exp(x * 1.001))},
+    "causal_excludes_diagonal": {"_visible_count": lambda i, n, causal: i if causal else n},
+    "scale_dropped": {"np": _NumpyWith(float32=lambda x: 1.0)},
+    "exp_weights_alternate_keys": {"np": _NumpyWith(exp=lambda x: np.exp(x) * (np.arange(x.shape[-1]) % 2 + 1))},
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_pins_catch_planted_mistakes(monkeypatch, mutant):
+    for name, val in MUTANTS[mutant].items():
+        monkeypatch.setattr(oracle_mod, name, val)
+    caught = 0
+    for check in (check_brute_force, check_closed_forms):
+        try:
+            check(attention_ref)
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"planted mistake {mutant} went unnoticed"
