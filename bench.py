@@ -1,0 +1,175 @@
+"""Benchmark: attention-forward TFLOPS on one MI355X, with roofline and CPU-oracle baseline.
+
+One step is one fa2_fwd call over the whole workload (B=1, H=8, N=8192, d=64,
+fp16, non-causal, scale 1/8; Q, K, V drawn from N(0,1) with seed 0), inputs
+resident in HBM.  W untimed warmup steps, then K timed steps bracketed by
+torch.cuda.synchronize(); HIP events recorded on the launch stream give the
+average kernel time used for the roofline figure.
+
+Prints one JSON line.  ``--workload NAME`` times one of the other seeded
+workloads instead (for the design notes; the default line is the headline one).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPS at 1 GPU (4BHN²d, causal halved) + % of MFMA peak"
+# MI355X dense fp16/bf16 MFMA peak: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz.
+MFMA_PEAK_TFLOPS = 2516.6
+# Best hand-written kernel on the leetCUDA notes page (RTX 4090, same shape):
+# 0.740 ms, which is 185.7 TFLOPS under this metric's 4*B*H*N^2*d count.
+PAGE_BEST_TFLOPS = 4 * 8 * 8192 ** 2 * 64 / 0.740e-3 / 1e12
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_21_amd", "csrc", f)
+                  for f in ("fa2_kernel.hpp", "fa2_api.hip")]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_sources_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, target_s: float = 12.0):
+    """Time the fp64 oracle on a bounded sample of the workload: the first R query
+    rows of every (batch, head), R grown until the run takes about target_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from exact_attention_21_amd import workloads as wl
+    from oracle import attention_ref
+
+    qf, kf, vf = (wl.to_float64(x, w.dtype) for x in (q, k, v))
+    rows = 64
+    while True:
+        idx = np.arange(min(rows, w.N))
+        t0 = time.perf_counter()
+        attention_ref(qf, kf, vf, w.softmax_scale(), w.causal, rows=idx)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 4 or rows >= w.N:
+            break
+        rows = min(w.N, rows * 4)
+    # FLOPs of the sampled rows under the metric's count (visible keys only when causal).
+    keys = (idx + 1).sum() if w.causal else idx.size * w.N
+    flops = 4.0 * w.B * w.H * float(keys) * w.d
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {idx.size} of {w.N} query rows of all {w.B * w.H} heads "
+                      f"({flops / 1e9:.1f} GFLOP fp64 in {dt:.2f} s; "
+                      f"host has {len(os.sched_getaffinity(0))} usable cores)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline_b1h8n8192d64_fp16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward pass has no cross-GPU step in this build)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from exact_attention_21_amd import forward, library
+    from exact_attention_21_amd import workloads as wl
+
+    library()  # fail loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    w = {x.name: x for x in wl.WORKLOADS}[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = wl.make_inputs(w, seed=0)
+
+    def to_dev(x):
+        t = torch.from_numpy(x) if w.dtype == wl.FP16 else \
+            torch.from_numpy(x.view("int16")).view(torch.bfloat16)
+        return t.to(dev)
+
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    out = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    scale = w.softmax_scale()
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        forward(tq, tk, tv, scale=scale, causal=w.causal, out=out, lse=lse)
+    torch.cuda.synchronize(dev)
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        forward(tq, tk, tv, scale=scale, causal=w.causal, out=out, lse=lse)
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    flops = w.flops()
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    traffic = read_traffic(w.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGE_BEST_TFLOPS, 3) if w.name == wl.HEADLINE.name else None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q, K, V; no dataset)",
+        "config": {"workload": w.name, **w.describe()},
+        "pct_of_mfma_peak": round(100.0 * value / MFMA_PEAK_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "kernel_ms": round(kernel_ms, 5),
+                     "kernel": "fa2_fwd_kernel", "flops_per_launch": flops},
+        "baseline_note": "vs_baseline divides by 185.7 TFLOPS: the leetCUDA notes page's best "
+                         "kernel (0.740 ms on an RTX 4090, same shape) under this metric's FLOP "
+                         "count; other hardware, context only",
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

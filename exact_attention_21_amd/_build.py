@@ -1,0 +1,50 @@
+"""Build step for the HIP library: one hipcc invocation for gfx950.
+
+``build_library()`` compiles ``csrc/fa2_api.hip`` (which includes the kernel
+header) into ``libfa2.so`` next to this file.  It always recompiles.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+REPO_DIR = os.path.dirname(PKG_DIR)
+LIB_PATH = os.path.join(PKG_DIR, "libfa2.so")
+SOURCES = [os.path.join(PKG_DIR, "csrc", "fa2_api.hip")]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (looked at $HIPCC, /opt/rocm/bin/hipcc and PATH)")
+
+
+def build_command(out: str = LIB_PATH) -> list:
+    return [
+        hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+        # Packed fp32 VALU forms are kept out of the generated code.
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", os.path.join(REPO_DIR, "include"),
+        "-I", os.path.join(PKG_DIR, "csrc"),
+        *SOURCES, "-o", out,
+    ]
+
+
+def build_library(verbose: bool = False) -> str:
+    tmp = LIB_PATH + ".tmp"
+    cmd = build_command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build_library(verbose=True))

@@ -1,0 +1,162 @@
+// C ABI of the FlashAttention-2 forward library (declared in include/fa2.h).
+//
+// Host side only: argument validation, tile-configuration choice, grid
+// mapping and the launch.  Every check runs before the first HIP call, so a
+// rejected call enqueues nothing.
+#include "fa2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "fa2_kernel.hpp"
+
+namespace {
+
+// Tile configuration per head dimension: keys per K/V tile and waves per
+// workgroup (each wave owns 32 query rows).
+struct TileCfg {
+  int bc;
+  int nw;
+};
+
+constexpr TileCfg cfg_for(int64_t d) {
+  return d == 64 ? TileCfg{64, 8} : d == 128 ? TileCfg{64, 8} : TileCfg{32, 4};
+}
+
+constexpr int lds_bytes_for(int64_t d) {
+  // Two buffers, each a K tile and a V tile of bc rows x d 16-bit values.
+  return 2 * 2 * cfg_for(d).bc * (int)d * 2;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+fa2_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int64_t* grid) {
+  if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_UNSUPPORTED_DTYPE;
+  if (d != 64 && d != 128 && d != 256) return FA2_ERR_UNSUPPORTED_HEAD_DIM;
+  if (B < 1 || H < 1 || N < 1) return FA2_ERR_BAD_SHAPE;
+  const int64_t br = 32 * cfg_for(d).nw;
+  // One head's slice is addressed with signed 32-bit byte offsets, including
+  // the zero-filled rows past N in the last query tile.
+  if ((N + br) * d * 2 >= (int64_t(1) << 31)) return FA2_ERR_BAD_SHAPE;
+  if (B > (int64_t(1) << 31) / H) return FA2_ERR_BAD_SHAPE;
+  const int64_t bh = B * H;
+  const int64_t tiles = (N + br - 1) / br;
+  if (tiles > ((int64_t(1) << 31) - 1) / bh) return FA2_ERR_BAD_SHAPE;
+  if (grid) *grid = tiles * bh;
+  return FA2_OK;
+}
+
+template <int D, int BC, int NW, bool BF16, bool CAUSAL>
+hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
+  constexpr int lds = 2 * 2 * BC * D * 2;
+  auto kern = fa2::fa2_fwd_kernel<D, BC, NW, BF16, CAUSAL>;
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16, bool CAUSAL>
+hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream) {
+  constexpr TileCfg c = cfg_for(D);
+  return launch<D, c.bc, c.nw, BF16, CAUSAL>(p, grid, stream);
+}
+
+template <bool BF16, bool CAUSAL>
+hipError_t launch_dt(int64_t d, const fa2::Params& p, int64_t grid, hipStream_t stream) {
+  switch (d) {
+    case 64: return launch_d<64, BF16, CAUSAL>(p, grid, stream);
+    case 128: return launch_d<128, BF16, CAUSAL>(p, grid, stream);
+    default: return launch_d<256, BF16, CAUSAL>(p, grid, stream);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa2_status_string(int status) {
+  switch (status) {
+    case FA2_OK: return "ok";
+    case FA2_ERR_NULL_POINTER: return "a buffer pointer is NULL";
+    case FA2_ERR_BAD_SHAPE: return "bad shape: B, H, N must be >= 1 and within the size limits";
+    case FA2_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension (supported: 64, 128, 256)";
+    case FA2_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype (supported: fp16, bf16)";
+    case FA2_ERR_BAD_SCALE: return "scale is not a finite number";
+    case FA2_ERR_MISALIGNED: return "Q, K, V, O must be 16-byte aligned and LSE 4-byte aligned";
+    case FA2_ERR_OVERLAP: return "O or LSE overlaps an input or each other";
+    case FA2_ERR_HIP: return "the HIP runtime reported an error at launch";
+    default: return "unknown status";
+  }
+}
+
+fa2_status_t fa2_launch_info(int64_t B, int64_t H, int64_t N, int64_t d, int is_causal, int dtype,
+                             int64_t* workgroups, int* threads, int* rows_per_wg,
+                             int* keys_per_tile, int* lds_bytes) {
+  (void)is_causal;
+  int64_t grid = 0;
+  const fa2_status_t st = check_shape(B, H, N, d, dtype, &grid);
+  if (st != FA2_OK) return st;
+  const TileCfg c = cfg_for(d);
+  if (workgroups) *workgroups = grid;
+  if (threads) *threads = c.nw * 64;
+  if (rows_per_wg) *rows_per_wg = c.nw * 32;
+  if (keys_per_tile) *keys_per_tile = c.bc;
+  if (lds_bytes) *lds_bytes = lds_bytes_for(d);
+  return FA2_OK;
+}
+
+fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     int64_t B, int64_t H, int64_t N, int64_t d, float scale, int is_causal,
+                     int dtype, void* stream) {
+  if (!Q || !K || !V || !O || !LSE) return FA2_ERR_NULL_POINTER;
+  int64_t grid = 0;
+  const fa2_status_t st = check_shape(B, H, N, d, dtype, &grid);
+  if (st != FA2_OK) return st;
+  if (!std::isfinite(scale)) return FA2_ERR_BAD_SCALE;
+  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u) return FA2_ERR_MISALIGNED;
+  if ((uintptr_t)LSE & 3u) return FA2_ERR_MISALIGNED;
+  const size_t tensor_bytes = (size_t)(B * H * N * d) * 2;
+  const size_t lse_bytes = (size_t)(B * H * N) * 4;
+  if (overlaps(O, tensor_bytes, Q, tensor_bytes) || overlaps(O, tensor_bytes, K, tensor_bytes) ||
+      overlaps(O, tensor_bytes, V, tensor_bytes) || overlaps(LSE, lse_bytes, Q, tensor_bytes) ||
+      overlaps(LSE, lse_bytes, K, tensor_bytes) || overlaps(LSE, lse_bytes, V, tensor_bytes) ||
+      overlaps(LSE, lse_bytes, O, tensor_bytes))
+    return FA2_ERR_OVERLAP;
+
+  const TileCfg c = cfg_for(d);
+  const int br = 32 * c.nw;
+  fa2::Params p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = LSE;
+  p.n = (int)N;
+  p.bh = (int)(B * H);
+  p.n_qtiles = (int)((N + br - 1) / br);
+  p.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+  p.q_sign = std::signbit(scale) && scale != 0.f ? 0x80008000u : 0u;
+
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dtype == FA2_DTYPE_BF16;
+  hipError_t err;
+  if (bf16) {
+    err = is_causal ? launch_dt<true, true>(d, p, grid, s) : launch_dt<true, false>(d, p, grid, s);
+  } else {
+    err = is_causal ? launch_dt<false, true>(d, p, grid, s) : launch_dt<false, false>(d, p, grid, s);
+  }
+  return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
+}
+
+}  // extern "C"

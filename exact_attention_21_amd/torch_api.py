@@ -1,0 +1,53 @@
+"""PyTorch entry point: allocate O and LSE with torch and call the C ABI.
+
+torch supplies device memory and the current stream; the computation runs in
+the HIP kernel behind ``fa2_fwd``.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from ._binding import FA2_DTYPE_BF16, FA2_DTYPE_FP16, FA2_OK, Fa2Error, fa2_fwd
+
+_DTYPES = {torch.float16: FA2_DTYPE_FP16, torch.bfloat16: FA2_DTYPE_BF16}
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+            causal: bool = False, out: torch.Tensor | None = None,
+            lse: torch.Tensor | None = None):
+    """Attention forward on [B, H, N, d] fp16/bf16 CUDA(HIP) tensors.
+
+    Returns (O, LSE): O has q's shape and dtype, LSE is float32 [B, H, N].
+    ``scale`` defaults to 1/sqrt(d).  ``out``/``lse`` may be given to reuse
+    buffers.  The kernel is enqueued on torch's current stream.
+    """
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must all be float16 or all bfloat16")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     B, H, N, d, float(scale), int(bool(causal)), _DTYPES[q.dtype], stream)
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_fwd")
+    return out, lse

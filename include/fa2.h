@@ -1,0 +1,108 @@
+/*
+ * fa2.h - C ABI of the FlashAttention-2 forward library for AMD Instinct MI355X (gfx950).
+ *
+ * Operation (one call):
+ *   For every batch b < B and head h < H, with S = scale * Q[b,h] * K[b,h]^T (N x N):
+ *     O[b,h]   = softmax_rows(S masked) * V[b,h]
+ *     LSE[b,h,i] = log( sum over visible keys j of exp(S[i,j]) )       (natural log)
+ *   Without the causal flag every key is visible to every query.  With it, key j
+ *   is visible to query i iff j <= i (queries and keys share one sequence, so
+ *   the mask is the square lower triangle).  The N x N score matrix is never
+ *   written to memory.
+ *
+ *   Definition and statistic: "FlashAttention-2 MMA 代码学习" (chuoer47.github.io),
+ *   step 0 (O = softmax(Q K^T scale) V) and step 1 (online (m, l) merge);
+ *   "第 15 章 FA2 前向：Tiling 与 Online Softmax" (yangyitao.com), §15.1 change 4
+ *   (one statistic L = m + log l per row) and the §15.3 kernel skeleton
+ *   (signature Q, K, V, O, LSE over [B, H, N, d], softmax_scale, is_causal;
+ *   scale before the max; causal mask; ragged N; a row with no visible key
+ *   gives O = 0 and LSE = +inf).
+ *
+ * Layouts (all contiguous, row-major, innermost dimension last):
+ *   Q, K, V, O : [B, H, N, d] elements of `dtype` (IEEE binary16 or bfloat16).
+ *   LSE        : [B, H, N] float32.
+ *
+ * Numerics: scores, row statistics and the output accumulator are fp32; the
+ * probabilities are rounded (to nearest even) to `dtype` before the second
+ * matrix product, as are the outputs.  `scale` may be any finite float,
+ * including 0 and negative values.
+ *
+ * Ownership: the caller allocates and owns all five buffers.  The library
+ * allocates no device memory, keeps no pointer after the call returns and has
+ * no mutable global state.  Q, K, V are read only; O and LSE are fully
+ * overwritten (every element, rows 0..N-1).  O and LSE must not overlap Q, K, V
+ * or each other.
+ *
+ * Execution: the call validates its arguments on the host, then enqueues one
+ * kernel on `stream` (a hipStream_t; NULL means the null stream) and returns
+ * without synchronising.  It is safe to call from several host threads.
+ *
+ * Errors: the return value is a status code; nothing is thrown across the ABI.
+ * All argument checks run before any HIP call, so a rejected call enqueues
+ * nothing and leaves O and LSE untouched.  A launch failure reported by the HIP
+ * runtime returns FA2_ERR_HIP.
+ */
+#ifndef FA2_H_
+#define FA2_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA2_DTYPE_FP16 = 0, /* IEEE 754 binary16 */
+  FA2_DTYPE_BF16 = 1  /* bfloat16 */
+} fa2_dtype_t;
+
+typedef enum {
+  FA2_OK = 0,
+  FA2_ERR_NULL_POINTER = 1,         /* a buffer pointer is NULL                            */
+  FA2_ERR_BAD_SHAPE = 2,            /* B, H or N < 1, or a size limit below is exceeded      */
+  FA2_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d is not 64, 128 or 256                               */
+  FA2_ERR_UNSUPPORTED_DTYPE = 4,    /* dtype is not FA2_DTYPE_FP16 or FA2_DTYPE_BF16         */
+  FA2_ERR_BAD_SCALE = 5,            /* scale is NaN or infinite                              */
+  FA2_ERR_MISALIGNED = 6,           /* Q, K, V, O not 16-byte aligned, or LSE not 4-byte     */
+  FA2_ERR_OVERLAP = 7,              /* O or LSE overlaps Q, K, V or each other               */
+  FA2_ERR_HIP = 8                   /* the HIP runtime reported an error at launch           */
+} fa2_status_t;
+
+/*
+ * fa2_fwd - attention forward with log-sum-exp, as described above.
+ *
+ *   Q, K, V   device pointers to [B, H, N, d] `dtype` tensors (read only).
+ *   O         device pointer to a [B, H, N, d] `dtype` tensor (written).
+ *   LSE       device pointer to a [B, H, N] float32 tensor (written).
+ *   B, H, N   batch, heads, sequence length; each >= 1.  Limits: N * d < 2^30
+ *             (one head's slice is addressed with 32-bit byte offsets) and
+ *             ceil(N / 256) * H * B < 2^31 (grid size).
+ *   d         head dimension: 64, 128 or 256.
+ *   scale     softmax scale applied to Q K^T before the row max; any finite value.
+ *   is_causal 0: all keys visible; nonzero: key j visible to query i iff j <= i.
+ *   dtype     element type of Q, K, V and O (fa2_dtype_t).
+ *   stream    hipStream_t to enqueue on; NULL is the null stream.
+ */
+fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     int64_t B, int64_t H, int64_t N, int64_t d, float scale, int is_causal,
+                     int dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa2_status_string(int status);
+
+/*
+ * fa2_launch_info - the launch fa2_fwd would make for these arguments, without
+ * launching.  Writes the number of workgroups, threads per workgroup, query
+ * rows per workgroup, keys per tile and LDS bytes per workgroup.  Returns the
+ * status fa2_fwd would return from its argument checks (pointers are not
+ * examined).  Any output pointer may be NULL.
+ */
+fa2_status_t fa2_launch_info(int64_t B, int64_t H, int64_t N, int64_t d, int is_causal, int dtype,
+                             int64_t* workgroups, int* threads, int* rows_per_wg,
+                             int* keys_per_tile, int* lds_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H_ */

@@ -1,0 +1,119 @@
+"""The C ABI on the host: the library loads, exports what include/fa2.h declares,
+and rejects bad arguments with status codes before any HIP call (so these
+tests need no GPU and launch nothing)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_21_amd as fa
+from exact_attention_21_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa2.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa2_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_functions():
+    assert declared_functions() == sorted(bd.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", bd.LIB_PATH], capture_output=True, text=True)
+    if out.returncode == 0:
+        for name in declared_functions():
+            assert re.search(rf"\bT {name}$", out.stdout, re.M), name
+
+
+def test_status_strings():
+    for st in range(0, 9):
+        s = fa.fa2_status_string(st)
+        assert isinstance(s, str) and s and s != "unknown status"
+    assert fa.fa2_status_string(99) == "unknown status"
+
+
+# Fake, 16-byte aligned, non-overlapping "device" addresses: the checks under
+# test return before anything dereferences them.
+Q, K, V, O, L = (0x10000000 * (i + 1) for i in range(5))
+
+
+def call(**kw):
+    args = dict(Q=Q, K=K, V=V, O=O, LSE=L, B=1, H=2, N=100, d=64, scale=0.125, is_causal=0,
+                dtype=fa.FA2_DTYPE_FP16, stream=0)
+    args.update(kw)
+    return fa.fa2_fwd(**args)
+
+
+@pytest.mark.parametrize("name", ["Q", "K", "V", "O", "LSE"])
+def test_null_pointer(name):
+    assert call(**{name: 0}) == bd.FA2_ERR_NULL_POINTER
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(B=-1), dict(N=-5),
+                                dict(N=1 << 24, d=64), dict(N=(1 << 22), d=256),
+                                dict(B=1 << 20, H=1 << 20)])
+def test_bad_shape(kw):
+    assert call(**kw) == bd.FA2_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("d", [0, 1, 32, 63, 65, 96, 192, 512])
+def test_unsupported_head_dim(d):
+    assert call(d=d) == bd.FA2_ERR_UNSUPPORTED_HEAD_DIM
+
+
+@pytest.mark.parametrize("dtype", [-1, 2, 7])
+def test_unsupported_dtype(dtype):
+    assert call(dtype=dtype) == bd.FA2_ERR_UNSUPPORTED_DTYPE
+
+
+@pytest.mark.parametrize("scale", [math.inf, -math.inf, math.nan])
+def test_bad_scale(scale):
+    assert call(scale=scale) == bd.FA2_ERR_BAD_SCALE
+
+
+@pytest.mark.parametrize("kw", [dict(Q=Q + 2), dict(K=K + 8), dict(V=V + 4), dict(O=O + 1),
+                                dict(LSE=L + 2)])
+def test_misaligned(kw):
+    assert call(**kw) == bd.FA2_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("kw", [dict(O=Q), dict(O=K + 16), dict(LSE=V + 64), dict(LSE=O + 32),
+                                dict(O=L - 16)])
+def test_overlap(kw):
+    assert call(**kw) == bd.FA2_ERR_OVERLAP
+
+
+def test_launch_info_headline_shape():
+    info = fa.fa2_launch_info(1, 8, 8192, 64, 0, fa.FA2_DTYPE_FP16)
+    assert info["rows_per_wg"] * math.ceil(8192 / info["rows_per_wg"]) * 8 \
+        == info["workgroups"] * info["rows_per_wg"]
+    assert info["threads"] % 64 == 0 and info["lds_bytes"] <= 160 * 1024
+    for d in (64, 128, 256):
+        i = fa.fa2_launch_info(4, 8, 2047, d, 1, fa.FA2_DTYPE_BF16)
+        assert i["workgroups"] == 32 * math.ceil(2047 / i["rows_per_wg"])
+        assert i["lds_bytes"] <= 160 * 1024
+
+
+def test_launch_info_rejects_what_fwd_rejects():
+    with pytest.raises(bd.Fa2Error):
+        fa.fa2_launch_info(1, 1, 1, 96, 0, 0)
+    with pytest.raises(bd.Fa2Error):
+        fa.fa2_launch_info(1, 1, 0, 64, 0, 0)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(bd, "_lib", None)
+    monkeypatch.setattr(bd, "LIB_PATH", str(tmp_path / "libfa2.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        bd.library()
