@@ -15,19 +15,22 @@
 
 namespace {
 
-// Tile configuration per head dimension: keys per K/V tile and waves per
-// workgroup (each wave owns 32 query rows).
+// Tile configuration per head dimension: keys per K/V tile, waves per
+// workgroup and 32-row query blocks per wave.
 struct TileCfg {
   int bc;
   int nw;
+  int qb;
 };
 
 constexpr TileCfg cfg_for(int64_t d) {
-  return d == 64 ? TileCfg{64, 8} : d == 128 ? TileCfg{64, 8} : TileCfg{32, 4};
+  return d == 64 ? TileCfg{128, 8, 1} : d == 128 ? TileCfg{32, 8, 1} : TileCfg{32, 4, 1};
 }
 
+constexpr int rows_per_wg(int64_t d) { return 32 * cfg_for(d).nw * cfg_for(d).qb; }
+
 constexpr int lds_bytes_for(int64_t d) {
-  // Two buffers, each a K tile and a V tile of bc rows x d 16-bit values.
+  // Two buffers each of a K tile and a V tile of bc rows x d 16-bit values.
   return 2 * 2 * cfg_for(d).bc * (int)d * 2;
 }
 
@@ -40,7 +43,7 @@ fa2_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, 
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_UNSUPPORTED_DTYPE;
   if (d != 64 && d != 128 && d != 256) return FA2_ERR_UNSUPPORTED_HEAD_DIM;
   if (B < 1 || H < 1 || N < 1) return FA2_ERR_BAD_SHAPE;
-  const int64_t br = 32 * cfg_for(d).nw;
+  const int64_t br = rows_per_wg(d);
   // One head's slice is addressed with signed 32-bit byte offsets, including
   // the zero-filled rows past N in the last query tile.
   if ((N + br) * d * 2 >= (int64_t(1) << 31)) return FA2_ERR_BAD_SHAPE;
@@ -52,10 +55,11 @@ fa2_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, 
   return FA2_OK;
 }
 
-template <int D, int BC, int NW, bool BF16, bool CAUSAL>
+template <int D, int BC, int NW, int QB, bool BF16, bool CAUSAL>
 hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
-  constexpr int lds = 2 * 2 * BC * D * 2;
-  auto kern = fa2::fa2_fwd_kernel<D, BC, NW, BF16, CAUSAL>;
+  constexpr int lds = fa2::Fa2Fwd<D, BC, NW, QB, BF16, CAUSAL>::LDS_BYTES;
+  static_assert(lds == lds_bytes_for(D), "LDS size");
+  auto kern = fa2::fa2_fwd_kernel<D, BC, NW, QB, BF16, CAUSAL>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
@@ -69,7 +73,7 @@ hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream) {
   constexpr TileCfg c = cfg_for(D);
-  return launch<D, c.bc, c.nw, BF16, CAUSAL>(p, grid, stream);
+  return launch<D, c.bc, c.nw, c.qb, BF16, CAUSAL>(p, grid, stream);
 }
 
 template <bool BF16, bool CAUSAL>
@@ -110,7 +114,7 @@ fa2_status_t fa2_launch_info(int64_t B, int64_t H, int64_t N, int64_t d, int is_
   const TileCfg c = cfg_for(d);
   if (workgroups) *workgroups = grid;
   if (threads) *threads = c.nw * 64;
-  if (rows_per_wg) *rows_per_wg = c.nw * 32;
+  if (rows_per_wg) *rows_per_wg = ::rows_per_wg(d);
   if (keys_per_tile) *keys_per_tile = c.bc;
   if (lds_bytes) *lds_bytes = lds_bytes_for(d);
   return FA2_OK;
@@ -134,8 +138,7 @@ fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float
       overlaps(LSE, lse_bytes, O, tensor_bytes))
     return FA2_ERR_OVERLAP;
 
-  const TileCfg c = cfg_for(d);
-  const int br = 32 * c.nw;
+  const int br = rows_per_wg(d);
   fa2::Params p;
   p.q = Q;
   p.k = K;

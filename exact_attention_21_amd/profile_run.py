@@ -1,0 +1,55 @@
+"""Driver for hardware-counter runs: a few fa2_fwd launches on one seeded
+workload, then one plain device-to-device copy of known size.
+
+The copy gives the factor that turns the FETCH_SIZE / WRITE_SIZE counters into
+bytes (it moves exactly ``copy_mb`` MiB each way).  Usage:
+
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -- \
+      python -m exact_attention_21_amd.profile_run --workload NAME
+"""
+from __future__ import annotations
+
+import argparse
+import sys
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="headline_b1h8n8192d64_fp16")
+    ap.add_argument("--launches", type=int, default=3)
+    ap.add_argument("--copy-mb", type=int, default=256)
+    args = ap.parse_args()
+
+    import torch
+
+    from . import forward, library
+    from . import workloads as wl
+
+    library()
+    w = {x.name: x for x in wl.WORKLOADS}[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = wl.make_inputs(w, seed=0)
+
+    def to_dev(x):
+        t = torch.from_numpy(x) if w.dtype == wl.FP16 else \
+            torch.from_numpy(x.view("int16")).view(torch.bfloat16)
+        return t.to(dev)
+
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    out = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    for _ in range(args.launches):
+        forward(tq, tk, tv, scale=w.softmax_scale(), causal=w.causal, out=out, lse=lse)
+    torch.cuda.synchronize(dev)
+    n = args.copy_mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize(dev)
+    dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    print(f"profile_run: {args.launches} launches of {w.name}, copy of {args.copy_mb} MiB", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
