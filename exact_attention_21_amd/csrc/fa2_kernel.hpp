@@ -126,35 +126,57 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 
 // LDS layouts.  A K or V tile is BC rows (keys) of D 16-bit values, stored as
-// 16-byte chunks; chunk c of row r sits at chunk position c ^ swz(r).  The XOR
-// only permutes chunks inside aligned groups of 8, so a row stays in place.
-//  * K rows are read 16 bytes per lane by 32 consecutive rows at one chunk:
-//    rows r..r+7 must land on 8 different chunk positions.
-//  * V rows are read 8 bytes per lane by ds_read_b64_tr_b16: a 16-lane group
-//    covers 4 consecutive rows x 2 adjacent chunks; 2*(r%4) spreads them over
-//    all 8 positions.
-__device__ __forceinline__ int swz_k(int row) { return row & 7; }
-__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 1; }
+// 16-byte chunks; chunk c of row r sits at chunk position c ^ swz(r).  The
+// gfx950 LDS serves 256 bytes (64 banks x 4 bytes) per cycle; a 16-byte read
+// by 64 lanes is served 16 lanes at a time, so 16 lanes must hit 16
+// different 16-byte bank groups to go at full rate (measured: the rows-only
+// layout runs at a quarter of that).
+//  * K rows are read 16 bytes per lane by 32 consecutive rows at one chunk.
+//    With 128-byte rows (d = 64) two rows share a 256-byte line, so rows with
+//    equal parity need distinct positions: XOR with (r/2)%8.  With rows of 256
+//    bytes or more every row starts a line: XOR with r%16.
+//  * V rows are read by ds_read_b64_tr_b16, which measured no faster with any
+//    swizzle than without, so V is stored unswizzled.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) { return D == 64 ? ((row >> 1) & 7) : (row & 15); }
+__device__ __forceinline__ int swz_v(int) { return 0; }
 
-template <int D, int BC, int NW, int QB, bool BF16, bool CAUSAL>
+// Work schedules inside a workgroup.
+enum Sched : int {
+  kSimple = 0,    // every wave owns QW rows of the query tile, all keys; one barrier per tile
+  kPingPong = 1,  // as kSimple, two 4-wave groups half a tile apart (run_pingpong)
+  kSplitKV = 2,   // two 4-wave groups own the same rows and split the keys (run_splitkv)
+};
+
+template <int D, int BC, int NW, int QB, int SCHED, bool BF16, bool CAUSAL>
 struct Fa2Fwd {
   static constexpr int THREADS = NW * 64;
   static constexpr int QW = 32 * QB;             // query rows per wave
-  static constexpr int BR = NW * QW;             // query rows per workgroup
+  // Waves that own distinct query rows (split-KV: the two groups share rows).
+  static constexpr int QWAVES = SCHED == kSplitKV ? NW / 2 : NW;
+  static constexpr int BR = QWAVES * QW;         // query rows per workgroup
+  // Threads that stage one K/V stream (split-KV: one stream per group).
+  static constexpr int STAGERS = SCHED == kSplitKV ? THREADS / 2 : THREADS;
+  static constexpr int STREAMS = SCHED == kSplitKV ? 2 : 1;
   static constexpr int KB = BC / 32;             // 32-key blocks per tile
   static constexpr int DB = D / 32;              // 32-row blocks of O^T
   static constexpr int DK = D / 16;              // 16-deep k-steps of S^T = K Q^T
   static constexpr int ROWB = D * 2;             // bytes per K/V row
   static constexpr int TILEB = BC * ROWB;        // bytes per K (or V) tile
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
-  static constexpr int CPT = BC * CPR / THREADS; // chunks per thread per tile (each of K, V)
-  static constexpr int LDS_BYTES = 4 * TILEB;    // K[0], K[1], V[0], V[1]
+  static constexpr int CPT = BC * CPR / STAGERS; // chunks per thread per tile (each of K, V)
+  static constexpr int STREAMB = 4 * TILEB;      // one stream: K[0], K[1], V[0], V[1]
+  // Split-KV merge area: per group-1 lane, O^T (QB*DB*16 floats) then m, l.
+  static constexpr int MERGE_FLOATS = QB * DB * 16 + 2 * QB;
+  static constexpr int MERGE_BYTES = SCHED == kSplitKV ? (NW / 2) * 64 * MERGE_FLOATS * 4 : 0;
+  static constexpr int LDS_BYTES = STREAMS * STREAMB > MERGE_BYTES ? STREAMS * STREAMB : MERGE_BYTES;
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert((BC * CPR) % THREADS == 0 && CPT >= 1, "staging split");
-  // Every LDS access below is a lane base register plus a compile-time
-  // offset; keeping the whole LDS image under 64 KiB lets the offsets ride in
-  // the instruction's 16-bit immediate.
-  static_assert(LDS_BYTES <= 65536, "LDS image must fit the ds immediate offset");
+  static_assert((BC * CPR) % STAGERS == 0 && CPT >= 1, "staging split");
+  static_assert(SCHED != kSplitKV || NW % 2 == 0, "split-KV needs two equal groups");
+  // Every LDS access in the tile loop is a lane base register plus a
+  // compile-time offset; keeping the tile buffers under 64 KiB lets the
+  // offsets ride in the instruction's 16-bit immediate.
+  static_assert(STREAMS * STREAMB <= 65536, "LDS image must fit the ds immediate offset");
 
   typedef __attribute__((address_space(3))) char lds_char;
 
@@ -192,30 +214,32 @@ struct Fa2Fwd {
     }
   }
 
-  // Online softmax of one tile: updates the exponent base m, the lane's share
-  // of l and (rarely) rescales O; turns the scores into packed probabilities
-  // laid out as the B operands of O^T += V^T P^T.
-  template <bool MASK>
-  static __device__ __forceinline__ void softmax(Scores& sc, u32x4 (&pb)[QB][KB][2], float (&m)[QB],
-                                                 float (&l)[QB], f32x16 (&o)[QB][DB], float c2,
-                                                 int lane, int k0, int qw0, int n) {
+  // Per-element mask of one tile (ragged tail and causal diagonal): hidden
+  // scores become -inf before the row max, as the pages require.
+  static __device__ __forceinline__ void mask_scores(Scores& sc, int lane, int k0, int qw0, int n) {
     const int half = lane >> 5;
     const float ninf = -__builtin_inff();
-    if constexpr (MASK) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = qw0 + 32 * qb + (lane & 31);
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qrow = qw0 + 32 * qb + (lane & 31);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool hide = (key >= n) || (CAUSAL && key > qrow);
-            sc.s[qb][kb][r] = hide ? ninf : sc.s[qb][kb][r];
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool hide = (key >= n) || (CAUSAL && key > qrow);
+          sc.s[qb][kb][r] = hide ? ninf : sc.s[qb][kb][r];
         }
       }
     }
+  }
+
+  // Row max of the tile and the online update of the exponent base m: the
+  // base moves (and O and l are rescaled) only when some row's tile max
+  // exceeds it by more than kRebase.
+  static __device__ __forceinline__ void update_base(const Scores& sc, float (&m)[QB], float (&l)[QB],
+                                                     f32x16 (&o)[QB][DB], float c2) {
+    const float ninf = -__builtin_inff();
     bool rebase = false;
     float mt[QB];
 #pragma unroll
@@ -246,19 +270,18 @@ struct Fa2Fwd {
         const float alpha = (m_new == ninf) ? 1.f : __builtin_amdgcn_exp2f(m[qb] - m_new);
         m[qb] = m_new;
         l[qb] *= alpha;
-        // In-place multiply: keeps O in the same registers on both sides of
-        // this rarely taken branch.
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = o[qb][db][r];
-            asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(alpha));
-            o[qb][db][r] = x;
-          }
-        }
+        for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
       }
     }
+  }
+
+  // Probabilities of one tile relative to the base m, packed as the B
+  // operands of O^T += V^T P^T, and the lane's share of their row sum.
+  template <bool MASK>
+  static __device__ __forceinline__ void exponentiate(Scores& sc, u32x4 (&pb)[QB][KB][2],
+                                                      const float (&m)[QB], float (&l)[QB], float c2) {
+    const float ninf = -__builtin_inff();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float mb = m[qb];
@@ -268,6 +291,8 @@ struct Fa2Fwd {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc.s[qb][kb][r], c2, -mb));
+          // Hidden keys give exactly 0 (also when the scale is 0 or the row
+          // has seen only hidden keys, where the exponent would be NaN).
           if constexpr (MASK) p = (sc.s[qb][kb][r] == ninf) ? 0.f : p;
           sc.s[qb][kb][r] = p;
         }
@@ -347,7 +372,12 @@ struct Fa2Fwd {
     const int qtile = CAUSAL ? (p.n_qtiles - 1 - t) : t;
     const int n = p.n;
     const int q0 = qtile * BR;
-    const int qw0 = q0 + wave * QW;  // first query of this wave
+    // Query rows of this wave.  Split-KV: waves w and w+NW/2 own the same rows.
+    const int qwave = SCHED == kSplitKV ? wave % QWAVES : wave;
+    const int qw0 = q0 + qwave * QW;
+    // Split-KV: the group's K/V stream and its LDS area.
+    const int grp = SCHED == kSplitKV ? wave / QWAVES : 0;
+    const int stid = SCHED == kSplitKV ? tid % STAGERS : tid;
 
     const size_t slice = (size_t)bh * (size_t)n * D;  // elements before this head
     const uint32_t slice_bytes = (uint32_t)n * D * 2;
@@ -358,23 +388,28 @@ struct Fa2Fwd {
     const auto rl = make_rsrc(p.lse + (size_t)bh * n, (uint32_t)n * 4);
 
     // Q^T operands: for k-step s, lane holds Q[row][16s + 8*half .. +7].
-    u32x4 qf[QB][DK];
+    State st;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int qrow = qw0 + 32 * qb + (lane & 31);
 #pragma unroll
       for (int s = 0; s < DK; ++s) {
-        qf[qb][s] = __builtin_amdgcn_raw_buffer_load_b128(rq, (qrow * D + 16 * s + 8 * half) * 2, 0, 0);
-        qf[qb][s] ^= p.q_sign;
+        st.qf[qb][s] = __builtin_amdgcn_raw_buffer_load_b128(rq, (qrow * D + 16 * s + 8 * half) * 2, 0, 0);
+        st.qf[qb][s] ^= p.q_sign;
       }
+      st.m[qb] = -__builtin_inff();  // exponent base (base-2 domain)
+      st.l[qb] = 0.f;                // this lane's share of the row sum
+#pragma unroll
+      for (int db = 0; db < DB; ++db) st.o[qb][db] = f32x16{};
     }
 
     // Lane-constant LDS offsets.
     LdsOffsets off;
     {
       const int row = lane & 31;
+      const int sbase = grp * STREAMB;  // this wave's K/V stream in LDS
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks) off.k[ks] = row * ROWB + (((2 * ks + half) ^ swz_k(row)) << 4);
+      for (int ks = 0; ks < DK; ++ks) off.k[ks] = sbase + row * ROWB + (((2 * ks + half) ^ swz_k<D>(row)) << 4);
       // V^T transposed reads: lane group g = lane/16 serves A rows (dims)
       // 16*(g%2) + lane%16 for key half g/2; as a source, lane 16g + 4e + u
       // reads key row 4*(g/2) + e at dims 16*(g%2) + 4u .. +3.  Rows 32kb+16u
@@ -384,84 +419,28 @@ struct Fa2Fwd {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int dim = 32 * db + 16 * (g & 1) + 4 * (lane & 3);
-        off.v[db] = key * ROWB + (((dim >> 3) ^ swz_v(key)) << 4) + ((dim & 7) << 1);
+        off.v[db] = sbase + key * ROWB + (((dim >> 3) ^ swz_v(key)) << 4) + ((dim & 7) << 1);
       }
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
-        const int c = tid + THREADS * j;
+        const int c = stid + STAGERS * j;
         const int r = c / CPR, col = c % CPR;
-        off.kst[j] = r * ROWB + ((col ^ swz_k(r)) << 4);
-        off.vst[j] = r * ROWB + ((col ^ swz_v(r)) << 4);
+        off.kst[j] = sbase + r * ROWB + ((col ^ swz_k<D>(r)) << 4);
+        off.vst[j] = sbase + r * ROWB + ((col ^ swz_v(r)) << 4);
         off.gld[j] = (r * D + col * 8) * 2;
       }
     }
 
-    const float c2 = p.scale_log2;
-    f32x16 o[QB][DB];
-    float m[QB], l[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      m[qb] = -__builtin_inff();  // exponent base (base-2 domain)
-      l[qb] = 0.f;                // this lane's share of the row sum
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[qb][db] = f32x16{};
-    }
-
     const int kend = CAUSAL ? min(n, q0 + BR) : n;
     const int ntiles = (kend + BC - 1) / BC;
-
-    // Staging of tile j: global -> registers (soffset = tile start), then LDS.
-    u32x4 stk[CPT], stv[CPT];
-    auto load = [&](int j) {
-      const int base = j * TILEB;
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        stk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off.gld[i], base, 0);
-        stv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off.gld[i], base, 0);
-      }
-    };
-    auto store = [&](auto buf) {
-      constexpr int B = decltype(buf)::value;
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        *(__attribute__((address_space(3))) u32x4*)(lds + B * TILEB + off.kst[i]) = stk[i];
-        *(__attribute__((address_space(3))) u32x4*)(lds + (2 + B) * TILEB + off.vst[i]) = stv[i];
-      }
-    };
-
-    // A wave takes part in tile j if some key of it is visible to some of its rows.
-    auto active = [&](int j) { return !CAUSAL || j * BC <= qw0 + QW - 1; };
-    // Tile j needs per-element masking (ragged tail or causal diagonal).
-    auto masked = [&](int j) { return (j * BC + BC > n) || (CAUSAL && j * BC + BC - 1 > qw0); };
-
-    // Tile j lives in buffer j%2 (K and V).  Its successor is loaded from
-    // global memory at the top of iteration j and written to the other buffer
-    // at the bottom; that buffer was last read in iteration j-1, before the
-    // barrier that ended it.
-    auto step = [&](int j, auto buf) {
-      constexpr int B = decltype(buf)::value;
-      const bool more = j + 1 < ntiles;
-      if (more) load(j + 1);
-      if (active(j)) {
-        Scores sc;
-        scores(lds + B * TILEB, off, qf, sc);
-        u32x4 pb[QB][KB][2];
-        if (masked(j))
-          softmax<true>(sc, pb, m, l, o, c2, lane, j * BC, qw0, n);
-        else
-          softmax<false>(sc, pb, m, l, o, c2, lane, j * BC, qw0, n);
-        pv(lds + (2 + B) * TILEB, off, pb, o);
-      }
-      if (more) store(std::integral_constant<int, 1 - B>{});
-      __syncthreads();
-    };
-
-    load(0);
-    store(std::integral_constant<int, 0>{});
-    __syncthreads();
-    for (int j = 0; j < ntiles; j += 2) {
-      step(j, std::integral_constant<int, 0>{});
-      if (j + 1 < ntiles) step(j + 1, std::integral_constant<int, 1>{});
+    const Ctx cx{rk, rv, lds, off, p.scale_log2, lane, tid, qw0, n, ntiles};
+    if constexpr (SCHED == kPingPong) {
+      run_pingpong(cx, st);
+    } else if constexpr (SCHED == kSplitKV) {
+      run_splitkv(cx, st, grp);
+      if (grp != 0) return;  // group 1 handed its state to group 0
+    } else {
+      run_simple(cx, st);
     }
 
     // Epilogue: combine the two halves' partial sums, divide once, store.
@@ -469,7 +448,7 @@ struct Fa2Fwd {
     for (int qb = 0; qb < QB; ++qb) {
       const int qrow = qw0 + 32 * qb + (lane & 31);
       float l_lo, l_hi;
-      halves(l[qb], l_lo, l_hi);
+      halves(st.l[qb], l_lo, l_hi);
       const float l_tot = l_lo + l_hi;
       const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
 #pragma unroll
@@ -477,25 +456,260 @@ struct Fa2Fwd {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           u32x2 w;
-          w[0] = pack2<BF16>(o[qb][db][4 * g + 0] * inv, o[qb][db][4 * g + 1] * inv);
-          w[1] = pack2<BF16>(o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv);
+          w[0] = pack2<BF16>(st.o[qb][db][4 * g + 0] * inv, st.o[qb][db][4 * g + 1] * inv);
+          w[1] = pack2<BF16>(st.o[qb][db][4 * g + 2] * inv, st.o[qb][db][4 * g + 3] * inv);
           const int dim = 32 * db + 8 * g + 4 * half;
           __builtin_amdgcn_raw_buffer_store_b64(w, ro, (qrow * D + dim) * 2, 0, 0);
         }
       }
       if (half == 0) {
-        const float lse = (l_tot > 0.f) ? (m[qb] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f
+        const float lse = (l_tot > 0.f) ? (st.m[qb] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f
                                         : __builtin_inff();
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qrow * 4, 0, 0);
       }
     }
   }
+
+  // Per-wave running state.
+  struct State {
+    u32x4 qf[QB][DK];  // Q^T operands
+    f32x16 o[QB][DB];  // O^T accumulators
+    float m[QB];       // exponent base per row (base-2 domain)
+    float l[QB];       // this lane's share of the row sum
+  };
+
+  // Loop-invariant context.
+  struct Ctx {
+    __amdgpu_buffer_rsrc_t rk, rv;
+    lds_char* lds;
+    LdsOffsets off;
+    float c2;
+    int lane, tid, qw0, n, ntiles;
+    // A wave takes part in tile j if some key of it is visible to some of its rows.
+    __device__ __forceinline__ bool active(int j) const { return !CAUSAL || j * BC <= qw0 + QW - 1; }
+    // Tile j needs per-element masking (ragged tail or causal diagonal).
+    __device__ __forceinline__ bool masked(int j) const {
+      return (j * BC + BC > n) || (CAUSAL && j * BC + BC - 1 > qw0);
+    }
+  };
+
+  // Global -> register staging of one K or V tile (soffset = tile start).
+  static __device__ __forceinline__ void stage_load(const Ctx& cx, const __amdgpu_buffer_rsrc_t& r, int j,
+                                                    u32x4 (&reg)[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) reg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, cx.off.gld[i], j * TILEB, 0);
+  }
+  // Register -> LDS store of one staged tile at a compile-time LDS offset.
+  template <int BASE>
+  static __device__ __forceinline__ void stage_store_k(const Ctx& cx, const u32x4 (&reg)[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) *(__attribute__((address_space(3))) u32x4*)(cx.lds + BASE + cx.off.kst[i]) = reg[i];
+  }
+  template <int BASE>
+  static __device__ __forceinline__ void stage_store_v(const Ctx& cx, const u32x4 (&reg)[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) *(__attribute__((address_space(3))) u32x4*)(cx.lds + BASE + cx.off.vst[i]) = reg[i];
+  }
+
+  // Softmax of tile j: scores -> probabilities (packed) and the online update.
+  static __device__ __forceinline__ void softmax_tile(const Ctx& cx, State& st, Scores& sc, int j,
+                                                      u32x4 (&pb)[QB][KB][2]) {
+    const bool msk = cx.masked(j);
+    if (msk) mask_scores(sc, cx.lane, j * BC, cx.qw0, cx.n);
+    update_base(sc, st.m, st.l, st.o, cx.c2);
+    if (msk)
+      exponentiate<true>(sc, pb, st.m, st.l, cx.c2);
+    else
+      exponentiate<false>(sc, pb, st.m, st.l, cx.c2);
+  }
+
+  // One barrier per tile; tile j lives in K/V buffer j%2.  Its successor is
+  // loaded from global memory at the top of iteration j and written to the
+  // other buffer at the bottom; that buffer was last read in iteration j-1,
+  // before the barrier that ended it.
+  static __device__ __forceinline__ void run_simple(const Ctx& cx, State& st) {
+    u32x4 stk[CPT], stv[CPT];
+    auto step = [&](int j, auto buf) {
+      constexpr int B = decltype(buf)::value;
+      const bool more = j + 1 < cx.ntiles;
+      if (more) {
+        stage_load(cx, cx.rk, j + 1, stk);
+        stage_load(cx, cx.rv, j + 1, stv);
+      }
+      if (cx.active(j)) {
+        Scores sc;
+        scores(cx.lds + B * TILEB, cx.off, st.qf, sc);
+        u32x4 pb[QB][KB][2];
+        softmax_tile(cx, st, sc, j, pb);
+        pv(cx.lds + (2 + B) * TILEB, cx.off, pb, st.o);
+      }
+      if (more) {
+        stage_store_k<(1 - B) * TILEB>(cx, stk);
+        stage_store_v<(3 - B) * TILEB>(cx, stv);
+      }
+      __syncthreads();
+    };
+    stage_load(cx, cx.rk, 0, stk);
+    stage_load(cx, cx.rv, 0, stv);
+    stage_store_k<0>(cx, stk);
+    stage_store_v<2 * TILEB>(cx, stv);
+    __syncthreads();
+    for (int j = 0; j < cx.ntiles; j += 2) {
+      step(j, std::integral_constant<int, 0>{});
+      if (j + 1 < cx.ntiles) step(j + 1, std::integral_constant<int, 1>{});
+    }
+  }
+
+  // Ping-pong schedule for 8 waves.  Waves 0-3 (group 0) and 4-7 (group 1)
+  // share the SIMDs pairwise and run half a tile apart, two barriers per tile:
+  //   phase 2i   : group 0 issues P V(i-1) and S^T(i) on the matrix cores,
+  //                group 1 runs the softmax of tile i-1 on the VALU;
+  //   phase 2i+1 : group 0 runs the softmax of tile i,
+  //                group 1 issues P V(i-1) and S^T(i).
+  // Tile i lives in K/V buffer i%2.  K(i) is read in phases 2i and 2i+1, V(i)
+  // in phases 2i+2 and 2i+3.  In phase 2i all waves write K(i+1) and V(i)
+  // (loaded from global memory during phase 2i-1) into the buffers that held
+  // K(i-1) and V(i-2), whose last reads were in phase 2i-1.
+  static __device__ __forceinline__ void run_pingpong(const Ctx& cx, State& st) {
+    static_assert(NW == 8, "ping-pong pairs two groups of four waves");
+    const bool g0 = (cx.tid >> 8) == 0;
+    const int T = cx.ntiles;
+    u32x4 stk[CPT], stv[CPT];
+    Scores sc;             // scores waiting for their softmax
+    u32x4 pb[QB][KB][2];   // probabilities waiting for P V
+
+    auto mfma_part = [&](int i, auto kbuf, auto vbuf) {
+      constexpr int KBUF = decltype(kbuf)::value, VBUF = decltype(vbuf)::value;
+      if (i >= 1 && cx.active(i - 1)) pv(cx.lds + (2 + VBUF) * TILEB, cx.off, pb, st.o);
+      if (i < T && cx.active(i)) scores(cx.lds + KBUF * TILEB, cx.off, st.qf, sc);
+    };
+    auto valu_part = [&](int j) {
+      if (j >= 0 && j < T && cx.active(j)) softmax_tile(cx, st, sc, j, pb);
+    };
+    // Iteration i: phases 2i and 2i+1.  PAR = i%2 selects the buffers:
+    // K(i) in K[PAR], V(i-1) in V[1-PAR]; this phase stores K(i+1) to
+    // K[1-PAR] and V(i) to V[PAR].
+    auto iteration = [&](int i, auto par) {
+      constexpr int PAR = decltype(par)::value;
+      if (i + 1 < T) stage_store_k<(1 - PAR) * TILEB>(cx, stk);
+      if (i < T) stage_store_v<(2 + PAR) * TILEB>(cx, stv);
+      if (g0)
+        mfma_part(i, std::integral_constant<int, PAR>{}, std::integral_constant<int, 1 - PAR>{});
+      else
+        valu_part(i - 1);
+      __syncthreads();
+      if (i + 2 < T) stage_load(cx, cx.rk, i + 2, stk);
+      if (i + 1 < T) stage_load(cx, cx.rv, i + 1, stv);
+      if (g0)
+        valu_part(i);
+      else
+        mfma_part(i, std::integral_constant<int, PAR>{}, std::integral_constant<int, 1 - PAR>{});
+      if (i < T) __syncthreads();
+    };
+
+    // Prologue: K(0) into K[0]; K(1) and V(0) staged for phase 0.
+    stage_load(cx, cx.rk, 0, stk);
+    stage_store_k<0>(cx, stk);
+    if (T > 1) stage_load(cx, cx.rk, 1, stk);
+    stage_load(cx, cx.rv, 0, stv);
+    __syncthreads();
+    for (int i = 0; i <= T; i += 2) {
+      iteration(i, std::integral_constant<int, 0>{});
+      if (i + 1 <= T) iteration(i + 1, std::integral_constant<int, 1>{});
+    }
+  }
+
+  // Split-KV: group 0 (waves 0..NW/2-1) takes key tiles [0, T0) and group 1
+  // the tiles [T0, T), T0 = ceil(T/2); waves w and w+NW/2 own the same query
+  // rows, so every SIMD runs one wave of each group and each K/V byte read
+  // from LDS feeds QB = 2 query blocks.  Each group has its own
+  // double-buffered K/V stream; both advance one tile per barrier.  At the
+  // end group 1 leaves (m, l, O) in LDS and group 0 merges them lane by lane
+  // with the same algebra as the online update.
+  static __device__ __forceinline__ void run_splitkv(const Ctx& cx, State& st, int grp) {
+    const int T = cx.ntiles;
+    const int T0 = (T + 1) / 2;
+    const int first = grp == 0 ? 0 : T0;           // first tile of this group
+    const int count = grp == 0 ? T0 : T - T0;      // tiles of this group (count <= T0)
+    u32x4 stk[CPT], stv[CPT];
+    auto step = [&](int s, auto buf) {
+      constexpr int B = decltype(buf)::value;
+      const int j = first + s;
+      const bool mine = s < count;
+      const bool more = s + 1 < count;
+      if (more) {
+        stage_load(cx, cx.rk, j + 1, stk);
+        stage_load(cx, cx.rv, j + 1, stv);
+      }
+      if (mine && cx.active(j)) {
+        Scores sc;
+        scores(cx.lds + B * TILEB, cx.off, st.qf, sc);
+        u32x4 pb[QB][KB][2];
+        softmax_tile(cx, st, sc, j, pb);
+        pv(cx.lds + (2 + B) * TILEB, cx.off, pb, st.o);
+      }
+      if (more) {
+        stage_store_k<(1 - B) * TILEB>(cx, stk);
+        stage_store_v<(3 - B) * TILEB>(cx, stv);
+      }
+      __syncthreads();
+    };
+    if (count > 0) {
+      stage_load(cx, cx.rk, first, stk);
+      stage_load(cx, cx.rv, first, stv);
+      stage_store_k<0>(cx, stk);
+      stage_store_v<2 * TILEB>(cx, stv);
+    }
+    __syncthreads();
+    for (int s = 0; s < T0; s += 2) {
+      step(s, std::integral_constant<int, 0>{});
+      if (s + 1 < T0) step(s + 1, std::integral_constant<int, 1>{});
+    }
+
+    // Merge (the tile buffers are free after the last barrier).
+    typedef __attribute__((address_space(3))) float lds_float;
+    const int slot = (cx.tid % (STAGERS)) * MERGE_FLOATS;  // same slot for waves w and w+NW/2
+    lds_float* mb = (lds_float*)cx.lds + slot;
+    if (grp != 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mb[(qb * DB + db) * 16 + r] = st.o[qb][db][r];
+        }
+        mb[QB * DB * 16 + 2 * qb] = st.m[qb];
+        mb[QB * DB * 16 + 2 * qb + 1] = st.l[qb];
+      }
+    }
+    __syncthreads();
+    if (grp == 0) {
+      const float ninf = -__builtin_inff();
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m1 = mb[QB * DB * 16 + 2 * qb];
+        const float l1 = mb[QB * DB * 16 + 2 * qb + 1];
+        const float m0 = st.m[qb];
+        const float mm = __builtin_fmaxf(m0, m1);
+        const float a0 = (m0 == ninf) ? 0.f : __builtin_amdgcn_exp2f(m0 - mm);
+        const float a1 = (m1 == ninf) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+        st.m[qb] = mm;
+        st.l[qb] = a0 * st.l[qb] + a1 * l1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            st.o[qb][db][r] = a0 * st.o[qb][db][r] + a1 * mb[(qb * DB + db) * 16 + r];
+        }
+      }
+    }
+  }
 };
 
-template <int D, int BC, int NW, int QB, bool BF16, bool CAUSAL>
+template <int D, int BC, int NW, int QB, int SCHED, bool BF16, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64, 1) fa2_fwd_kernel(const Params p) {
   extern __shared__ __attribute__((aligned(16))) char lds_generic[];
-  Fa2Fwd<D, BC, NW, QB, BF16, CAUSAL>::run(
+  Fa2Fwd<D, BC, NW, QB, SCHED, BF16, CAUSAL>::run(
       p, (__attribute__((address_space(3))) char*)(__attribute__((address_space(3))) void*)lds_generic);
 }
 
