@@ -41,7 +41,7 @@ def kernel_hash() -> str:
 def read_traffic(workload_name: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.md")
+    path = os.path.join(ROOT, "profiles", f"fa2_fwd_kernel_{workload_name}.md")
     if not os.path.exists(path):
         return None
     vals = {}
