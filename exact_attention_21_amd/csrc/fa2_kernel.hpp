@@ -146,18 +146,27 @@ enum Sched : int {
   kSimple = 0,    // every wave owns QW rows of the query tile, all keys; one barrier per tile
   kPingPong = 1,  // as kSimple, two 4-wave groups half a tile apart (run_pingpong)
   kSplitKV = 2,   // two 4-wave groups own the same rows and split the keys (run_splitkv)
+  kPipe = 3,      // one wave per SIMD; S(j+1) and P(j-1)V(j-1) MFMAs interleaved with softmax(j) (run_pipe)
 };
+
+// Per-lane partial row sums of one tile above this value send the tile to the
+// rebase path: every probability of the tile is then below it, so it is finite
+// and exact to the usual relative rounding in fp16 as well as bf16.
+constexpr float kTileSumLimit = 32768.0f;
 
 template <int D, int BC, int NW, int QB, int SCHED, bool BF16, bool CAUSAL>
 struct Fa2Fwd {
   static constexpr int THREADS = NW * 64;
   static constexpr int QW = 32 * QB;             // query rows per wave
   // Waves that own distinct query rows (split-KV: the two groups share rows).
-  static constexpr int QWAVES = SCHED == kSplitKV ? NW / 2 : NW;
+  // Two groups of NW/2 waves own the same query rows and split the key tiles
+  // (split-KV; the pipelined schedule with 8 waves does the same).
+  static constexpr bool SPLIT = SCHED == kSplitKV || (SCHED == kPipe && NW == 8);
+  static constexpr int QWAVES = SPLIT ? NW / 2 : NW;
   static constexpr int BR = QWAVES * QW;         // query rows per workgroup
   // Threads that stage one K/V stream (split-KV: one stream per group).
-  static constexpr int STAGERS = SCHED == kSplitKV ? THREADS / 2 : THREADS;
-  static constexpr int STREAMS = SCHED == kSplitKV ? 2 : 1;
+  static constexpr int STAGERS = SPLIT ? THREADS / 2 : THREADS;
+  static constexpr int STREAMS = SPLIT ? 2 : 1;
   static constexpr int KB = BC / 32;             // 32-key blocks per tile
   static constexpr int DB = D / 32;              // 32-row blocks of O^T
   static constexpr int DK = D / 16;              // 16-deep k-steps of S^T = K Q^T
@@ -168,7 +177,7 @@ struct Fa2Fwd {
   static constexpr int STREAMB = 4 * TILEB;      // one stream: K[0], K[1], V[0], V[1]
   // Split-KV merge area: per group-1 lane, O^T (QB*DB*16 floats) then m, l.
   static constexpr int MERGE_FLOATS = QB * DB * 16 + 2 * QB;
-  static constexpr int MERGE_BYTES = SCHED == kSplitKV ? (NW / 2) * 64 * MERGE_FLOATS * 4 : 0;
+  static constexpr int MERGE_BYTES = SPLIT ? (NW / 2) * 64 * MERGE_FLOATS * 4 : 0;
   static constexpr int LDS_BYTES = STREAMS * STREAMB > MERGE_BYTES ? STREAMS * STREAMB : MERGE_BYTES;
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert((BC * CPR) % STAGERS == 0 && CPT >= 1, "staging split");
@@ -373,11 +382,11 @@ struct Fa2Fwd {
     const int n = p.n;
     const int q0 = qtile * BR;
     // Query rows of this wave.  Split-KV: waves w and w+NW/2 own the same rows.
-    const int qwave = SCHED == kSplitKV ? wave % QWAVES : wave;
+    const int qwave = SPLIT ? wave % QWAVES : wave;
     const int qw0 = q0 + qwave * QW;
     // Split-KV: the group's K/V stream and its LDS area.
-    const int grp = SCHED == kSplitKV ? wave / QWAVES : 0;
-    const int stid = SCHED == kSplitKV ? tid % STAGERS : tid;
+    const int grp = SPLIT ? wave / QWAVES : 0;
+    const int stid = SPLIT ? tid % STAGERS : tid;
 
     const size_t slice = (size_t)bh * (size_t)n * D;  // elements before this head
     const uint32_t slice_bytes = (uint32_t)n * D * 2;
@@ -434,7 +443,16 @@ struct Fa2Fwd {
     const int kend = CAUSAL ? min(n, q0 + BR) : n;
     const int ntiles = (kend + BC - 1) / BC;
     const Ctx cx{rk, rv, lds, off, p.scale_log2, lane, tid, qw0, n, ntiles};
-    if constexpr (SCHED == kPingPong) {
+    if constexpr (SCHED == kPipe && SPLIT) {
+      // Group 0 takes key tiles [0, T0), group 1 [T0, 2*T0); tiles past the
+      // end are fully masked.  Both run T0 iterations, so their barriers pair.
+      const int t0 = (ntiles + 1) / 2;
+      run_pipe(cx, st, grp == 0 ? 0 : t0, t0);
+      merge_groups(cx, st, grp);
+      if (grp != 0) return;  // group 1 handed its state to group 0
+    } else if constexpr (SCHED == kPipe) {
+      run_pipe(cx, st, 0, ntiles);
+    } else if constexpr (SCHED == kPingPong) {
       run_pingpong(cx, st);
     } else if constexpr (SCHED == kSplitKV) {
       run_splitkv(cx, st, grp);
@@ -493,11 +511,13 @@ struct Fa2Fwd {
     }
   };
 
-  // Global -> register staging of one K or V tile (soffset = tile start).
+  // Global -> register staging of one K or V tile.  The tile offset is part of
+  // the VGPR offset, so the buffer range check covers it: rows past N (and
+  // whole tiles past the end) read as zeros.
   static __device__ __forceinline__ void stage_load(const Ctx& cx, const __amdgpu_buffer_rsrc_t& r, int j,
                                                     u32x4 (&reg)[CPT]) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) reg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, cx.off.gld[i], j * TILEB, 0);
+    for (int i = 0; i < CPT; ++i) reg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, cx.off.gld[i] + j * TILEB, 0, 0);
   }
   // Register -> LDS store of one staged tile at a compile-time LDS offset.
   template <int BASE>
@@ -557,6 +577,284 @@ struct Fa2Fwd {
     for (int j = 0; j < cx.ntiles; j += 2) {
       step(j, std::integral_constant<int, 0>{});
       if (j + 1 < cx.ntiles) step(j + 1, std::integral_constant<int, 1>{});
+    }
+  }
+
+
+  // ---- Pipelined schedule (kPipe) --------------------------------------
+  // Iteration j issues the MFMAs of S(j+1) = K(j+1) Q^T and of
+  // O^T += V(j-1)^T P(j-1)^T one at a time, each followed by its share of the
+  // softmax of tile j on the VALU, so the matrix cores and the vector ALU of a
+  // SIMD work side by side inside one wave.  The softmax of a tile uses the
+  // current exponent base without first taking the tile's row max; a tile whose
+  // probabilities could overflow (or whose base is still -inf) is caught by the
+  // size of its row sums and redone through the rebase path, which takes the
+  // row max, rescales O and l, and recomputes the probabilities.  The result is
+  // the online softmax of the pages with a lazily moved base.
+  //
+  // Every iteration runs the same instruction stream: a tile past the wave's
+  // causal diagonal is processed as a fully masked tile (its probabilities are
+  // 0), the S of the tile after the last one is computed and discarded, and
+  // P(-1) is 0 against a zeroed V buffer.  Only the masking of ragged and
+  // diagonal tiles and the rare rebase branch off.
+  //
+  // LDS: K(t) lives in K buffer t%2 and V(t) in V buffer t%2.  Iteration j
+  // reads K((j+1)%2) and V((j-1)%2), and writes K(j+2) into K(j%2) and V(j)
+  // into V(j%2); both were last read in iteration j-1, which ended with the
+  // barrier.
+
+  static constexpr int PIPE_PF = 4;  // slots between an LDS fragment read and its first use
+
+  static __device__ __forceinline__ u32x4 kfrag(const lds_char* sk, const LdsOffsets& off, int kb, int ks) {
+    return *(const __attribute__((address_space(3))) u32x4*)(sk + off.k[ks] + kb * 32 * ROWB);
+  }
+  static __device__ __forceinline__ u32x4 vfrag(const lds_char* sv, const LdsOffsets& off, int kb, int u, int db) {
+    const int rows = (kb * 32 + 16 * u) * ROWB;
+    const s16x4 va = lds_read_tr16(sv + off.v[db] + rows);
+    const s16x4 vb = lds_read_tr16(sv + off.v[db] + rows + 8 * ROWB);
+    u32x4 a;
+    a[0] = __builtin_bit_cast(u32x2, va)[0];
+    a[1] = __builtin_bit_cast(u32x2, va)[1];
+    a[2] = __builtin_bit_cast(u32x2, vb)[0];
+    a[3] = __builtin_bit_cast(u32x2, vb)[1];
+    return a;
+  }
+
+  // Keeps a value where it is computed: later code motion cannot sink the
+  // instructions that produce it past this point.
+  template <typename T>
+  static __device__ __forceinline__ void pin(T& x) {
+    asm volatile("" : "+v"(x));
+  }
+
+  // Probabilities of score registers (r0, r0+1) of block (qb, kb) against the
+  // current base, packed into the P operand; returns them for the sums.
+  template <bool GUARD>
+  static __device__ __forceinline__ void prob_pair(const Scores& sc, u32x4 (&pb)[QB][KB][2], const float (&m)[QB],
+                                                   float c2, int qb, int kb, int r0, float& p0, float& p1) {
+    const float s0 = sc.s[qb][kb][r0], s1 = sc.s[qb][kb][r0 + 1];
+    p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c2, -m[qb]));
+    p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c2, -m[qb]));
+    if constexpr (GUARD) {
+      // Hidden keys give exactly 0 (also where the exponent would be NaN:
+      // scale 0, or a row that has seen only hidden keys).
+      const float ninf = -__builtin_inff();
+      p0 = s0 == ninf ? 0.f : p0;
+      p1 = s1 == ninf ? 0.f : p1;
+    }
+    uint32_t w = pack2<BF16>(p0, p1);
+    pin(w);
+    pb[qb][kb][r0 >> 3][(r0 & 7) >> 1] = w;
+  }
+
+  // Softmax of a whole tile against the current base (no interleaving).
+  template <bool GUARD>
+  static __device__ __forceinline__ void probs_tile(const Scores& sc, u32x4 (&pb)[QB][KB][2], const float (&m)[QB],
+                                                    float c2, float (&lt)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float la = 0.f, lb = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += 2) {
+          float p0, p1;
+          prob_pair<GUARD>(sc, pb, m, c2, qb, kb, r0, p0, p1);
+          la += p0;
+          lb += p1;
+        }
+      }
+      lt[qb] = la + lb;
+    }
+  }
+
+  // Rebase path: move each row's base to its running max, rescale O and l,
+  // and recompute the tile's probabilities and sums.
+  static __device__ __forceinline__ void pipe_rebase(const Scores& sc, State& st, u32x4 (&pb)[QB][KB][2],
+                                                     float (&lt)[QB], float c2) {
+    const float ninf = -__builtin_inff();
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float ma = ninf, mb = ninf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          ma = __builtin_fmaxf(ma, sc.s[qb][kb][r]);
+          mb = __builtin_fmaxf(mb, sc.s[qb][kb][r + 1]);
+        }
+      }
+      float mx = __builtin_fmaxf(ma, mb), lo, hi;
+      halves(mx, lo, hi);
+      mx = __builtin_fmaxf(lo, hi);
+      const float mt = (mx == ninf) ? ninf : mx * c2;
+      const float m_new = __builtin_fmaxf(st.m[qb], mt);
+      const float alpha = (m_new == ninf) ? 1.f : __builtin_amdgcn_exp2f(st.m[qb] - m_new);
+      st.m[qb] = m_new;
+      st.l[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) st.o[qb][db] *= alpha;
+    }
+    probs_tile<true>(sc, pb, st.m, c2, lt);
+  }
+
+  // Accept the tile's sums, or send it through the rebase path.
+  static __device__ __forceinline__ void pipe_accept(const Scores& sc, State& st, u32x4 (&pb)[QB][KB][2],
+                                                     float (&lt)[QB], float c2) {
+    bool bad = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) bad |= !(lt[qb] <= kTileSumLimit);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) pipe_rebase(sc, st, pb, lt, c2);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) st.l[qb] += lt[qb];
+  }
+
+  // The interleaved body of iteration j.  B = j % 2.
+  template <int B>
+  static __device__ __forceinline__ void pipe_body(const Ctx& cx, State& st, Scores (&sc)[2],
+                                                   u32x4 (&pb)[2][QB][KB][2], float (&lt)[QB]) {
+    const lds_char* sk = cx.lds + (1 - B) * TILEB;  // K(j+1)
+    const lds_char* sv = cx.lds + (3 - B) * TILEB;  // V(j-1)
+    constexpr int NMF = KB * DK * QB;               // MFMAs of each product (S and P V alike)
+    constexpr int NSLOT = 2 * NMF;
+    constexpr int NPAIR = QB * KB * 8;              // probability pairs of tile j
+    constexpr int NKF = KB * DK, NVF = KB * 2 * DB;
+    static_assert(KB * 2 * DB * QB == NMF, "S and P V have equally many MFMAs");
+    u32x4 kf[NKF], vf[NVF];
+    float la[QB], lb[QB];
+#pragma unroll
+    for (int s = 0; s < NSLOT; ++s) {
+      // LDS fragments first used PIPE_PF slots from now (all of the first
+      // PIPE_PF slots' fragments at slot 0).
+#pragma unroll
+      for (int f = 0; f < NKF; ++f) {
+        const int use = 2 * f * QB;
+        if ((use - PIPE_PF > 0 ? use - PIPE_PF : 0) == s) kf[f] = kfrag(sk, cx.off, f / DK, f % DK);
+      }
+#pragma unroll
+      for (int g = 0; g < NVF; ++g) {
+        const int use = 2 * g * QB + 1;
+        if ((use - PIPE_PF > 0 ? use - PIPE_PF : 0) == s) vf[g] = vfrag(sv, cx.off, g / (2 * DB), (g / DB) % 2, g % DB);
+      }
+      const int t = s / 2;
+      if (s % 2 == 0) {
+        // S MFMA t: K fragment (kb, ks), query block qb.
+        const int qb = t % QB, f = t / QB, kb = f / DK, ks = f % DK;
+        sc[1 - B].s[qb][kb] = mfma32<BF16>(kf[f], st.qf[qb][ks], ks == 0 ? f32x16{} : sc[1 - B].s[qb][kb]);
+      } else {
+        // P V MFMA t: V fragment (kb, u, db), query block qb.
+        const int qb = t % QB, g = t / QB, kb = g / (2 * DB), u = (g / DB) % 2, db = g % DB;
+        st.o[qb][db] = mfma32<BF16>(vf[g], pb[1 - B][qb][kb][u], st.o[qb][db]);
+      }
+#pragma unroll
+      for (int c = s * NPAIR / NSLOT; c < (s + 1) * NPAIR / NSLOT; ++c) {
+        const int qb = c / (KB * 8), kb = (c / 8) % KB, r0 = 2 * (c % 8);
+        float p0, p1;
+        prob_pair<false>(sc[B], pb[B], st.m, cx.c2, qb, kb, r0, p0, p1);
+        if (kb == 0 && r0 == 0) {
+          la[qb] = p0;
+          lb[qb] = p1;
+        } else {
+          la[qb] += p0;
+          lb[qb] += p1;
+        }
+        pin(la[qb]);
+        pin(lb[qb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lt[qb] = la[qb] + lb[qb];
+  }
+
+  template <int B>
+  static __device__ __forceinline__ void pipe_iter(const Ctx& cx, State& st, Scores (&sc)[2],
+                                                   u32x4 (&pb)[2][QB][KB][2], u32x4 (&stk)[CPT],
+                                                   u32x4 (&stv)[CPT], int j) {
+    // K(j+2) and V(j); past the last tile the range check returns zeros.
+    stage_load(cx, cx.rk, j + 2, stk);
+    stage_load(cx, cx.rv, j, stv);
+    if (!cx.active(j) || cx.masked(j)) mask_scores(sc[B], cx.lane, j * BC, cx.qw0, cx.n);
+    float lt[QB];
+    pipe_body<B>(cx, st, sc, pb, lt);
+    pipe_accept(sc[B], st, pb[B], lt, cx.c2);
+    stage_store_k<B * TILEB>(cx, stk);
+    stage_store_v<(2 + B) * TILEB>(cx, stv);
+    __syncthreads();
+  }
+
+  // Tiles first .. first+count-1 (count >= 1) through the pipeline.
+  static __device__ __forceinline__ void run_pipe(const Ctx& cx, State& st, int first, int count) {
+    Scores sc[2];
+    u32x4 pb[2][QB][KB][2];
+    u32x4 stk[CPT], stv[CPT];
+    // P(first-1) = 0 against a zeroed V buffer 1 (0 * garbage could be NaN).
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) pb[1][qb][kb][0] = pb[1][qb][kb][1] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) stv[i] = u32x4{0u, 0u, 0u, 0u};
+    stage_store_v<3 * TILEB>(cx, stv);
+    // K(first) into K buffer 0.
+    stage_load(cx, cx.rk, first, stk);
+    stage_store_k<0>(cx, stk);
+    __syncthreads();
+    // Iteration -1: S(first); K(first+1) into K buffer 1.
+    stage_load(cx, cx.rk, first + 1, stk);
+    scores(cx.lds, cx.off, st.qf, sc[0]);
+    stage_store_k<TILEB>(cx, stk);
+    __syncthreads();
+    for (int s = 0; s < count; s += 2) {
+      pipe_iter<0>(cx, st, sc, pb, stk, stv, first + s);
+      if (s + 1 < count) pipe_iter<1>(cx, st, sc, pb, stk, stv, first + s + 1);
+    }
+    // Iteration count: P V of the last tile.
+    if ((count - 1) % 2 == 0)
+      pv(cx.lds + 2 * TILEB, cx.off, pb[0], st.o);
+    else
+      pv(cx.lds + 3 * TILEB, cx.off, pb[1], st.o);
+  }
+
+  // Split-KV merge: group 1 leaves (O, m, l) in LDS and group 0 combines them
+  // lane by lane with the algebra of the online update.  The K/V buffers are
+  // free once both groups have passed their last barrier.
+  static __device__ __forceinline__ void merge_groups(const Ctx& cx, State& st, int grp) {
+    typedef __attribute__((address_space(3))) float lds_float;
+    __syncthreads();
+    const int slot = (cx.tid % STAGERS) * MERGE_FLOATS;  // same slot for waves w and w+NW/2
+    lds_float* mb = (lds_float*)cx.lds + slot;
+    if (grp != 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mb[(qb * DB + db) * 16 + r] = st.o[qb][db][r];
+        }
+        mb[QB * DB * 16 + 2 * qb] = st.m[qb];
+        mb[QB * DB * 16 + 2 * qb + 1] = st.l[qb];
+      }
+    }
+    __syncthreads();
+    if (grp == 0) {
+      const float ninf = -__builtin_inff();
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m1 = mb[QB * DB * 16 + 2 * qb];
+        const float l1 = mb[QB * DB * 16 + 2 * qb + 1];
+        const float m0 = st.m[qb];
+        const float mm = __builtin_fmaxf(m0, m1);
+        const float a0 = (m0 == ninf) ? 0.f : __builtin_amdgcn_exp2f(m0 - mm);
+        const float a1 = (m1 == ninf) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+        st.m[qb] = mm;
+        st.l[qb] = a0 * st.l[qb] + a1 * l1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st.o[qb][db][r] = a0 * st.o[qb][db][r] + a1 * mb[(qb * DB + db) * 16 + r];
+        }
+      }
     }
   }
 
@@ -666,43 +964,7 @@ struct Fa2Fwd {
       if (s + 1 < T0) step(s + 1, std::integral_constant<int, 1>{});
     }
 
-    // Merge (the tile buffers are free after the last barrier).
-    typedef __attribute__((address_space(3))) float lds_float;
-    const int slot = (cx.tid % (STAGERS)) * MERGE_FLOATS;  // same slot for waves w and w+NW/2
-    lds_float* mb = (lds_float*)cx.lds + slot;
-    if (grp != 0) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mb[(qb * DB + db) * 16 + r] = st.o[qb][db][r];
-        }
-        mb[QB * DB * 16 + 2 * qb] = st.m[qb];
-        mb[QB * DB * 16 + 2 * qb + 1] = st.l[qb];
-      }
-    }
-    __syncthreads();
-    if (grp == 0) {
-      const float ninf = -__builtin_inff();
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float m1 = mb[QB * DB * 16 + 2 * qb];
-        const float l1 = mb[QB * DB * 16 + 2 * qb + 1];
-        const float m0 = st.m[qb];
-        const float mm = __builtin_fmaxf(m0, m1);
-        const float a0 = (m0 == ninf) ? 0.f : __builtin_amdgcn_exp2f(m0 - mm);
-        const float a1 = (m1 == ninf) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
-        st.m[qb] = mm;
-        st.l[qb] = a0 * st.l[qb] + a1 * l1;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            st.o[qb][db][r] = a0 * st.o[qb][db][r] + a1 * mb[(qb * DB + db) * 16 + r];
-        }
-      }
-    }
+    merge_groups(cx, st, grp);
   }
 };
 
