@@ -28,8 +28,8 @@ def build_command(out: str = LIB_PATH) -> list:
         hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
         # Packed fp32 VALU forms are kept out of the generated code.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA results in arch VGPRs: the softmax reads the score accumulators
-        # with VALU instructions, which cannot address AGPRs directly.
+        # MFMA results in arch VGPRs unless a kernel asks for AGPRs: the
+        # softmax reads the score accumulators with VALU instructions.
         "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", os.path.join(REPO_DIR, "include"),
         "-I", os.path.join(PKG_DIR, "csrc"),

@@ -89,6 +89,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// The descriptor make_rsrc builds, as its four dwords: base address (48 bits,
+// stride 0), number of bytes, word 3.  Uniform across the wave.
+__device__ __forceinline__ u32x4 rsrc_words(const void* tensor, size_t byte_off, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)tensor + byte_off;
+  u32x4 w;
+  w[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  w[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  w[2] = __builtin_amdgcn_readfirstlane(bytes);
+  w[3] = (uint32_t)kRsrcWord3;
+  return w;
+}
+
 // Values of the pair of lanes L and L^32: (lower-half lane's, upper-half lane's),
 // identical in both lanes of the pair.
 __device__ __forceinline__ void halves(float x, float& lo, float& hi) {
@@ -105,6 +117,50 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
   } else {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// Output MFMA of the pipelined schedule for head dims of 128 and more: the
+// O^T accumulators are kept in AGPRs (only MFMAs and the rare rescale touch
+// them), which leaves the arch VGPRs to the scores, probabilities and LDS
+// fragments.  Dependent MFMAs of one accumulator are always separated by other
+// MFMAs, and nothing else reads O until after an explicit wait (see pipe_sub).
+// Score MFMAs of the same schedule: Q^T (only MFMAs read it) in AGPRs, the
+// scores in arch VGPRs for the softmax.
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma32_qa0(const u32x4& a, const u32x4& q) {
+  f32x16 d;
+  if constexpr (BF16)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(q));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(q));
+  return d;
+}
+template <bool BF16>
+__device__ __forceinline__ void mfma32_qa(f32x16& c, const u32x4& a, const u32x4& q) {
+  if constexpr (BF16)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(q));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(q));
+}
+
+template <bool BF16>
+__device__ __forceinline__ void mfma32_acc_agpr(f32x16& c, const u32x4& a, const u32x4& b) {
+  if constexpr (BF16)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 16x16x32 MFMA, used to sum probabilities on the matrix cores.
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
 }
 
@@ -174,7 +230,10 @@ struct Fa2Fwd {
   static constexpr int TILEB = BC * ROWB;        // bytes per K (or V) tile
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int CPT = BC * CPR / STAGERS; // chunks per thread per tile (each of K, V)
-  static constexpr int STREAMB = 4 * TILEB;      // one stream: K[0], K[1], V[0], V[1]
+  // One K/V stream in LDS: two tiles each of K and V (the pipelined
+  // schedule keeps a ring of four of each).
+  static constexpr int SLOTS = SCHED == kPipe ? 4 : 2;
+  static constexpr int STREAMB = 2 * SLOTS * TILEB;
   // Split-KV merge area: per group-1 lane, O^T (QB*DB*16 floats) then m, l.
   static constexpr int MERGE_FLOATS = QB * DB * 16 + 2 * QB;
   static constexpr int MERGE_BYTES = SPLIT ? (NW / 2) * 64 * MERGE_FLOATS * 4 : 0;
@@ -185,7 +244,7 @@ struct Fa2Fwd {
   // Every LDS access in the tile loop is a lane base register plus a
   // compile-time offset; keeping the tile buffers under 64 KiB lets the
   // offsets ride in the instruction's 16-bit immediate.
-  static_assert(STREAMS * STREAMB <= 65536, "LDS image must fit the ds immediate offset");
+  static_assert(STREAMB <= 65536, "LDS image must fit the ds immediate offset");
 
   typedef __attribute__((address_space(3))) char lds_char;
 
@@ -196,6 +255,8 @@ struct Fa2Fwd {
     int kst[CPT];  // staging store of chunk j, K layout
     int vst[CPT];  // staging store of chunk j, V layout
     int gld[CPT];  // global byte offset of chunk j inside a tile
+    int gdk[CPT];  // global byte offset of the K chunk a direct-to-LDS load lands at linear slot j
+    int dma;       // this wave's first linear slot (bytes) of a direct-to-LDS tile load
   };
 
   // S^T accumulators of one tile for all query blocks of the wave.
@@ -437,16 +498,22 @@ struct Fa2Fwd {
         off.kst[j] = sbase + r * ROWB + ((col ^ swz_k<D>(r)) << 4);
         off.vst[j] = sbase + r * ROWB + ((col ^ swz_v(r)) << 4);
         off.gld[j] = (r * D + col * 8) * 2;
+        // A direct-to-LDS load writes lane L's 16 bytes at the wave's base +
+        // 16 L, i.e. linear slot c; that slot of the swizzled K layout holds
+        // global chunk col ^ swz(r) (the swizzle is an involution).
+        off.gdk[j] = (r * D + (col ^ swz_k<D>(r)) * 8) * 2;
       }
+      off.dma = __builtin_amdgcn_readfirstlane(sbase + (stid & ~63) * 16);
     }
 
     const int kend = CAUSAL ? min(n, q0 + BR) : n;
     const int ntiles = (kend + BC - 1) / BC;
-    const Ctx cx{rk, rv, lds, off, p.scale_log2, lane, tid, qw0, n, ntiles};
+    const Ctx cx{rk, rv, rsrc_words(p.k, slice * 2, slice_bytes), rsrc_words(p.v, slice * 2, slice_bytes), ones_operand(lane), lds, off, p.scale_log2, lane, tid, qw0, n, ntiles};
     if constexpr (SCHED == kPipe && SPLIT) {
-      // Group 0 takes key tiles [0, T0), group 1 [T0, 2*T0); tiles past the
-      // end are fully masked.  Both run T0 iterations, so their barriers pair.
-      const int t0 = (ntiles + 1) / 2;
+      // Group 0 takes key tiles [0, T0) with T0 even, group 1 [T0, 2*T0);
+      // tiles past the end are fully masked.  Both run T0 sub-iterations, so
+      // their barriers pair.
+      const int t0 = 2 * ((ntiles + 3) / 4);
       run_pipe(cx, st, grp == 0 ? 0 : t0, t0);
       merge_groups(cx, st, grp);
       if (grp != 0) return;  // group 1 handed its state to group 0
@@ -467,7 +534,7 @@ struct Fa2Fwd {
       const int qrow = qw0 + 32 * qb + (lane & 31);
       float l_lo, l_hi;
       halves(st.l[qb], l_lo, l_hi);
-      const float l_tot = l_lo + l_hi;
+      const float l_tot = L_FULL ? st.l[qb] : l_lo + l_hi;
       const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -493,12 +560,17 @@ struct Fa2Fwd {
     u32x4 qf[QB][DK];  // Q^T operands
     f32x16 o[QB][DB];  // O^T accumulators
     float m[QB];       // exponent base per row (base-2 domain)
-    float l[QB];       // this lane's share of the row sum
+    float l[QB];       // row sum: this lane's share (or all of it, L_FULL)
+    float lc[QB][2];   // pipelined schedule: row sums of queries lane%16 and 16 + lane%16
   };
+  // The pipelined schedule ends with each lane holding its row's whole sum.
+  static constexpr bool L_FULL = SCHED == kPipe;
 
   // Loop-invariant context.
   struct Ctx {
     __amdgpu_buffer_rsrc_t rk, rv;
+    u32x4 wk, wv;  // the same K and V buffer descriptors as raw words (for inline asm)
+    u32x4 ones;    // A operand of the row-sum MFMA (see ones_operand)
     lds_char* lds;
     LdsOffsets off;
     float c2;
@@ -530,6 +602,29 @@ struct Fa2Fwd {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) *(__attribute__((address_space(3))) u32x4*)(cx.lds + BASE + cx.off.vst[i]) = reg[i];
   }
+
+  // Global -> LDS loads of one K or V tile straight into LDS buffer BASE (no
+  // VGPR staging); rows past N read as zeros.  The data is in LDS once the
+  // wave's vector-memory counter has drained (dma_wait).  The load is written
+  // as inline asm so that the compiler, which cannot tell these LDS writes
+  // from the fragment reads of other buffers, does not drain the counter
+  // before every LDS read; dma_wait before each barrier is the only wait.
+  static __device__ __forceinline__ void dma16(const u32x4& rsrc, const lds_char* dst, int voffset) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %0\n s_nop 0\n buffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(m0), "v"(voffset), "s"(rsrc) : "memory", "m0");
+  }
+  template <int BASE>
+  static __device__ __forceinline__ void stage_dma_k(const Ctx& cx, int tile) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) dma16(cx.wk, cx.lds + BASE + cx.off.dma + STAGERS * 16 * i, cx.off.gdk[i] + tile * TILEB);
+  }
+  template <int BASE>
+  static __device__ __forceinline__ void stage_dma_v(const Ctx& cx, int tile) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) dma16(cx.wv, cx.lds + BASE + cx.off.dma + STAGERS * 16 * i, cx.off.gld[i] + tile * TILEB);
+  }
+  static __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
   // Softmax of tile j: scores -> probabilities (packed) and the online update.
   static __device__ __forceinline__ void softmax_tile(const Ctx& cx, State& st, Scores& sc, int j,
@@ -603,7 +698,9 @@ struct Fa2Fwd {
   // into V(j%2); both were last read in iteration j-1, which ended with the
   // barrier.
 
-  static constexpr int PIPE_PF = 4;  // slots between an LDS fragment read and its first use
+  static constexpr int PIPE_PF = 4;    // positions between an LDS fragment read and its first use
+  static constexpr int PIPE_LEAD = 2;  // positions of softmax work before the first MFMA
+  static constexpr bool O_AGPR = D >= 128;  // output accumulators in AGPRs (see mfma32_acc_agpr)
 
   static __device__ __forceinline__ u32x4 kfrag(const lds_char* sk, const LdsOffsets& off, int kb, int ks) {
     return *(const __attribute__((address_space(3))) u32x4*)(sk + off.k[ks] + kb * 32 * ROWB);
@@ -650,28 +747,52 @@ struct Fa2Fwd {
   // Softmax of a whole tile against the current base (no interleaving).
   template <bool GUARD>
   static __device__ __forceinline__ void probs_tile(const Scores& sc, u32x4 (&pb)[QB][KB][2], const float (&m)[QB],
-                                                    float c2, float (&lt)[QB]) {
+                                                    float c2) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float la = 0.f, lb = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r0 = 0; r0 < 16; r0 += 2) {
           float p0, p1;
           prob_pair<GUARD>(sc, pb, m, c2, qb, kb, r0, p0, p1);
-          la += p0;
-          lb += p1;
         }
       }
-      lt[qb] = la + lb;
     }
   }
 
-  // Rebase path: move each row's base to its running max, rescale O and l,
-  // and recompute the tile's probabilities and sums.
-  static __device__ __forceinline__ void pipe_rebase(const Scores& sc, State& st, u32x4 (&pb)[QB][KB][2],
-                                                     float (&lt)[QB], float c2) {
+  // Row sums on the matrix cores.  The packed probabilities of k-step u are
+  // the B operand of the output MFMA (lane L: query L%32, eight keys of the
+  // 16-key step).  Read as the B operand of a 16x16x32 MFMA, lane L's eight
+  // values sit in column L%16 and k-group L/16; with A[i][k] = 1 where
+  // (k/8)%2 == i%2 (else 0), row i of the result is the sum over the step's
+  // keys of query L%16 (i even) or 16 + L%16 (i odd).  In the 16x16 result
+  // lane L holds rows 4(L/16)+r, so register r = 0 is query L%16 and r = 1 is
+  // query 16 + L%16.  These are the sums of the rounded probabilities that the
+  // output MFMA consumes.
+  static __device__ __forceinline__ u32x4 ones_operand(int lane) {
+    const uint32_t one = BF16 ? 0x3f803f80u : 0x3c003c00u;
+    const uint32_t w = (((lane >> 4) & 1) == (lane & 1)) ? one : 0u;
+    return u32x4{w, w, w, w};
+  }
+  // Sums of one tile's probabilities for every query block.
+  static __device__ __forceinline__ void tile_sums(const u32x4& ones, const u32x4 (&pb)[QB][KB][2], f32x4 (&ct)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int g = 0; g < KB * 2; ++g) ct[qb] = mfma16<BF16>(ones, pb[qb][g / 2][g % 2], g == 0 ? f32x4{} : ct[qb]);
+    }
+  }
+
+  // Value of `x` held by lane `src` (every lane reads).
+  static __device__ __forceinline__ float lane_value(float x, int src) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+  }
+
+  // Rebase path: move each row's base to its running max, rescale O and the
+  // row sums, and recompute the tile's probabilities and sums.
+  static __device__ __forceinline__ void pipe_rebase(const Ctx& cx, const Scores& sc, State& st,
+                                                     u32x4 (&pb)[QB][KB][2], f32x4 (&ct)[QB]) {
     const float ninf = -__builtin_inff();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -687,133 +808,182 @@ struct Fa2Fwd {
       float mx = __builtin_fmaxf(ma, mb), lo, hi;
       halves(mx, lo, hi);
       mx = __builtin_fmaxf(lo, hi);
-      const float mt = (mx == ninf) ? ninf : mx * c2;
+      const float mt = (mx == ninf) ? ninf : mx * cx.c2;
       const float m_new = __builtin_fmaxf(st.m[qb], mt);
       const float alpha = (m_new == ninf) ? 1.f : __builtin_amdgcn_exp2f(st.m[qb] - m_new);
       st.m[qb] = m_new;
-      st.l[qb] *= alpha;
+      // alpha of query q lives in lanes q and q+32.
+      st.lc[qb][0] *= lane_value(alpha, cx.lane & 15);
+      st.lc[qb][1] *= lane_value(alpha, 16 + (cx.lane & 15));
 #pragma unroll
       for (int db = 0; db < DB; ++db) st.o[qb][db] *= alpha;
     }
-    probs_tile<true>(sc, pb, st.m, c2, lt);
+    probs_tile<true>(sc, pb, st.m, cx.c2);
+    tile_sums(cx.ones, pb, ct);
   }
 
-  // Accept the tile's sums, or send it through the rebase path.
-  static __device__ __forceinline__ void pipe_accept(const Scores& sc, State& st, u32x4 (&pb)[QB][KB][2],
-                                                     float (&lt)[QB], float c2) {
+  // Accept the tile's sums, or send it through the rebase path.  A sum above
+  // the limit (or not a number: an exponent base still at -inf) means some
+  // probability may have overflowed.
+  static __device__ __forceinline__ void pipe_accept(const Ctx& cx, const Scores& sc, State& st,
+                                                     u32x4 (&pb)[QB][KB][2], f32x4 (&ct)[QB]) {
     bool bad = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) bad |= !(lt[qb] <= kTileSumLimit);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) pipe_rebase(sc, st, pb, lt, c2);
+    for (int qb = 0; qb < QB; ++qb) bad |= !(ct[qb][0] <= kTileSumLimit) || !(ct[qb][1] <= kTileSumLimit);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) pipe_rebase(cx, sc, st, pb, ct);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) st.l[qb] += lt[qb];
+    for (int qb = 0; qb < QB; ++qb) {
+      st.lc[qb][0] += ct[qb][0];
+      st.lc[qb][1] += ct[qb][1];
+    }
   }
 
-  // The interleaved body of iteration j.  B = j % 2.
-  template <int B>
+  // The interleaved body of iteration j; S4 = (j - first) % 4 names the ring
+  // slots: K(j+1) in K slot (S4+1)%4, V(j-1) in V slot (S4+3)%4, and the
+  // score/probability register sets alternate with j.
+  template <int S4>
   static __device__ __forceinline__ void pipe_body(const Ctx& cx, State& st, Scores (&sc)[2],
-                                                   u32x4 (&pb)[2][QB][KB][2], float (&lt)[QB]) {
-    const lds_char* sk = cx.lds + (1 - B) * TILEB;  // K(j+1)
-    const lds_char* sv = cx.lds + (3 - B) * TILEB;  // V(j-1)
+                                                   u32x4 (&pb)[2][QB][KB][2], f32x4 (&ct)[QB]) {
+    constexpr int B = S4 % 2;
+    const lds_char* sk = cx.lds + ((S4 + 1) % 4) * TILEB;      // K(j+1)
+    const lds_char* sv = cx.lds + (4 + (S4 + 3) % 4) * TILEB;  // V(j-1)
     constexpr int NMF = KB * DK * QB;               // MFMAs of each product (S and P V alike)
     constexpr int NSLOT = 2 * NMF;
     constexpr int NPAIR = QB * KB * 8;              // probability pairs of tile j
     constexpr int NKF = KB * DK, NVF = KB * 2 * DB;
     static_assert(KB * 2 * DB * QB == NMF, "S and P V have equally many MFMAs");
     u32x4 kf[NKF], vf[NVF];
-    float la[QB], lb[QB];
+    // Position i issues MFMA i - PIPE_LEAD (S and P V alternating) and the
+    // softmax pairs of slot i; LDS fragments are read PIPE_PF positions before
+    // their MFMA (all early ones at position 0), so the softmax work of the
+    // first positions covers the LDS latency.
 #pragma unroll
-    for (int s = 0; s < NSLOT; ++s) {
-      // LDS fragments first used PIPE_PF slots from now (all of the first
-      // PIPE_PF slots' fragments at slot 0).
+    for (int i = 0; i < NSLOT + PIPE_LEAD; ++i) {
 #pragma unroll
       for (int f = 0; f < NKF; ++f) {
-        const int use = 2 * f * QB;
-        if ((use - PIPE_PF > 0 ? use - PIPE_PF : 0) == s) kf[f] = kfrag(sk, cx.off, f / DK, f % DK);
+        const int use = 2 * f * QB + PIPE_LEAD;
+        if ((use - PIPE_PF > 0 ? use - PIPE_PF : 0) == i) kf[f] = kfrag(sk, cx.off, f / DK, f % DK);
       }
 #pragma unroll
       for (int g = 0; g < NVF; ++g) {
-        const int use = 2 * g * QB + 1;
-        if ((use - PIPE_PF > 0 ? use - PIPE_PF : 0) == s) vf[g] = vfrag(sv, cx.off, g / (2 * DB), (g / DB) % 2, g % DB);
+        const int use = 2 * g * QB + 1 + PIPE_LEAD;
+        if ((use - PIPE_PF > 0 ? use - PIPE_PF : 0) == i) vf[g] = vfrag(sv, cx.off, g / (2 * DB), (g / DB) % 2, g % DB);
       }
-      const int t = s / 2;
-      if (s % 2 == 0) {
-        // S MFMA t: K fragment (kb, ks), query block qb.
-        const int qb = t % QB, f = t / QB, kb = f / DK, ks = f % DK;
-        sc[1 - B].s[qb][kb] = mfma32<BF16>(kf[f], st.qf[qb][ks], ks == 0 ? f32x16{} : sc[1 - B].s[qb][kb]);
-      } else {
-        // P V MFMA t: V fragment (kb, u, db), query block qb.
-        const int qb = t % QB, g = t / QB, kb = g / (2 * DB), u = (g / DB) % 2, db = g % DB;
-        st.o[qb][db] = mfma32<BF16>(vf[g], pb[1 - B][qb][kb][u], st.o[qb][db]);
-      }
-#pragma unroll
-      for (int c = s * NPAIR / NSLOT; c < (s + 1) * NPAIR / NSLOT; ++c) {
-        const int qb = c / (KB * 8), kb = (c / 8) % KB, r0 = 2 * (c % 8);
-        float p0, p1;
-        prob_pair<false>(sc[B], pb[B], st.m, cx.c2, qb, kb, r0, p0, p1);
-        if (kb == 0 && r0 == 0) {
-          la[qb] = p0;
-          lb[qb] = p1;
+      const int s = i - PIPE_LEAD;
+      if (s >= 0) {
+        const int t = s / 2;
+        if (s % 2 == 0) {
+          // S MFMA t: K fragment (kb, ks), query block qb.
+          const int qb = t % QB, f = t / QB, kb = f / DK, ks = f % DK;
+          if constexpr (O_AGPR) {
+            if (ks == 0)
+              sc[1 - B].s[qb][kb] = mfma32_qa0<BF16>(kf[f], st.qf[qb][ks]);
+            else
+              mfma32_qa<BF16>(sc[1 - B].s[qb][kb], kf[f], st.qf[qb][ks]);
+          } else {
+            sc[1 - B].s[qb][kb] = mfma32<BF16>(kf[f], st.qf[qb][ks], ks == 0 ? f32x16{} : sc[1 - B].s[qb][kb]);
+          }
         } else {
-          la[qb] += p0;
-          lb[qb] += p1;
+          // P V MFMA t: V fragment (kb, u, db), query block qb.
+          const int qb = t % QB, g = t / QB, kb = g / (2 * DB), u = (g / DB) % 2, db = g % DB;
+          if constexpr (O_AGPR)
+            mfma32_acc_agpr<BF16>(st.o[qb][db], vf[g], pb[1 - B][qb][kb][u]);
+          else
+            st.o[qb][db] = mfma32<BF16>(vf[g], pb[1 - B][qb][kb][u], st.o[qb][db]);
         }
-        pin(la[qb]);
-        pin(lb[qb]);
+      }
+      if (i < NSLOT) {
+#pragma unroll
+        for (int c = i * NPAIR / NSLOT; c < (i + 1) * NPAIR / NSLOT; ++c) {
+          const int qb = c / (KB * 8), kb = (c / 8) % KB, r0 = 2 * (c % 8);
+          float p0, p1;
+          prob_pair<false>(sc[B], pb[B], st.m, cx.c2, qb, kb, r0, p0, p1);
+          if (c % 4 == 3) {
+            // Group (qb, kb, u) of four packed words is complete: its sums.
+            const int g = (c / 4) % (KB * 2);
+            ct[qb] = mfma16<BF16>(cx.ones, pb[B][qb][kb][(c % 8) / 4], g == 0 ? f32x4{} : ct[qb]);
+          }
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) lt[qb] = la[qb] + lb[qb];
   }
 
-  template <int B>
-  static __device__ __forceinline__ void pipe_iter(const Ctx& cx, State& st, Scores (&sc)[2],
-                                                   u32x4 (&pb)[2][QB][KB][2], u32x4 (&stk)[CPT],
-                                                   u32x4 (&stv)[CPT], int j) {
-    // K(j+2) and V(j); past the last tile the range check returns zeros.
-    stage_load(cx, cx.rk, j + 2, stk);
-    stage_load(cx, cx.rv, j, stv);
+  // Sub-iteration j (S4 = (j - first) % 4): S(j+1), softmax(j), P(j-1)V(j-1).
+  template <int S4>
+  static __device__ __forceinline__ void pipe_sub(const Ctx& cx, State& st, Scores (&sc)[2],
+                                                  u32x4 (&pb)[2][QB][KB][2], int j) {
+    constexpr int B = S4 % 2;
     if (!cx.active(j) || cx.masked(j)) mask_scores(sc[B], cx.lane, j * BC, cx.qw0, cx.n);
-    float lt[QB];
-    pipe_body<B>(cx, st, sc, pb, lt);
-    pipe_accept(sc[B], st, pb[B], lt, cx.c2);
-    stage_store_k<B * TILEB>(cx, stk);
-    stage_store_v<(2 + B) * TILEB>(cx, stv);
+    f32x4 ct[QB];
+    pipe_body<S4>(cx, st, sc, pb, ct);
+    // With O and Q^T in AGPRs the MFMAs above are inline asm the compiler does
+    // not track: keep every other reader of their results (the softmax of the
+    // next tile, the rebase path, the final output MFMA issued by the
+    // compiler) more than an MFMA result latency away.
+    if constexpr (O_AGPR) asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
+    pipe_accept(cx, sc[B], st, pb[B], ct);
+  }
+
+  // Pair of sub-iterations j = first + r, first + r + 1 (P2 = (r / 2) % 2)
+  // and one barrier.  At its start the pair sends the tiles the next pair
+  // reads straight to LDS: K(r+3), K(r+4) into K slots (r+3)%4, r%4 and V(r+1),
+  // V(r+2) into V slots (r+1)%4, (r+2)%4 (r relative to first).  Those slots
+  // were last read in the previous pair, which ended with the barrier; the
+  // loads have landed once every wave has drained its vector-memory counter
+  // before this pair's barrier.
+  template <int P2>
+  static __device__ __forceinline__ void pipe_pair(const Ctx& cx, State& st, Scores (&sc)[2],
+                                                   u32x4 (&pb)[2][QB][KB][2], int first, int r) {
+    stage_dma_k<((2 * P2 + 3) % 4) * TILEB>(cx, first + r + 3);
+    stage_dma_k<((2 * P2) % 4) * TILEB>(cx, first + r + 4);
+    stage_dma_v<(4 + (2 * P2 + 1) % 4) * TILEB>(cx, first + r + 1);
+    stage_dma_v<(4 + (2 * P2 + 2) % 4) * TILEB>(cx, first + r + 2);
+    pipe_sub<2 * P2>(cx, st, sc, pb, first + r);
+    pipe_sub<2 * P2 + 1>(cx, st, sc, pb, first + r + 1);
+    dma_wait();
     __syncthreads();
   }
 
-  // Tiles first .. first+count-1 (count >= 1) through the pipeline.
+  // Tiles first .. first+count-1 (count >= 1) through the pipeline, in pairs;
+  // with an odd count the last pair's second tile lies past the range and is
+  // fully masked (keys past N, or past the causal bound of every row).
   static __device__ __forceinline__ void run_pipe(const Ctx& cx, State& st, int first, int count) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) st.lc[qb][0] = st.lc[qb][1] = 0.f;
     Scores sc[2];
     u32x4 pb[2][QB][KB][2];
-    u32x4 stk[CPT], stv[CPT];
-    // P(first-1) = 0 against a zeroed V buffer 1 (0 * garbage could be NaN).
+    u32x4 stg[CPT];
+    // P(first-1) = 0 against a zeroed V slot 3 (0 * garbage could be NaN).
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) pb[1][qb][kb][0] = pb[1][qb][kb][1] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) stv[i] = u32x4{0u, 0u, 0u, 0u};
-    stage_store_v<3 * TILEB>(cx, stv);
-    // K(first) into K buffer 0.
-    stage_load(cx, cx.rk, first, stk);
-    stage_store_k<0>(cx, stk);
+    for (int i = 0; i < CPT; ++i) stg[i] = u32x4{0u, 0u, 0u, 0u};
+    stage_store_v<7 * TILEB>(cx, stg);
+    // K(first..first+2) into K slots 0..2, V(first) into V slot 0.
+    stage_dma_k<0>(cx, first);
+    stage_dma_k<TILEB>(cx, first + 1);
+    stage_dma_k<2 * TILEB>(cx, first + 2);
+    stage_dma_v<4 * TILEB>(cx, first);
+    dma_wait();
     __syncthreads();
-    // Iteration -1: S(first); K(first+1) into K buffer 1.
-    stage_load(cx, cx.rk, first + 1, stk);
-    scores(cx.lds, cx.off, st.qf, sc[0]);
-    stage_store_k<TILEB>(cx, stk);
-    __syncthreads();
-    for (int s = 0; s < count; s += 2) {
-      pipe_iter<0>(cx, st, sc, pb, stk, stv, first + s);
-      if (s + 1 < count) pipe_iter<1>(cx, st, sc, pb, stk, stv, first + s + 1);
+    scores(cx.lds, cx.off, st.qf, sc[0]);  // S(first)
+    __syncthreads();  // K slot 0 is rewritten at the end of the first pair
+    const int count2 = (count + 1) & ~1;
+    for (int r = 0; r < count2; r += 4) {
+      pipe_pair<0>(cx, st, sc, pb, first, r);
+      if (r + 2 < count2) pipe_pair<1>(cx, st, sc, pb, first, r + 2);
     }
-    // Iteration count: P V of the last tile.
-    if ((count - 1) % 2 == 0)
-      pv(cx.lds + 2 * TILEB, cx.off, pb[0], st.o);
+    // P V of the last tile (relative index count2-1: odd, V slot (count2-1)%4).
+    if (count2 % 4 == 0)
+      pv(cx.lds + 7 * TILEB, cx.off, pb[1], st.o);
     else
-      pv(cx.lds + 3 * TILEB, cx.off, pb[1], st.o);
+      pv(cx.lds + 5 * TILEB, cx.off, pb[1], st.o);
+    // Each lane keeps the whole sum of its query (lane%32).
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) st.l[qb] = (cx.lane & 16) ? st.lc[qb][1] : st.lc[qb][0];
   }
 
   // Split-KV merge: group 1 leaves (O, m, l) in LDS and group 0 combines them

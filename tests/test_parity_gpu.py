@@ -130,3 +130,46 @@ def test_bad_argument_launches_nothing(gpu_device):
     torch.cuda.synchronize()
     assert st == FA2_ERR_UNSUPPORTED_HEAD_DIM
     assert torch.all(o == 7.0) and torch.all(lse == 7.0)
+
+
+def _spiky_inputs(B, H, N, d, dtype, seed, factor, where):
+    """N(0,1) inputs whose keys at the given relative positions are scaled by
+    ``factor``: the running row max jumps in the middle of the key sequence,
+    so the online softmax must move its exponent base (and rescale O and l)
+    after many tiles have already been accumulated."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    for frac in where:
+        j = int(frac * N)
+        k[:, :, j:j + 3] *= factor
+    return tuple(wl.round_to_storage(x, dtype) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("d,dtype", [(64, wl.FP16), (128, wl.BF16), (256, wl.FP16)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_late_score_jumps_rebase(gpu_device, d, dtype, causal):
+    """Score jumps of several hundred (base-2 units) half-way through and near
+    the end of the keys; every row with a jump visible must be rescaled."""
+    B, H, N = 1, 2, 1500
+    q, k, v = _spiky_inputs(B, H, N, d, dtype, seed=31, factor=12.0, where=(0.5, 0.83))
+    scale = 1 / math.sqrt(d)
+    o, lse = run_gpu(q, k, v, dtype, scale, causal, gpu_device)
+    o_ref, lse_ref = attention_ref(*(wl.to_float64(x, dtype) for x in (q, k, v)), scale, causal)
+    assert_close(o, lse, o_ref, lse_ref, dtype, f"late jumps d{d} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_steadily_growing_scores(gpu_device, causal):
+    """Keys scaled up along the sequence: the row max keeps growing, so the
+    exponent base moves many times."""
+    B, H, N, d = 1, 2, 2048, 64
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d)) * np.linspace(0.5, 8.0, N)[None, None, :, None]
+    v = rng.standard_normal((B, H, N, d))
+    q, k, v = (wl.round_to_storage(x, wl.FP16) for x in (q, k, v))
+    o, lse = run_gpu(q, k, v, wl.FP16, 0.125, causal, gpu_device)
+    o_ref, lse_ref = attention_ref(*(wl.to_float64(x, wl.FP16) for x in (q, k, v)), 0.125, causal)
+    assert_close(o, lse, o_ref, lse_ref, wl.FP16, f"growing scores causal={causal}")
