@@ -123,33 +123,36 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 // Output MFMA of the pipelined schedule for head dims of 128 and more: the
 // O^T accumulators are kept in AGPRs (only MFMAs and the rare rescale touch
 // them), which leaves the arch VGPRs to the scores, probabilities and LDS
-// fragments.  Dependent MFMAs of one accumulator are always separated by other
-// MFMAs, and nothing else reads O until after an explicit wait (see pipe_sub).
+// fragments.  The compiler does not see inside inline asm, so each of these
+// MFMAs carries its own two wait states for operands that a VALU instruction
+// (an AGPR copy, the rescale) may have written just before; dependent MFMAs of
+// one accumulator are always separated by other MFMAs, and nothing else reads
+// O until after an explicit wait (see pipe_sub).
 // Score MFMAs of the same schedule: Q^T (only MFMAs read it) in AGPRs, the
 // scores in arch VGPRs for the softmax.
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32_qa0(const u32x4& a, const u32x4& q) {
   f32x16 d;
   if constexpr (BF16)
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(q));
+    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(q));
   else
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(q));
+    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(q));
   return d;
 }
 template <bool BF16>
 __device__ __forceinline__ void mfma32_qa(f32x16& c, const u32x4& a, const u32x4& q) {
   if constexpr (BF16)
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(q));
+    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(q));
   else
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(q));
+    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(q));
 }
 
 template <bool BF16>
 __device__ __forceinline__ void mfma32_acc_agpr(f32x16& c, const u32x4& a, const u32x4& b) {
   if constexpr (BF16)
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
   else
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -2,15 +2,18 @@
 workload, then one plain device-to-device copy of known size.
 
 The copy gives the factor that turns the FETCH_SIZE / WRITE_SIZE counters into
-bytes (it moves exactly ``copy_mb`` MiB each way).  Usage:
+bytes (it moves exactly ``copy_mb`` MiB each way).  Usage (from any directory):
 
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -- \
-      python -m exact_attention_21_amd.profile_run --workload NAME
+      python3 REPO/exact_attention_21_amd/profile_run.py --workload NAME
 """
 from __future__ import annotations
 
 import argparse
+import os
 import sys
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 
 
 def main() -> int:
@@ -22,8 +25,8 @@ def main() -> int:
 
     import torch
 
-    from . import forward, library
-    from . import workloads as wl
+    from exact_attention_21_amd import forward, library
+    from exact_attention_21_amd import workloads as wl
 
     library()
     w = {x.name: x for x in wl.WORKLOADS}[args.workload]
