@@ -123,11 +123,14 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 // Output MFMA of the pipelined schedule for head dims of 128 and more: the
 // O^T accumulators are kept in AGPRs (only MFMAs and the rare rescale touch
 // them), which leaves the arch VGPRs to the scores, probabilities and LDS
-// fragments.  The compiler does not see inside inline asm, so each of these
-// MFMAs carries its own two wait states for operands that a VALU instruction
-// (an AGPR copy, the rescale) may have written just before; dependent MFMAs of
-// one accumulator are always separated by other MFMAs, and nothing else reads
-// O until after an explicit wait (see pipe_sub).
+// fragments.  The compiler does not see inside inline asm: the operands of
+// this MFMA are never written by a VALU instruction shortly before it (P is
+// packed a whole sub-iteration earlier, O is only rescaled by the rebase path,
+// which is followed by softmax work before the next output MFMA), dependent
+// MFMAs of one accumulator are always separated by other MFMAs, and nothing
+// else reads O until after an explicit wait (see pipe_sub).  The score MFMAs
+// below read Q^T from AGPRs, which the compiler may refill with VALU copies
+// right before them, so they carry their own two wait states.
 // Score MFMAs of the same schedule: Q^T (only MFMAs read it) in AGPRs, the
 // scores in arch VGPRs for the softmax.
 template <bool BF16>
@@ -150,9 +153,9 @@ __device__ __forceinline__ void mfma32_qa(f32x16& c, const u32x4& a, const u32x4
 template <bool BF16>
 __device__ __forceinline__ void mfma32_acc_agpr(f32x16& c, const u32x4& a, const u32x4& b) {
   if constexpr (BF16)
-    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
   else
-    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -216,6 +219,10 @@ constexpr float kTileSumLimit = 32768.0f;
 template <int D, int BC, int NW, int QB, int SCHED, bool BF16, bool CAUSAL>
 struct Fa2Fwd {
   static constexpr int THREADS = NW * 64;
+  // Pipelined schedule: K and V tiles each in a ring of PIPE_RING LDS slots,
+  // one barrier per PIPE_RING / 2 sub-iterations.
+  static constexpr int PIPE_RING = 4;
+  static constexpr int PIPE_G = PIPE_RING / 2;
   static constexpr int QW = 32 * QB;             // query rows per wave
   // Waves that own distinct query rows (split-KV: the two groups share rows).
   // Two groups of NW/2 waves own the same query rows and split the key tiles
@@ -235,7 +242,7 @@ struct Fa2Fwd {
   static constexpr int CPT = BC * CPR / STAGERS; // chunks per thread per tile (each of K, V)
   // One K/V stream in LDS: two tiles each of K and V (the pipelined
   // schedule keeps a ring of four of each).
-  static constexpr int SLOTS = SCHED == kPipe ? 4 : 2;
+  static constexpr int SLOTS = SCHED == kPipe ? PIPE_RING : 2;
   static constexpr int STREAMB = 2 * SLOTS * TILEB;
   // Split-KV merge area: per group-1 lane, O^T (QB*DB*16 floats) then m, l.
   static constexpr int MERGE_FLOATS = QB * DB * 16 + 2 * QB;
@@ -705,6 +712,7 @@ struct Fa2Fwd {
   static constexpr int PIPE_LEAD = 2;  // positions of softmax work before the first MFMA
   static constexpr bool O_AGPR = D >= 128;  // output accumulators in AGPRs (see mfma32_acc_agpr)
 
+
   static __device__ __forceinline__ u32x4 kfrag(const lds_char* sk, const LdsOffsets& off, int kb, int ks) {
     return *(const __attribute__((address_space(3))) u32x4*)(sk + off.k[ks] + kb * 32 * ROWB);
   }
@@ -841,23 +849,27 @@ struct Fa2Fwd {
     }
   }
 
-  // The interleaved body of iteration j; S4 = (j - first) % 4 names the ring
-  // slots: K(j+1) in K slot (S4+1)%4, V(j-1) in V slot (S4+3)%4, and the
-  // score/probability register sets alternate with j.
+  // The interleaved body of iteration j; S4 = (j - first) % PIPE_RING names
+  // the ring slots: K(j+1) in K slot S4+1, V(j-1) in V slot S4-1 (mod the
+  // ring), and the score/probability register sets alternate with j.
   template <int S4>
   static __device__ __forceinline__ void pipe_body(const Ctx& cx, State& st, Scores (&sc)[2],
                                                    u32x4 (&pb)[2][QB][KB][2], f32x4 (&ct)[QB]) {
     constexpr int B = S4 % 2;
-    const lds_char* sk = cx.lds + ((S4 + 1) % 4) * TILEB;      // K(j+1)
-    const lds_char* sv = cx.lds + (4 + (S4 + 3) % 4) * TILEB;  // V(j-1)
+    const lds_char* sk = cx.lds + ((S4 + 1) % PIPE_RING) * TILEB;                          // K(j+1)
+    const lds_char* sv = cx.lds + (PIPE_RING + (S4 + PIPE_RING - 1) % PIPE_RING) * TILEB;  // V(j-1)
     constexpr int NMF = KB * DK * QB;               // MFMAs of each product (S and P V alike)
     constexpr int NSLOT = 2 * NMF;
     constexpr int NPAIR = QB * KB * 8;              // probability pairs of tile j
     constexpr int NKF = KB * DK, NVF = KB * 2 * DB;
+    // Positions that carry softmax work: at most one probability pair each, so
+    // with fewer pairs than MFMAs (d >= 128) the softmax and its row-sum MFMAs
+    // finish early in the body and the sums are ready for the check at its end.
+    constexpr int NVPOS = NPAIR < NSLOT ? NPAIR : NSLOT;
     static_assert(KB * 2 * DB * QB == NMF, "S and P V have equally many MFMAs");
     u32x4 kf[NKF], vf[NVF];
     // Position i issues MFMA i - PIPE_LEAD (S and P V alternating) and the
-    // softmax pairs of slot i; LDS fragments are read PIPE_PF positions before
+    // softmax pairs of position i; LDS fragments are read PIPE_PF positions before
     // their MFMA (all early ones at position 0), so the softmax work of the
     // first positions covers the LDS latency.
 #pragma unroll
@@ -895,9 +907,9 @@ struct Fa2Fwd {
             st.o[qb][db] = mfma32<BF16>(vf[g], pb[1 - B][qb][kb][u], st.o[qb][db]);
         }
       }
-      if (i < NSLOT) {
+      if (i < NVPOS) {
 #pragma unroll
-        for (int c = i * NPAIR / NSLOT; c < (i + 1) * NPAIR / NSLOT; ++c) {
+        for (int c = i * NPAIR / NVPOS; c < (i + 1) * NPAIR / NVPOS; ++c) {
           const int qb = c / (KB * 8), kb = (c / 8) % KB, r0 = 2 * (c % 8);
           float p0, p1;
           prob_pair<false>(sc[B], pb[B], st.m, cx.c2, qb, kb, r0, p0, p1);
@@ -912,7 +924,7 @@ struct Fa2Fwd {
     }
   }
 
-  // Sub-iteration j (S4 = (j - first) % 4): S(j+1), softmax(j), P(j-1)V(j-1).
+  // Sub-iteration j (S4 = (j - first) % PIPE_RING): S(j+1), softmax(j), P(j-1)V(j-1).
   template <int S4>
   static __device__ __forceinline__ void pipe_sub(const Ctx& cx, State& st, Scores (&sc)[2],
                                                   u32x4 (&pb)[2][QB][KB][2], int j) {
@@ -928,62 +940,81 @@ struct Fa2Fwd {
     pipe_accept(cx, sc[B], st, pb[B], ct);
   }
 
-  // Pair of sub-iterations j = first + r, first + r + 1 (P2 = (r / 2) % 2)
-  // and one barrier.  At its start the pair sends the tiles the next pair
-  // reads straight to LDS: K(r+3), K(r+4) into K slots (r+3)%4, r%4 and V(r+1),
-  // V(r+2) into V slots (r+1)%4, (r+2)%4 (r relative to first).  Those slots
-  // were last read in the previous pair, which ended with the barrier; the
-  // loads have landed once every wave has drained its vector-memory counter
-  // before this pair's barrier.
-  template <int P2>
-  static __device__ __forceinline__ void pipe_pair(const Ctx& cx, State& st, Scores (&sc)[2],
-                                                   u32x4 (&pb)[2][QB][KB][2], int first, int r) {
-    stage_dma_k<((2 * P2 + 3) % 4) * TILEB>(cx, first + r + 3);
-    stage_dma_k<((2 * P2) % 4) * TILEB>(cx, first + r + 4);
-    stage_dma_v<(4 + (2 * P2 + 1) % 4) * TILEB>(cx, first + r + 1);
-    stage_dma_v<(4 + (2 * P2 + 2) % 4) * TILEB>(cx, first + r + 2);
-    pipe_sub<2 * P2>(cx, st, sc, pb, first + r);
-    pipe_sub<2 * P2 + 1>(cx, st, sc, pb, first + r + 1);
+  // Group of G = PIPE_RING / 2 sub-iterations j = first + r .. first + r + G-1
+  // (r relative to first, H = (r / G) % 2) and one barrier.  The group reads
+  // K(r+1 .. r+G) and V(r-1 .. r+G-2); at its start it sends the tiles the next
+  // group reads straight to LDS: K(r+G+1 .. r+2G) and V(r+G-1 .. r+2G-2), into
+  // the slots of K(r-G+1 .. r) and V(r-G-1 .. r-2), which the previous group
+  // read before its barrier.  The loads have landed once every wave has drained
+  // its vector-memory counter before this group's barrier.
+  template <int H, int I>
+  static __device__ __forceinline__ void pipe_group_subs(const Ctx& cx, State& st, Scores (&sc)[2],
+                                                         u32x4 (&pb)[2][QB][KB][2], int first, int r) {
+    if constexpr (I < PIPE_G) {
+      pipe_sub<H * PIPE_G + I>(cx, st, sc, pb, first + r + I);
+      pipe_group_subs<H, I + 1>(cx, st, sc, pb, first, r);
+    }
+  }
+  template <int H, int I>
+  static __device__ __forceinline__ void pipe_group_loads(const Ctx& cx, int first, int r) {
+    if constexpr (I < PIPE_G) {
+      stage_dma_k<((H * PIPE_G + PIPE_G + 1 + I) % PIPE_RING) * TILEB>(cx, first + r + PIPE_G + 1 + I);
+      stage_dma_v<(PIPE_RING + (H * PIPE_G + PIPE_G - 1 + I) % PIPE_RING) * TILEB>(cx, first + r + PIPE_G - 1 + I);
+      pipe_group_loads<H, I + 1>(cx, first, r);
+    }
+  }
+  template <int H>
+  static __device__ __forceinline__ void pipe_group(const Ctx& cx, State& st, Scores (&sc)[2],
+                                                    u32x4 (&pb)[2][QB][KB][2], int first, int r) {
+    pipe_group_loads<H, 0>(cx, first, r);
+    pipe_group_subs<H, 0>(cx, st, sc, pb, first, r);
     dma_wait();
     __syncthreads();
   }
 
-  // Tiles first .. first+count-1 (count >= 1) through the pipeline, in pairs;
-  // with an odd count the last pair's second tile lies past the range and is
-  // fully masked (keys past N, or past the causal bound of every row).
+  // Prologue loads: K(0 .. G) and V(0 .. G-2) (relative to first).
+  template <int I>
+  static __device__ __forceinline__ void pipe_prologue_loads(const Ctx& cx, int first) {
+    if constexpr (I <= PIPE_G) {
+      stage_dma_k<I * TILEB>(cx, first + I);
+      if constexpr (I <= PIPE_G - 2) stage_dma_v<(PIPE_RING + I) * TILEB>(cx, first + I);
+      pipe_prologue_loads<I + 1>(cx, first);
+    }
+  }
+
+  // Tiles first .. first+count-1 (count >= 1) through the pipeline, in groups
+  // of PIPE_G; tiles of the last group past the range are fully masked (keys
+  // past N, or past the causal bound of every row).
   static __device__ __forceinline__ void run_pipe(const Ctx& cx, State& st, int first, int count) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) st.lc[qb][0] = st.lc[qb][1] = 0.f;
     Scores sc[2];
     u32x4 pb[2][QB][KB][2];
     u32x4 stg[CPT];
-    // P(first-1) = 0 against a zeroed V slot 3 (0 * garbage could be NaN).
+    // P(first-1) = 0 against a zeroed last V slot (0 * garbage could be NaN).
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) pb[1][qb][kb][0] = pb[1][qb][kb][1] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < CPT; ++i) stg[i] = u32x4{0u, 0u, 0u, 0u};
-    stage_store_v<7 * TILEB>(cx, stg);
-    // K(first..first+2) into K slots 0..2, V(first) into V slot 0.
-    stage_dma_k<0>(cx, first);
-    stage_dma_k<TILEB>(cx, first + 1);
-    stage_dma_k<2 * TILEB>(cx, first + 2);
-    stage_dma_v<4 * TILEB>(cx, first);
+    stage_store_v<(2 * PIPE_RING - 1) * TILEB>(cx, stg);
+    pipe_prologue_loads<0>(cx, first);
     dma_wait();
     __syncthreads();
     scores(cx.lds, cx.off, st.qf, sc[0]);  // S(first)
-    __syncthreads();  // K slot 0 is rewritten at the end of the first pair
-    const int count2 = (count + 1) & ~1;
-    for (int r = 0; r < count2; r += 4) {
-      pipe_pair<0>(cx, st, sc, pb, first, r);
-      if (r + 2 < count2) pipe_pair<1>(cx, st, sc, pb, first, r + 2);
+    __syncthreads();  // K slot 0 is rewritten by the first group's loads
+    const int count2 = (count + PIPE_G - 1) / PIPE_G * PIPE_G;
+    for (int r = 0; r < count2; r += 2 * PIPE_G) {
+      pipe_group<0>(cx, st, sc, pb, first, r);
+      if (r + PIPE_G < count2) pipe_group<1>(cx, st, sc, pb, first, r + PIPE_G);
     }
-    // P V of the last tile (relative index count2-1: odd, V slot (count2-1)%4).
-    if (count2 % 4 == 0)
-      pv(cx.lds + 7 * TILEB, cx.off, pb[1], st.o);
+    // P V of the last tile (relative index count2-1: odd, V slot (count2-1) % ring).
+    static_assert(PIPE_G % 2 == 0, "the last tile of a group has odd parity");
+    if (count2 % PIPE_RING == 0)
+      pv(cx.lds + (2 * PIPE_RING - 1) * TILEB, cx.off, pb[1], st.o);
     else
-      pv(cx.lds + 5 * TILEB, cx.off, pb[1], st.o);
+      pv(cx.lds + (PIPE_RING + PIPE_G - 1) * TILEB, cx.off, pb[1], st.o);
     // Each lane keeps the whole sum of its query (lane%32).
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) st.l[qb] = (cx.lane & 16) ? st.lc[qb][1] : st.lc[qb][0];
