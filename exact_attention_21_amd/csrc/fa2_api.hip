@@ -27,7 +27,7 @@ struct TileCfg {
 constexpr TileCfg cfg_for(int64_t d) {
   return d == 64    ? TileCfg{32, 8, 2, fa2::kPipe}
          : d == 128 ? TileCfg{32, 4, 2, fa2::kPipe}
-                    : TileCfg{32, 4, 1, fa2::kSimple};
+                    : TileCfg{32, 4, 1, fa2::kPipe};
 }
 
 template <int D>

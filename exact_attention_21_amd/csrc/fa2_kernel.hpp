@@ -245,7 +245,7 @@ struct Fa2Fwd {
   static constexpr int SLOTS = SCHED == kPipe ? PIPE_RING : 2;
   static constexpr int STREAMB = 2 * SLOTS * TILEB;
   // Split-KV merge area: per group-1 lane, O^T (QB*DB*16 floats) then m, l.
-  static constexpr int MERGE_FLOATS = QB * DB * 16 + 2 * QB;
+  static constexpr int MERGE_FLOATS = QB * DB * 16 + 3 * QB;
   static constexpr int MERGE_BYTES = SPLIT ? (NW / 2) * 64 * MERGE_FLOATS * 4 : 0;
   static constexpr int LDS_BYTES = STREAMS * STREAMB > MERGE_BYTES ? STREAMS * STREAMB : MERGE_BYTES;
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
@@ -254,7 +254,10 @@ struct Fa2Fwd {
   // Every LDS access in the tile loop is a lane base register plus a
   // compile-time offset; keeping the tile buffers under 64 KiB lets the
   // offsets ride in the instruction's 16-bit immediate.
-  static_assert(STREAMB <= 65536, "LDS image must fit the ds immediate offset");
+  // The pipelined schedule keeps the start of the V ring in the lanes' V
+  // offsets, so each ring (K, V) only needs its own 64 KiB of immediates.
+  static constexpr int VBASE = SCHED == kPipe ? SLOTS * TILEB : 0;
+  static_assert(STREAMB - VBASE <= 65536 && VBASE <= 65536, "LDS image must fit the ds immediate offset");
 
   typedef __attribute__((address_space(3))) char lds_char;
 
@@ -499,7 +502,7 @@ struct Fa2Fwd {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int dim = 32 * db + 16 * (g & 1) + 4 * (lane & 3);
-        off.v[db] = sbase + key * ROWB + (((dim >> 3) ^ swz_v(key)) << 4) + ((dim & 7) << 1);
+        off.v[db] = sbase + VBASE + key * ROWB + (((dim >> 3) ^ swz_v(key)) << 4) + ((dim & 7) << 1);
       }
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
@@ -558,7 +561,8 @@ struct Fa2Fwd {
         }
       }
       if (half == 0) {
-        const float lse = (l_tot > 0.f) ? (st.m[qb] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f
+        const float l_lse = (L_FULL && LSE_FP32) ? st.lf[qb] : l_tot;
+        const float lse = (l_lse > 0.f) ? (st.m[qb] + __builtin_amdgcn_logf(l_lse)) * 0.69314718055994531f
                                         : __builtin_inff();
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qrow * 4, 0, 0);
       }
@@ -572,7 +576,14 @@ struct Fa2Fwd {
     float m[QB];       // exponent base per row (base-2 domain)
     float l[QB];       // row sum: this lane's share (or all of it, L_FULL)
     float lc[QB][2];   // pipelined schedule: row sums of queries lane%16 and 16 + lane%16
+    float lf[QB];      // pipelined schedule, bf16: this lane's share of the unrounded row sum
   };
+  // bf16 rounds each probability by up to 2^-9: the output is normalised by
+  // the sum of the rounded values (those the output MFMA multiplies, so one
+  // dominant key gives its V row exactly), but the LSE takes the sum of the
+  // unrounded ones, which is the definition.  fp16's 2^-11 keeps the LSE of
+  // the rounded sum within 2^-11 (natural-log units) of it.
+  static constexpr bool LSE_FP32 = BF16;
   // The pipelined schedule ends with each lane holding its row's whole sum.
   static constexpr bool L_FULL = SCHED == kPipe;
 
@@ -758,17 +769,21 @@ struct Fa2Fwd {
   // Softmax of a whole tile against the current base (no interleaving).
   template <bool GUARD>
   static __device__ __forceinline__ void probs_tile(const Scores& sc, u32x4 (&pb)[QB][KB][2], const float (&m)[QB],
-                                                    float c2) {
+                                                    float c2, float (&lt)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      float la = 0.f, lb = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r0 = 0; r0 < 16; r0 += 2) {
           float p0, p1;
           prob_pair<GUARD>(sc, pb, m, c2, qb, kb, r0, p0, p1);
+          la += p0;
+          lb += p1;
         }
       }
+      lt[qb] = la + lb;
     }
   }
 
@@ -803,7 +818,7 @@ struct Fa2Fwd {
   // Rebase path: move each row's base to its running max, rescale O and the
   // row sums, and recompute the tile's probabilities and sums.
   static __device__ __forceinline__ void pipe_rebase(const Ctx& cx, const Scores& sc, State& st,
-                                                     u32x4 (&pb)[QB][KB][2], f32x4 (&ct)[QB]) {
+                                                     u32x4 (&pb)[QB][KB][2], f32x4 (&ct)[QB], float (&lt)[QB]) {
     const float ninf = -__builtin_inff();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -826,10 +841,11 @@ struct Fa2Fwd {
       // alpha of query q lives in lanes q and q+32.
       st.lc[qb][0] *= lane_value(alpha, cx.lane & 15);
       st.lc[qb][1] *= lane_value(alpha, 16 + (cx.lane & 15));
+      st.lf[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) st.o[qb][db] *= alpha;
     }
-    probs_tile<true>(sc, pb, st.m, cx.c2);
+    probs_tile<true>(sc, pb, st.m, cx.c2, lt);
     tile_sums(cx.ones, pb, ct);
   }
 
@@ -837,15 +853,16 @@ struct Fa2Fwd {
   // the limit (or not a number: an exponent base still at -inf) means some
   // probability may have overflowed.
   static __device__ __forceinline__ void pipe_accept(const Ctx& cx, const Scores& sc, State& st,
-                                                     u32x4 (&pb)[QB][KB][2], f32x4 (&ct)[QB]) {
+                                                     u32x4 (&pb)[QB][KB][2], f32x4 (&ct)[QB], float (&lt)[QB]) {
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) bad |= !(ct[qb][0] <= kTileSumLimit) || !(ct[qb][1] <= kTileSumLimit);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) pipe_rebase(cx, sc, st, pb, ct);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) pipe_rebase(cx, sc, st, pb, ct, lt);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       st.lc[qb][0] += ct[qb][0];
       st.lc[qb][1] += ct[qb][1];
+      if constexpr (LSE_FP32) st.lf[qb] += lt[qb];
     }
   }
 
@@ -854,10 +871,10 @@ struct Fa2Fwd {
   // ring), and the score/probability register sets alternate with j.
   template <int S4>
   static __device__ __forceinline__ void pipe_body(const Ctx& cx, State& st, Scores (&sc)[2],
-                                                   u32x4 (&pb)[2][QB][KB][2], f32x4 (&ct)[QB]) {
+                                                   u32x4 (&pb)[2][QB][KB][2], f32x4 (&ct)[QB], float (&lt)[QB]) {
     constexpr int B = S4 % 2;
     const lds_char* sk = cx.lds + ((S4 + 1) % PIPE_RING) * TILEB;                          // K(j+1)
-    const lds_char* sv = cx.lds + (PIPE_RING + (S4 + PIPE_RING - 1) % PIPE_RING) * TILEB;  // V(j-1)
+    const lds_char* sv = cx.lds + ((S4 + PIPE_RING - 1) % PIPE_RING) * TILEB;  // V(j-1) (V ring base in off.v)
     constexpr int NMF = KB * DK * QB;               // MFMAs of each product (S and P V alike)
     constexpr int NSLOT = 2 * NMF;
     constexpr int NPAIR = QB * KB * 8;              // probability pairs of tile j
@@ -868,6 +885,7 @@ struct Fa2Fwd {
     constexpr int NVPOS = NPAIR < NSLOT ? NPAIR : NSLOT;
     static_assert(KB * 2 * DB * QB == NMF, "S and P V have equally many MFMAs");
     u32x4 kf[NKF], vf[NVF];
+    float la[QB], lb[QB];
     // Position i issues MFMA i - PIPE_LEAD (S and P V alternating) and the
     // softmax pairs of position i; LDS fragments are read PIPE_PF positions before
     // their MFMA (all early ones at position 0), so the softmax work of the
@@ -913,6 +931,10 @@ struct Fa2Fwd {
           const int qb = c / (KB * 8), kb = (c / 8) % KB, r0 = 2 * (c % 8);
           float p0, p1;
           prob_pair<false>(sc[B], pb[B], st.m, cx.c2, qb, kb, r0, p0, p1);
+          if constexpr (LSE_FP32) {
+            la[qb] = (kb == 0 && r0 == 0) ? p0 : la[qb] + p0;
+            lb[qb] = (kb == 0 && r0 == 0) ? p1 : lb[qb] + p1;
+          }
           if (c % 4 == 3) {
             // Group (qb, kb, u) of four packed words is complete: its sums.
             const int g = (c / 4) % (KB * 2);
@@ -922,22 +944,29 @@ struct Fa2Fwd {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (LSE_FP32) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) lt[qb] = la[qb] + lb[qb];
+    }
   }
 
   // Sub-iteration j (S4 = (j - first) % PIPE_RING): S(j+1), softmax(j), P(j-1)V(j-1).
+  // Tiles past a wave's causal diagonal run as fully masked tiles (P = 0);
+  // skipping them with a branch measured no faster.
   template <int S4>
   static __device__ __forceinline__ void pipe_sub(const Ctx& cx, State& st, Scores (&sc)[2],
                                                   u32x4 (&pb)[2][QB][KB][2], int j) {
     constexpr int B = S4 % 2;
     if (!cx.active(j) || cx.masked(j)) mask_scores(sc[B], cx.lane, j * BC, cx.qw0, cx.n);
     f32x4 ct[QB];
-    pipe_body<S4>(cx, st, sc, pb, ct);
+    float lt[QB];
+    pipe_body<S4>(cx, st, sc, pb, ct, lt);
     // With O and Q^T in AGPRs the MFMAs above are inline asm the compiler does
     // not track: keep every other reader of their results (the softmax of the
     // next tile, the rebase path, the final output MFMA issued by the
     // compiler) more than an MFMA result latency away.
     if constexpr (O_AGPR) asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
-    pipe_accept(cx, sc[B], st, pb[B], ct);
+    pipe_accept(cx, sc[B], st, pb[B], ct, lt);
   }
 
   // Group of G = PIPE_RING / 2 sub-iterations j = first + r .. first + r + G-1
@@ -987,7 +1016,7 @@ struct Fa2Fwd {
   // past N, or past the causal bound of every row).
   static __device__ __forceinline__ void run_pipe(const Ctx& cx, State& st, int first, int count) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) st.lc[qb][0] = st.lc[qb][1] = 0.f;
+    for (int qb = 0; qb < QB; ++qb) st.lc[qb][0] = st.lc[qb][1] = st.lf[qb] = 0.f;
     Scores sc[2];
     u32x4 pb[2][QB][KB][2];
     u32x4 stg[CPT];
@@ -1012,12 +1041,20 @@ struct Fa2Fwd {
     // P V of the last tile (relative index count2-1: odd, V slot (count2-1) % ring).
     static_assert(PIPE_G % 2 == 0, "the last tile of a group has odd parity");
     if (count2 % PIPE_RING == 0)
-      pv(cx.lds + (2 * PIPE_RING - 1) * TILEB, cx.off, pb[1], st.o);
+      pv(cx.lds + (PIPE_RING - 1) * TILEB, cx.off, pb[1], st.o);
     else
-      pv(cx.lds + (PIPE_RING + PIPE_G - 1) * TILEB, cx.off, pb[1], st.o);
-    // Each lane keeps the whole sum of its query (lane%32).
+      pv(cx.lds + (PIPE_G - 1) * TILEB, cx.off, pb[1], st.o);
+    // Each lane keeps the whole sum of its query (lane%32); with LSE_FP32 the
+    // unrounded sum (the lane halves' shares added) goes to lf.
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) st.l[qb] = (cx.lane & 16) ? st.lc[qb][1] : st.lc[qb][0];
+    for (int qb = 0; qb < QB; ++qb) {
+      st.l[qb] = (cx.lane & 16) ? st.lc[qb][1] : st.lc[qb][0];
+      if constexpr (LSE_FP32) {
+        float lo, hi;
+        halves(st.lf[qb], lo, hi);
+        st.lf[qb] = lo + hi;
+      }
+    }
   }
 
   // Split-KV merge: group 1 leaves (O, m, l) in LDS and group 0 combines them
@@ -1038,6 +1075,7 @@ struct Fa2Fwd {
         }
         mb[QB * DB * 16 + 2 * qb] = st.m[qb];
         mb[QB * DB * 16 + 2 * qb + 1] = st.l[qb];
+        mb[QB * DB * 16 + 2 * QB + qb] = st.lf[qb];
       }
     }
     __syncthreads();
@@ -1053,6 +1091,7 @@ struct Fa2Fwd {
         const float a1 = (m1 == ninf) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
         st.m[qb] = mm;
         st.l[qb] = a0 * st.l[qb] + a1 * l1;
+        st.lf[qb] = a0 * st.lf[qb] + a1 * mb[QB * DB * 16 + 2 * QB + qb];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
 #pragma unroll
