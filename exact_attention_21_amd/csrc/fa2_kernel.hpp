@@ -720,7 +720,7 @@ struct Fa2Fwd {
   // barrier.
 
   static constexpr int PIPE_PF = 4;    // positions between an LDS fragment read and its first use
-  static constexpr int PIPE_LEAD = 2;  // positions of softmax work before the first MFMA
+  static constexpr int PIPE_LEAD = 0;  // positions of softmax work before the first MFMA
   static constexpr bool O_AGPR = D >= 128;  // output accumulators in AGPRs (see mfma32_acc_agpr)
 
 
