@@ -160,13 +160,22 @@ __device__ __forceinline__ void mfma32_acc_agpr(f32x16& c, const u32x4& a, const
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// 16x16x32 MFMA, used to sum probabilities on the matrix cores.
+typedef _Float16 f16x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+// Sparse 16x16x64 MFMA (A 4:2 structured: two nonzeros in every group of four
+// k, their positions given by the index word), used to sum probabilities on
+// the matrix cores: c + A B with B the 64 x 16 operand (b0, b1).
 template <bool BF16>
-__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+__device__ __forceinline__ f32x4 smfmac16(const u32x4& a, const u32x4& b0, const u32x4& b1, const f32x4& c, int idx) {
+  const u32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
   if constexpr (BF16) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x16, b), c,
+                                                     idx, 0, 0);
   } else {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x16, b), c,
+                                                    idx, 0, 0);
   }
 }
 
@@ -215,6 +224,10 @@ enum Sched : int {
 // rebase path: every probability of the tile is then below it, so it is finite
 // and exact to the usual relative rounding in fp16 as well as bf16.
 constexpr float kTileSumLimit = 32768.0f;
+// Exponent base of a row with no visible key in the first tile of an
+// unchecked run: finite (hidden keys still give exp2(-inf) = 0), and so far
+// below any score that a visible key overflows the row sum.
+constexpr float kUnseenBase = 1.0e30f;
 
 template <int D, int BC, int NW, int QB, int SCHED, bool BF16, bool CAUSAL>
 struct Fa2Fwd {
@@ -521,17 +534,26 @@ struct Fa2Fwd {
 
     const int kend = CAUSAL ? min(n, q0 + BR) : n;
     const int ntiles = (kend + BC - 1) / BC;
-    const Ctx cx{rk, rv, rsrc_words(p.k, slice * 2, slice_bytes), rsrc_words(p.v, slice * 2, slice_bytes), ones_operand(lane), lds, off, p.scale_log2, lane, tid, qw0, n, ntiles};
+    const Ctx cx{rk, rv, rsrc_words(p.k, slice * 2, slice_bytes), rsrc_words(p.v, slice * 2, slice_bytes), ones_operand(lane), ones_index(lane), lds, off, p.scale_log2, lane, tid, qw0, n, ntiles};
     if constexpr (SCHED == kPipe && SPLIT) {
       // Group 0 takes key tiles [0, T0) with T0 even, group 1 [T0, 2*T0);
       // tiles past the end are fully masked.  Both run T0 sub-iterations, so
       // their barriers pair.
       const int t0 = 2 * ((ntiles + 3) / 4);
-      run_pipe(cx, st, grp == 0 ? 0 : t0, t0);
+      const int first = grp == 0 ? 0 : t0;
+      // The LDS tiles are loaded by all waves together: a rerun is the whole
+      // workgroup's.
+      run_pipe<!OPTIMISTIC>(cx, st, first, t0);
+      if constexpr (OPTIMISTIC) {
+        if (__syncthreads_or(pipe_failed(st))) run_pipe<true>(cx, st, first, t0);
+      }
       merge_groups(cx, st, grp);
       if (grp != 0) return;  // group 1 handed its state to group 0
     } else if constexpr (SCHED == kPipe) {
-      run_pipe(cx, st, 0, ntiles);
+      run_pipe<!OPTIMISTIC>(cx, st, 0, ntiles);
+      if constexpr (OPTIMISTIC) {
+        if (__syncthreads_or(pipe_failed(st))) run_pipe<true>(cx, st, 0, ntiles);
+      }
     } else if constexpr (SCHED == kPingPong) {
       run_pingpong(cx, st);
     } else if constexpr (SCHED == kSplitKV) {
@@ -576,6 +598,7 @@ struct Fa2Fwd {
     float m[QB];       // exponent base per row (base-2 domain)
     float l[QB];       // row sum: this lane's share (or all of it, L_FULL)
     float lc[QB][2];   // pipelined schedule: row sums of queries lane%16 and 16 + lane%16
+    f32x4 ls[QB];      // unchecked pipeline: running row-sum MFMA results (see tile_sums)
     float lf[QB];      // pipelined schedule, bf16: this lane's share of the unrounded row sum
   };
   // bf16 rounds each probability by up to 2^-9: the output is normalised by
@@ -586,12 +609,18 @@ struct Fa2Fwd {
   static constexpr bool LSE_FP32 = BF16;
   // The pipelined schedule ends with each lane holding its row's whole sum.
   static constexpr bool L_FULL = SCHED == kPipe;
+  // Pipelined schedule: first an unchecked run, rerun checked only if some row
+  // overflowed (see run_pipe).  At d=64 the per-tile check is a noticeable
+  // part of a tile's work; with d >= 128 the second copy of the pipeline does
+  // not fit the registers beside the AGPR operands.
+  static constexpr bool OPTIMISTIC = D == 64;
 
   // Loop-invariant context.
   struct Ctx {
     __amdgpu_buffer_rsrc_t rk, rv;
     u32x4 wk, wv;  // the same K and V buffer descriptors as raw words (for inline asm)
     u32x4 ones;    // A operand of the row-sum MFMA (see ones_operand)
+    int ones_idx;  // its sparsity index (see ones_operand)
     lds_char* lds;
     LdsOffsets off;
     float c2;
@@ -721,6 +750,8 @@ struct Fa2Fwd {
 
   static constexpr int PIPE_PF = 4;    // positions between an LDS fragment read and its first use
   static constexpr int PIPE_LEAD = 0;  // positions of softmax work before the first MFMA
+  static constexpr int PIPE_TAIL = 0;  // MFMA positions after the last softmax pair
+  static constexpr int PIPE_SKEW = 1;  // positions between a pair's exponentials and its packing
   static constexpr bool O_AGPR = D >= 128;  // output accumulators in AGPRs (see mfma32_acc_agpr)
 
 
@@ -761,6 +792,16 @@ struct Fa2Fwd {
       p0 = s0 == ninf ? 0.f : p0;
       p1 = s1 == ninf ? 0.f : p1;
     }
+    pack_pair(pb, qb, kb, r0, p0, p1);
+  }
+  // Exponentials of score registers (r0, r0+1) of block (qb, kb) against the current base.
+  static __device__ __forceinline__ void exp_pair(const Scores& sc, const float (&m)[QB], float c2, int qb, int kb,
+                                                  int r0, float& p0, float& p1) {
+    p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc.s[qb][kb][r0], c2, -m[qb]));
+    p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc.s[qb][kb][r0 + 1], c2, -m[qb]));
+  }
+  // Round a pair of probabilities into its word of the P operand.
+  static __device__ __forceinline__ void pack_pair(u32x4 (&pb)[QB][KB][2], int qb, int kb, int r0, float p0, float p1) {
     uint32_t w = pack2<BF16>(p0, p1);
     pin(w);
     pb[qb][kb][r0 >> 3][(r0 & 7) >> 1] = w;
@@ -787,26 +828,41 @@ struct Fa2Fwd {
     }
   }
 
-  // Row sums on the matrix cores.  The packed probabilities of k-step u are
-  // the B operand of the output MFMA (lane L: query L%32, eight keys of the
-  // 16-key step).  Read as the B operand of a 16x16x32 MFMA, lane L's eight
-  // values sit in column L%16 and k-group L/16; with A[i][k] = 1 where
-  // (k/8)%2 == i%2 (else 0), row i of the result is the sum over the step's
-  // keys of query L%16 (i even) or 16 + L%16 (i odd).  In the 16x16 result
-  // lane L holds rows 4(L/16)+r, so register r = 0 is query L%16 and r = 1 is
-  // query 16 + L%16.  These are the sums of the rounded probabilities that the
-  // output MFMA consumes.
+  // Row sums on the matrix cores.  The packed probabilities of a 32-key tile
+  // are the B operands of the output MFMA: for k-step u, lane L holds eight
+  // keys of query L%32.  Both steps' words together are the 64 x 16 B operand
+  // of a sparse 16x16x64 MFMA, in which the 16 values of lane L sit in
+  // column L%16; lane groups 0 and 2 (L/16) hold query L%16, groups 1 and 3
+  // query 16 + L%16.  The compressed A operand of lane L is row L%16; its
+  // slots 0-3 meet the k of lane group 2(L/16 % 2) of B and slots 4-7 those of
+  // group 2(L/16 % 2) + 1, each slot pair at the positions that the index
+  // names in a group of four k.  So row i with ones in slots 0-3 (i even) or
+  // 4-7 (i odd) and index positions {0,1} (i%4 < 2) or {2,3} (i%4 >= 2) sums
+  // half of the values of query L%16 (i even) or 16 + L%16 (i odd), and in the
+  // 16x16 result, where lane L holds rows 4(L/16)+r, registers 0 + 2 are the
+  // sum of query L%16 and registers 1 + 3 that of query 16 + L%16.  These are
+  // the sums of the rounded probabilities that the output MFMA consumes.
   static __device__ __forceinline__ u32x4 ones_operand(int lane) {
     const uint32_t one = BF16 ? 0x3f803f80u : 0x3c003c00u;
-    const uint32_t w = (((lane >> 4) & 1) == (lane & 1)) ? one : 0u;
-    return u32x4{w, w, w, w};
+    return (lane & 1) ? u32x4{0u, 0u, one, one} : u32x4{one, one, 0u, 0u};
+  }
+  static __device__ __forceinline__ int ones_index(int lane) {
+    // Two 2-bit positions per group of four k (first in the low bits), the
+    // same in both 16-bit halves.
+    return (lane & 2) ? (int)0xEEEEEEEEu : 0x44444444;
+  }
+  // Sum MFMA of query block qb of a tile, accumulated over the tile's 32-key
+  // blocks (ACC: also over the tiles before it).
+  template <bool ACC = false>
+  static __device__ __forceinline__ void tile_sum_mfma(const Ctx& cx, const u32x4 (&pbq)[KB][2], int kb, f32x4& ct) {
+    ct = smfmac16<BF16>(cx.ones, pbq[kb][0], pbq[kb][1], (kb == 0 && !ACC) ? f32x4{} : ct, cx.ones_idx);
   }
   // Sums of one tile's probabilities for every query block.
-  static __device__ __forceinline__ void tile_sums(const u32x4& ones, const u32x4 (&pb)[QB][KB][2], f32x4 (&ct)[QB]) {
+  static __device__ __forceinline__ void tile_sums(const Ctx& cx, const u32x4 (&pb)[QB][KB][2], f32x4 (&ct)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-      for (int g = 0; g < KB * 2; ++g) ct[qb] = mfma16<BF16>(ones, pb[qb][g / 2][g % 2], g == 0 ? f32x4{} : ct[qb]);
+      for (int kb = 0; kb < KB; ++kb) tile_sum_mfma(cx, pb[qb], kb, ct[qb]);
     }
   }
 
@@ -846,7 +902,7 @@ struct Fa2Fwd {
       for (int db = 0; db < DB; ++db) st.o[qb][db] *= alpha;
     }
     probs_tile<true>(sc, pb, st.m, cx.c2, lt);
-    tile_sums(cx.ones, pb, ct);
+    tile_sums(cx, pb, ct);
   }
 
   // Accept the tile's sums, or send it through the rebase path.  A sum above
@@ -856,12 +912,13 @@ struct Fa2Fwd {
                                                      u32x4 (&pb)[QB][KB][2], f32x4 (&ct)[QB], float (&lt)[QB]) {
     bool bad = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) bad |= !(ct[qb][0] <= kTileSumLimit) || !(ct[qb][1] <= kTileSumLimit);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) pipe_rebase(cx, sc, st, pb, ct, lt);
+    for (int qb = 0; qb < QB; ++qb)
+      bad |= !(ct[qb][0] + ct[qb][2] <= kTileSumLimit) || !(ct[qb][1] + ct[qb][3] <= kTileSumLimit);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0)) pipe_rebase(cx, sc, st, pb, ct, lt);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      st.lc[qb][0] += ct[qb][0];
-      st.lc[qb][1] += ct[qb][1];
+      st.lc[qb][0] += ct[qb][0] + ct[qb][2];
+      st.lc[qb][1] += ct[qb][1] + ct[qb][3];
       if constexpr (LSE_FP32) st.lf[qb] += lt[qb];
     }
   }
@@ -869,7 +926,7 @@ struct Fa2Fwd {
   // The interleaved body of iteration j; S4 = (j - first) % PIPE_RING names
   // the ring slots: K(j+1) in K slot S4+1, V(j-1) in V slot S4-1 (mod the
   // ring), and the score/probability register sets alternate with j.
-  template <int S4>
+  template <int S4, bool CHECKED>
   static __device__ __forceinline__ void pipe_body(const Ctx& cx, State& st, Scores (&sc)[2],
                                                    u32x4 (&pb)[2][QB][KB][2], f32x4 (&ct)[QB], float (&lt)[QB]) {
     constexpr int B = S4 % 2;
@@ -882,14 +939,26 @@ struct Fa2Fwd {
     // Positions that carry softmax work: at most one probability pair each, so
     // with fewer pairs than MFMAs (d >= 128) the softmax and its row-sum MFMAs
     // finish early in the body and the sums are ready for the check at its end.
-    constexpr int NVPOS = NPAIR < NSLOT ? NPAIR : NSLOT;
+    constexpr int NVPOS = NPAIR < NSLOT - PIPE_TAIL ? NPAIR : NSLOT - PIPE_TAIL;
     static_assert(KB * 2 * DB * QB == NMF, "S and P V have equally many MFMAs");
     u32x4 kf[NKF], vf[NVF];
     float la[QB], lb[QB];
-    // Position i issues MFMA i - PIPE_LEAD (S and P V alternating) and the
-    // softmax pairs of position i; LDS fragments are read PIPE_PF positions before
-    // their MFMA (all early ones at position 0), so the softmax work of the
-    // first positions covers the LDS latency.
+    float pe[NPAIR][2];  // exponentials waiting to be packed
+    // Pairs of position ip: c in [ip * NPAIR / NVPOS, (ip + 1) * NPAIR / NVPOS).
+    // Packing them (and the row-sum MFMA of each completed block of eight words).
+    auto pack_position = [&](int ip) {
+#pragma unroll
+      for (int c = ip * NPAIR / NVPOS; c < (ip + 1) * NPAIR / NVPOS; ++c) {
+        const int qb = c / (KB * 8), kb = (c / 8) % KB, r0 = 2 * (c % 8);
+        pack_pair(pb[B], qb, kb, r0, pe[c][0], pe[c][1]);
+        if (c % 8 == 7) tile_sum_mfma<!CHECKED>(cx, pb[B][qb], kb, ct[qb]);
+      }
+    };
+    // Position i issues MFMA i - PIPE_LEAD (S and P V alternating), the
+    // exponentials of the softmax pairs of position i and the packing of those
+    // of position i - PIPE_SKEW, so that no packing waits on the latency of the
+    // exponentials just issued; LDS fragments are read PIPE_PF positions before
+    // their MFMA (all early ones at position 0).
 #pragma unroll
     for (int i = 0; i < NSLOT + PIPE_LEAD; ++i) {
 #pragma unroll
@@ -929,20 +998,20 @@ struct Fa2Fwd {
 #pragma unroll
         for (int c = i * NPAIR / NVPOS; c < (i + 1) * NPAIR / NVPOS; ++c) {
           const int qb = c / (KB * 8), kb = (c / 8) % KB, r0 = 2 * (c % 8);
-          float p0, p1;
-          prob_pair<false>(sc[B], pb[B], st.m, cx.c2, qb, kb, r0, p0, p1);
+          exp_pair(sc[B], st.m, cx.c2, qb, kb, r0, pe[c][0], pe[c][1]);
           if constexpr (LSE_FP32) {
-            la[qb] = (kb == 0 && r0 == 0) ? p0 : la[qb] + p0;
-            lb[qb] = (kb == 0 && r0 == 0) ? p1 : lb[qb] + p1;
-          }
-          if (c % 4 == 3) {
-            // Group (qb, kb, u) of four packed words is complete: its sums.
-            const int g = (c / 4) % (KB * 2);
-            ct[qb] = mfma16<BF16>(cx.ones, pb[B][qb][kb][(c % 8) / 4], g == 0 ? f32x4{} : ct[qb]);
+            la[qb] = (kb == 0 && r0 == 0) ? pe[c][0] : la[qb] + pe[c][0];
+            lb[qb] = (kb == 0 && r0 == 0) ? pe[c][1] : lb[qb] + pe[c][1];
           }
         }
       }
+      if (i >= PIPE_SKEW && i - PIPE_SKEW < NVPOS) pack_position(i - PIPE_SKEW);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    // Positions whose packing would fall past the last MFMA position.
+#pragma unroll
+    for (int ip = NSLOT + PIPE_LEAD - PIPE_SKEW; ip < NVPOS; ++ip) {
+      if (ip >= 0) pack_position(ip);
     }
     if constexpr (LSE_FP32) {
 #pragma unroll
@@ -952,21 +1021,28 @@ struct Fa2Fwd {
 
   // Sub-iteration j (S4 = (j - first) % PIPE_RING): S(j+1), softmax(j), P(j-1)V(j-1).
   // Tiles past a wave's causal diagonal run as fully masked tiles (P = 0);
-  // skipping them with a branch measured no faster.
-  template <int S4>
+  // skipping them with a branch measured no faster.  CHECKED: each tile's sums
+  // go through the overflow check (and the rebase path); otherwise they only
+  // accumulate, and an overflow shows in the final row sums.
+  template <int S4, bool CHECKED>
   static __device__ __forceinline__ void pipe_sub(const Ctx& cx, State& st, Scores (&sc)[2],
                                                   u32x4 (&pb)[2][QB][KB][2], int j) {
     constexpr int B = S4 % 2;
-    if (!cx.active(j) || cx.masked(j)) mask_scores(sc[B], cx.lane, j * BC, cx.qw0, cx.n);
+    if (__builtin_expect(!cx.active(j) || cx.masked(j), 0)) mask_scores(sc[B], cx.lane, j * BC, cx.qw0, cx.n);
     f32x4 ct[QB];
     float lt[QB];
-    pipe_body<S4>(cx, st, sc, pb, ct, lt);
+    pipe_body<S4, CHECKED>(cx, st, sc, pb, CHECKED ? ct : st.ls, lt);
     // With O and Q^T in AGPRs the MFMAs above are inline asm the compiler does
     // not track: keep every other reader of their results (the softmax of the
     // next tile, the rebase path, the final output MFMA issued by the
     // compiler) more than an MFMA result latency away.
     if constexpr (O_AGPR) asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
-    pipe_accept(cx, sc[B], st, pb[B], ct, lt);
+    if constexpr (CHECKED) {
+      pipe_accept(cx, sc[B], st, pb[B], ct, lt);
+    } else if constexpr (LSE_FP32) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) st.lf[qb] += lt[qb];
+    }
   }
 
   // Group of G = PIPE_RING / 2 sub-iterations j = first + r .. first + r + G-1
@@ -976,12 +1052,12 @@ struct Fa2Fwd {
   // the slots of K(r-G+1 .. r) and V(r-G-1 .. r-2), which the previous group
   // read before its barrier.  The loads have landed once every wave has drained
   // its vector-memory counter before this group's barrier.
-  template <int H, int I>
+  template <int H, int I, bool CHECKED>
   static __device__ __forceinline__ void pipe_group_subs(const Ctx& cx, State& st, Scores (&sc)[2],
                                                          u32x4 (&pb)[2][QB][KB][2], int first, int r) {
     if constexpr (I < PIPE_G) {
-      pipe_sub<H * PIPE_G + I>(cx, st, sc, pb, first + r + I);
-      pipe_group_subs<H, I + 1>(cx, st, sc, pb, first, r);
+      pipe_sub<H * PIPE_G + I, CHECKED>(cx, st, sc, pb, first + r + I);
+      pipe_group_subs<H, I + 1, CHECKED>(cx, st, sc, pb, first, r);
     }
   }
   template <int H, int I>
@@ -992,11 +1068,11 @@ struct Fa2Fwd {
       pipe_group_loads<H, I + 1>(cx, first, r);
     }
   }
-  template <int H>
+  template <int H, bool CHECKED>
   static __device__ __forceinline__ void pipe_group(const Ctx& cx, State& st, Scores (&sc)[2],
                                                     u32x4 (&pb)[2][QB][KB][2], int first, int r) {
     pipe_group_loads<H, 0>(cx, first, r);
-    pipe_group_subs<H, 0>(cx, st, sc, pb, first, r);
+    pipe_group_subs<H, 0, CHECKED>(cx, st, sc, pb, first, r);
     dma_wait();
     __syncthreads();
   }
@@ -1011,12 +1087,36 @@ struct Fa2Fwd {
     }
   }
 
+  // Whether an unchecked run left some row of this lane with a row sum that
+  // is not finite.
+  static __device__ __forceinline__ bool pipe_failed(const State& st) {
+    bool bad = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) bad |= !(st.l[qb] <= 3.0e38f);  // infinite or NaN
+    return bad;
+  }
   // Tiles first .. first+count-1 (count >= 1) through the pipeline, in groups
   // of PIPE_G; tiles of the last group past the range are fully masked (keys
-  // past N, or past the causal bound of every row).
+  // past N, or past the causal bound of every row).  Starts from O = 0 and
+  // the row state of no keys seen.
+  //
+  // CHECKED = false is the optimistic form: the exponent base is fixed at the
+  // row max of the first tile (a row with no visible key there gets a base so
+  // low that any later visible key overflows) and no tile is checked; a
+  // probability past the range of the 16-bit format makes the row sum
+  // infinite (a NaN input makes it NaN), which the caller detects at the end
+  // (pipe_failed) and answers by running the same tiles CHECKED, where every
+  // tile's sums are checked and the base moves as needed.
+  template <bool CHECKED>
   static __device__ __forceinline__ void run_pipe(const Ctx& cx, State& st, int first, int count) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) st.lc[qb][0] = st.lc[qb][1] = st.lf[qb] = 0.f;
+    for (int qb = 0; qb < QB; ++qb) {
+      st.m[qb] = -__builtin_inff();
+      st.lc[qb][0] = st.lc[qb][1] = st.lf[qb] = 0.f;
+      st.ls[qb] = f32x4{};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) st.o[qb][db] = f32x16{};
+    }
     Scores sc[2];
     u32x4 pb[2][QB][KB][2];
     u32x4 stg[CPT];
@@ -1033,10 +1133,26 @@ struct Fa2Fwd {
     __syncthreads();
     scores(cx.lds, cx.off, st.qf, sc[0]);  // S(first)
     __syncthreads();  // K slot 0 is rewritten by the first group's loads
+    if constexpr (!CHECKED) {
+      // Fixed base: the row max of the first tile (both lane halves), scaled.
+      if (!cx.active(first) || cx.masked(first)) mask_scores(sc[0], cx.lane, first * BC, cx.qw0, cx.n);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sc[0].s[qb][kb][r]);
+        float lo, hi;
+        halves(mx, lo, hi);
+        mx = __builtin_fmaxf(lo, hi);
+        st.m[qb] = mx == -__builtin_inff() ? -kUnseenBase : mx * cx.c2;
+      }
+    }
     const int count2 = (count + PIPE_G - 1) / PIPE_G * PIPE_G;
     for (int r = 0; r < count2; r += 2 * PIPE_G) {
-      pipe_group<0>(cx, st, sc, pb, first, r);
-      if (r + PIPE_G < count2) pipe_group<1>(cx, st, sc, pb, first, r + PIPE_G);
+      pipe_group<0, CHECKED>(cx, st, sc, pb, first, r);
+      if (r + PIPE_G < count2) pipe_group<1, CHECKED>(cx, st, sc, pb, first, r + PIPE_G);
     }
     // P V of the last tile (relative index count2-1: odd, V slot (count2-1) % ring).
     static_assert(PIPE_G % 2 == 0, "the last tile of a group has odd parity");
@@ -1048,7 +1164,10 @@ struct Fa2Fwd {
     // unrounded sum (the lane halves' shares added) goes to lf.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      st.l[qb] = (cx.lane & 16) ? st.lc[qb][1] : st.lc[qb][0];
+      if constexpr (CHECKED)
+        st.l[qb] = (cx.lane & 16) ? st.lc[qb][1] : st.lc[qb][0];
+      else
+        st.l[qb] = (cx.lane & 16) ? st.ls[qb][1] + st.ls[qb][3] : st.ls[qb][0] + st.ls[qb][2];
       if constexpr (LSE_FP32) {
         float lo, hi;
         halves(st.lf[qb], lo, hi);
