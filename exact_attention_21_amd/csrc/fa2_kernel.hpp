@@ -217,7 +217,7 @@ enum Sched : int {
   kSimple = 0,    // every wave owns QW rows of the query tile, all keys; one barrier per tile
   kPingPong = 1,  // as kSimple, two 4-wave groups half a tile apart (run_pingpong)
   kSplitKV = 2,   // two 4-wave groups own the same rows and split the keys (run_splitkv)
-  kPipe = 3,      // one wave per SIMD; S(j+1) and P(j-1)V(j-1) MFMAs interleaved with softmax(j) (run_pipe)
+  kPipe = 3,      // S(j+1) and P(j-1)V(j-1) MFMAs interleaved with softmax(j) inside each wave (run_pipe)
 };
 
 // Per-lane partial row sums of one tile above this value send the tile to the
