@@ -206,11 +206,22 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 //    With 128-byte rows (d = 64) two rows share a 256-byte line, so rows with
 //    equal parity need distinct positions: XOR with (r/2)%8.  With rows of 256
 //    bytes or more every row starts a line: XOR with r%16.
-//  * V rows are read by ds_read_b64_tr_b16, which measured no faster with any
-//    swizzle than without, so V is stored unswizzled.
+//  * V rows are read 8 bytes per lane by ds_read_b64_tr_b16: 32 lanes at a
+//    time read 4 consecutive rows 4h+e at 64 bytes (chunks 4b..4b+3) each.
+//    With rows of 256 bytes or more the 4 rows meet the same banks (4-way
+//    conflicts), with 128-byte rows rows e and e+2 do; XOR chunk bits 2-3 with
+//    e (bit 2 with e/2 at d = 64) so the 4 rows fill distinct bank groups.  The
+//    swizzle keeps row%4, which the row offsets added as immediates (multiples
+//    of 8 rows) preserve.  Measured: 3% faster at d = 256, no change at d = 64,
+//    and at d = 128 slower despite the conflicts it removes (the per-block V
+//    offsets it needs cost registers that d = 128 does not have), so d = 128
+//    keeps V unswizzled.
 template <int D>
 __device__ __forceinline__ int swz_k(int row) { return D == 64 ? ((row >> 1) & 7) : (row & 15); }
-__device__ __forceinline__ int swz_v(int) { return 0; }
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  return D == 64 ? (((row >> 1) & 1) << 2) : D == 128 ? 0 : ((row & 3) << 2);
+}
 
 // Work schedules inside a workgroup.
 enum Sched : int {
@@ -282,6 +293,7 @@ struct Fa2Fwd {
     int vst[CPT];  // staging store of chunk j, V layout
     int gld[CPT];  // global byte offset of chunk j inside a tile
     int gdk[CPT];  // global byte offset of the K chunk a direct-to-LDS load lands at linear slot j
+    int gdv[CPT];  // the same for the V layout
     int dma;       // this wave's first linear slot (bytes) of a direct-to-LDS tile load
   };
 
@@ -515,19 +527,20 @@ struct Fa2Fwd {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int dim = 32 * db + 16 * (g & 1) + 4 * (lane & 3);
-        off.v[db] = sbase + VBASE + key * ROWB + (((dim >> 3) ^ swz_v(key)) << 4) + ((dim & 7) << 1);
+        off.v[db] = sbase + VBASE + key * ROWB + (((dim >> 3) ^ swz_v<D>(key)) << 4) + ((dim & 7) << 1);
       }
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         const int c = stid + STAGERS * j;
         const int r = c / CPR, col = c % CPR;
         off.kst[j] = sbase + r * ROWB + ((col ^ swz_k<D>(r)) << 4);
-        off.vst[j] = sbase + r * ROWB + ((col ^ swz_v(r)) << 4);
+        off.vst[j] = sbase + r * ROWB + ((col ^ swz_v<D>(r)) << 4);
         off.gld[j] = (r * D + col * 8) * 2;
         // A direct-to-LDS load writes lane L's 16 bytes at the wave's base +
         // 16 L, i.e. linear slot c; that slot of the swizzled K layout holds
         // global chunk col ^ swz(r) (the swizzle is an involution).
         off.gdk[j] = (r * D + (col ^ swz_k<D>(r)) * 8) * 2;
+        off.gdv[j] = (r * D + (col ^ swz_v<D>(r)) * 8) * 2;
       }
       off.dma = __builtin_amdgcn_readfirstlane(sbase + (stid & ~63) * 16);
     }
@@ -672,7 +685,7 @@ struct Fa2Fwd {
   template <int BASE>
   static __device__ __forceinline__ void stage_dma_v(const Ctx& cx, int tile) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) dma16(cx.wv, cx.lds + BASE + cx.off.dma + STAGERS * 16 * i, cx.off.gld[i] + tile * TILEB);
+    for (int i = 0; i < CPT; ++i) dma16(cx.wv, cx.lds + BASE + cx.off.dma + STAGERS * 16 * i, cx.off.gdv[i] + tile * TILEB);
   }
   static __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -753,6 +766,10 @@ struct Fa2Fwd {
   static constexpr int PIPE_TAIL = 0;  // MFMA positions after the last softmax pair
   static constexpr int PIPE_SKEW = 1;  // positions between a pair's exponentials and its packing
   static constexpr bool O_AGPR = D >= 128;  // output accumulators in AGPRs (see mfma32_acc_agpr)
+  // Q^T operands in AGPRs too (see mfma32_qa).  Measured per head size: at
+  // d = 128 it frees the VGPRs the schedule needs, at d = 256 (one query
+  // block) the VGPR form is faster.
+  static constexpr bool Q_AGPR = D == 128;
 
 
   static __device__ __forceinline__ u32x4 kfrag(const lds_char* sk, const LdsOffsets& off, int kb, int ks) {
@@ -977,7 +994,7 @@ struct Fa2Fwd {
         if (s % 2 == 0) {
           // S MFMA t: K fragment (kb, ks), query block qb.
           const int qb = t % QB, f = t / QB, kb = f / DK, ks = f % DK;
-          if constexpr (O_AGPR) {
+          if constexpr (Q_AGPR) {
             if (ks == 0)
               sc[1 - B].s[qb][kb] = mfma32_qa0<BF16>(kf[f], st.qf[qb][ks]);
             else
