@@ -122,34 +122,13 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 
 // Output MFMA of the pipelined schedule for head dims of 128 and more: the
 // O^T accumulators are kept in AGPRs (only MFMAs and the rare rescale touch
-// them), which leaves the arch VGPRs to the scores, probabilities and LDS
-// fragments.  The compiler does not see inside inline asm: the operands of
+// them), which leaves the arch VGPRs to Q^T, the scores, probabilities and
+// LDS fragments.  The compiler does not see inside inline asm: the operands of
 // this MFMA are never written by a VALU instruction shortly before it (P is
 // packed a whole sub-iteration earlier, O is only rescaled by the rebase path,
 // which is followed by softmax work before the next output MFMA), dependent
 // MFMAs of one accumulator are always separated by other MFMAs, and nothing
-// else reads O until after an explicit wait (see pipe_sub).  The score MFMAs
-// below read Q^T from AGPRs, which the compiler may refill with VALU copies
-// right before them, so they carry their own two wait states.
-// Score MFMAs of the same schedule: Q^T (only MFMAs read it) in AGPRs, the
-// scores in arch VGPRs for the softmax.
-template <bool BF16>
-__device__ __forceinline__ f32x16 mfma32_qa0(const u32x4& a, const u32x4& q) {
-  f32x16 d;
-  if constexpr (BF16)
-    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(q));
-  else
-    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(q));
-  return d;
-}
-template <bool BF16>
-__device__ __forceinline__ void mfma32_qa(f32x16& c, const u32x4& a, const u32x4& q) {
-  if constexpr (BF16)
-    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(q));
-  else
-    asm volatile("s_nop 1\n v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(q));
-}
-
+// else reads O until after an explicit wait (see pipe_sub).
 template <bool BF16>
 __device__ __forceinline__ void mfma32_acc_agpr(f32x16& c, const u32x4& a, const u32x4& b) {
   if constexpr (BF16)
@@ -766,10 +745,6 @@ struct Fa2Fwd {
   static constexpr int PIPE_TAIL = 0;  // MFMA positions after the last softmax pair
   static constexpr int PIPE_SKEW = 1;  // positions between a pair's exponentials and its packing
   static constexpr bool O_AGPR = D >= 128;  // output accumulators in AGPRs (see mfma32_acc_agpr)
-  // Q^T operands in AGPRs too (see mfma32_qa).  Measured per head size: at
-  // d = 128 it frees the VGPRs the schedule needs, at d = 256 (one query
-  // block) the VGPR form is faster.
-  static constexpr bool Q_AGPR = D == 128;
 
 
   static __device__ __forceinline__ u32x4 kfrag(const lds_char* sk, const LdsOffsets& off, int kb, int ks) {
@@ -892,6 +867,9 @@ struct Fa2Fwd {
   // row sums, and recompute the tile's probabilities and sums.
   static __device__ __forceinline__ void pipe_rebase(const Ctx& cx, const Scores& sc, State& st,
                                                      u32x4 (&pb)[QB][KB][2], f32x4 (&ct)[QB], float (&lt)[QB]) {
+    // With O in AGPRs the output MFMAs are inline asm the compiler does not
+    // track: keep the reads of O below an MFMA result latency after them.
+    if constexpr (O_AGPR) asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
     const float ninf = -__builtin_inff();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -916,7 +894,19 @@ struct Fa2Fwd {
       st.lc[qb][1] *= lane_value(alpha, 16 + (cx.lane & 15));
       st.lf[qb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) st.o[qb][db] *= alpha;
+      for (int db = 0; db < DB; ++db) {
+        if constexpr (O_AGPR) {
+          // One 16-register block at a time through VGPRs: the empty asm
+          // statements pin the block to its AGPRs on both sides, so the
+          // compiler cannot read all of O into VGPRs at once (a peak that
+          // would push loop-invariant operands out to AGPRs for the whole loop).
+          asm volatile("" : "+a"(st.o[qb][db]));
+          st.o[qb][db] *= alpha;
+          asm volatile("" : "+a"(st.o[qb][db]));
+        } else {
+          st.o[qb][db] *= alpha;
+        }
+      }
     }
     probs_tile<true>(sc, pb, st.m, cx.c2, lt);
     tile_sums(cx, pb, ct);
@@ -994,14 +984,7 @@ struct Fa2Fwd {
         if (s % 2 == 0) {
           // S MFMA t: K fragment (kb, ks), query block qb.
           const int qb = t % QB, f = t / QB, kb = f / DK, ks = f % DK;
-          if constexpr (Q_AGPR) {
-            if (ks == 0)
-              sc[1 - B].s[qb][kb] = mfma32_qa0<BF16>(kf[f], st.qf[qb][ks]);
-            else
-              mfma32_qa<BF16>(sc[1 - B].s[qb][kb], kf[f], st.qf[qb][ks]);
-          } else {
-            sc[1 - B].s[qb][kb] = mfma32<BF16>(kf[f], st.qf[qb][ks], ks == 0 ? f32x16{} : sc[1 - B].s[qb][kb]);
-          }
+          sc[1 - B].s[qb][kb] = mfma32<BF16>(kf[f], st.qf[qb][ks], ks == 0 ? f32x16{} : sc[1 - B].s[qb][kb]);
         } else {
           // P V MFMA t: V fragment (kb, u, db), query block qb.
           const int qb = t % QB, g = t / QB, kb = g / (2 * DB), u = (g / DB) % 2, db = g % DB;
@@ -1049,11 +1032,6 @@ struct Fa2Fwd {
     f32x4 ct[QB];
     float lt[QB];
     pipe_body<S4, CHECKED>(cx, st, sc, pb, CHECKED ? ct : st.ls, lt);
-    // With O and Q^T in AGPRs the MFMAs above are inline asm the compiler does
-    // not track: keep every other reader of their results (the softmax of the
-    // next tile, the rebase path, the final output MFMA issued by the
-    // compiler) more than an MFMA result latency away.
-    if constexpr (O_AGPR) asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
     if constexpr (CHECKED) {
       pipe_accept(cx, sc[B], st, pb[B], ct, lt);
     } else if constexpr (LSE_FP32) {
@@ -1171,8 +1149,11 @@ struct Fa2Fwd {
       pipe_group<0, CHECKED>(cx, st, sc, pb, first, r);
       if (r + PIPE_G < count2) pipe_group<1, CHECKED>(cx, st, sc, pb, first, r + PIPE_G);
     }
-    // P V of the last tile (relative index count2-1: odd, V slot (count2-1) % ring).
+    // P V of the last tile (relative index count2-1: odd, V slot (count2-1) % ring),
+    // an MFMA the compiler issues: an MFMA result latency after the inline-asm
+    // output MFMAs it accumulates onto.
     static_assert(PIPE_G % 2 == 0, "the last tile of a group has odd parity");
+    if constexpr (O_AGPR) asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
     if (count2 % PIPE_RING == 0)
       pv(cx.lds + (PIPE_RING - 1) * TILEB, cx.off, pb[1], st.o);
     else
