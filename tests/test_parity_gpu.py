@@ -160,17 +160,19 @@ def test_late_score_jumps_rebase(gpu_device, d, dtype, causal):
     assert_close(o, lse, o_ref, lse_ref, dtype, f"late jumps d{d} {dtype} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 256])
 @pytest.mark.parametrize("dtype", [wl.FP16, wl.BF16])
 @pytest.mark.parametrize("causal", [False, True])
-def test_dominant_first_keys(gpu_device, dtype, causal):
+def test_dominant_first_keys(gpu_device, d, dtype, causal):
     """The first keys score far above the rest (an attention-sink pattern):
     an exponent base taken from the first tile stays the row max, and the
     later probabilities are tiny (fp16 subnormal) but still counted."""
-    B, H, N, d = 1, 2, 1800, 64
+    B, H, N = 1, 2, 1800
     q, k, v = _spiky_inputs(B, H, N, d, dtype, seed=53, factor=4.0, where=(0.0,))
-    o, lse = run_gpu(q, k, v, dtype, 0.125, causal, gpu_device)
-    o_ref, lse_ref = attention_ref(*(wl.to_float64(x, dtype) for x in (q, k, v)), 0.125, causal)
-    assert_close(o, lse, o_ref, lse_ref, dtype, f"dominant first keys {dtype} causal={causal}")
+    scale = 1 / math.sqrt(d)
+    o, lse = run_gpu(q, k, v, dtype, scale, causal, gpu_device)
+    o_ref, lse_ref = attention_ref(*(wl.to_float64(x, dtype) for x in (q, k, v)), scale, causal)
+    assert_close(o, lse, o_ref, lse_ref, dtype, f"dominant first keys d{d} {dtype} causal={causal}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
