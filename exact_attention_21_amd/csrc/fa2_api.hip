@@ -16,22 +16,21 @@
 namespace {
 
 // Tile configuration per head dimension: keys per K/V tile, waves per
-// workgroup, 32-row query blocks per wave, and the in-workgroup schedule.
+// workgroup (8: two split-KV groups of 4), 32-row query blocks per wave.
 struct TileCfg {
   int bc;
   int nw;
   int qb;
-  int sched;
 };
 
 constexpr TileCfg cfg_for(int64_t d) {
-  return d == 64    ? TileCfg{32, 8, 2, fa2::kPipe}
-         : d == 128 ? TileCfg{32, 4, 2, fa2::kPipe}
-                    : TileCfg{32, 4, 1, fa2::kPipe};
+  return d == 64    ? TileCfg{32, 8, 2}
+         : d == 128 ? TileCfg{32, 4, 2}
+                    : TileCfg{32, 4, 1};
 }
 
 template <int D>
-using KernelFor = fa2::Fa2Fwd<D, cfg_for(D).bc, cfg_for(D).nw, cfg_for(D).qb, cfg_for(D).sched, false, false>;
+using KernelFor = fa2::Fa2Fwd<D, cfg_for(D).bc, cfg_for(D).nw, cfg_for(D).qb, false, false>;
 
 constexpr int rows_per_wg(int64_t d) {
   return d == 64 ? KernelFor<64>::BR : d == 128 ? KernelFor<128>::BR : KernelFor<256>::BR;
@@ -62,11 +61,11 @@ fa2_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, 
   return FA2_OK;
 }
 
-template <int D, int BC, int NW, int QB, int SCHED, bool BF16, bool CAUSAL>
+template <int D, int BC, int NW, int QB, bool BF16, bool CAUSAL>
 hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
-  constexpr int lds = fa2::Fa2Fwd<D, BC, NW, QB, SCHED, BF16, CAUSAL>::LDS_BYTES;
+  constexpr int lds = fa2::Fa2Fwd<D, BC, NW, QB, BF16, CAUSAL>::LDS_BYTES;
   static_assert(lds == lds_bytes_for(D), "LDS size");
-  auto kern = fa2::fa2_fwd_kernel<D, BC, NW, QB, SCHED, BF16, CAUSAL>;
+  auto kern = fa2::fa2_fwd_kernel<D, BC, NW, QB, BF16, CAUSAL>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
@@ -80,7 +79,7 @@ hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream) {
   constexpr TileCfg c = cfg_for(D);
-  return launch<D, c.bc, c.nw, c.qb, c.sched, BF16, CAUSAL>(p, grid, stream);
+  return launch<D, c.bc, c.nw, c.qb, BF16, CAUSAL>(p, grid, stream);
 }
 
 template <bool BF16, bool CAUSAL>

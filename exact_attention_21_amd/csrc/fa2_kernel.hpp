@@ -81,10 +81,6 @@ struct Params {
 // no swizzle, offsets range-checked against num_records).
 constexpr int kRsrcWord3 = 0x00020000;
 
-// The exponent base moves only when a row's tile max exceeds it by more than
-// this (base-2 units), so probabilities stay below 2^kRebase.
-constexpr float kRebase = 8.0f;
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
@@ -159,8 +155,6 @@ __device__ __forceinline__ f32x4 smfmac16(const u32x4& a, const u32x4& b0, const
 }
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ f16x2 as_f16x2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
-__device__ __forceinline__ f16x2 ones_f16x2() { return f16x2{(_Float16)1.0f, (_Float16)1.0f}; }
 
 // Two fp32 values -> one dword of two 16-bit values, round to nearest even.
 template <bool BF16>
@@ -198,14 +192,6 @@ __device__ __forceinline__ int swz_k(int row) { return D == 64 ? ((row >> 1) & 7
 template <int D>
 __device__ __forceinline__ int swz_v(int row) { return D == 64 ? (((row >> 1) & 1) << 2) : ((row & 3) << 2); }
 
-// Work schedules inside a workgroup.
-enum Sched : int {
-  kSimple = 0,    // every wave owns QW rows of the query tile, all keys; one barrier per tile
-  kPingPong = 1,  // as kSimple, two 4-wave groups half a tile apart (run_pingpong)
-  kSplitKV = 2,   // two 4-wave groups own the same rows and split the keys (run_splitkv)
-  kPipe = 3,      // S(j+1) and P(j-1)V(j-1) MFMAs interleaved with softmax(j) inside each wave (run_pipe)
-};
-
 // Per-lane partial row sums of one tile above this value send the tile to the
 // rebase path: every probability of the tile is then below it, so it is finite
 // and exact to the usual relative rounding in fp16 as well as bf16.
@@ -215,7 +201,7 @@ constexpr float kTileSumLimit = 32768.0f;
 // below any score that a visible key overflows the row sum.
 constexpr float kUnseenBase = 1.0e30f;
 
-template <int D, int BC, int NW, int QB, int SCHED, bool BF16, bool CAUSAL>
+template <int D, int BC, int NW, int QB, bool BF16, bool CAUSAL>
 struct Fa2Fwd {
   static constexpr int THREADS = NW * 64;
   // Pipelined schedule: K and V tiles each in a ring of PIPE_RING LDS slots,
@@ -223,10 +209,9 @@ struct Fa2Fwd {
   static constexpr int PIPE_RING = 4;
   static constexpr int PIPE_G = PIPE_RING / 2;
   static constexpr int QW = 32 * QB;             // query rows per wave
-  // Waves that own distinct query rows (split-KV: the two groups share rows).
-  // Two groups of NW/2 waves own the same query rows and split the key tiles
-  // (split-KV; the pipelined schedule with 8 waves does the same).
-  static constexpr bool SPLIT = SCHED == kSplitKV || (SCHED == kPipe && NW == 8);
+  // With 8 waves, two groups of 4 own the same query rows and split the key
+  // tiles (split-KV), so every SIMD runs two waves.
+  static constexpr bool SPLIT = NW == 8;
   static constexpr int QWAVES = SPLIT ? NW / 2 : NW;
   static constexpr int BR = QWAVES * QW;         // query rows per workgroup
   // Threads that stage one K/V stream (split-KV: one stream per group).
@@ -239,9 +224,8 @@ struct Fa2Fwd {
   static constexpr int TILEB = BC * ROWB;        // bytes per K (or V) tile
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int CPT = BC * CPR / STAGERS; // chunks per thread per tile (each of K, V)
-  // One K/V stream in LDS: two tiles each of K and V (the pipelined
-  // schedule keeps a ring of four of each).
-  static constexpr int SLOTS = SCHED == kPipe ? PIPE_RING : 2;
+  // One K/V stream in LDS: a ring of PIPE_RING tiles each of K and V.
+  static constexpr int SLOTS = PIPE_RING;
   static constexpr int STREAMB = 2 * SLOTS * TILEB;
   // Split-KV merge area: per group-1 lane, O^T (QB*DB*16 floats) then m, l.
   static constexpr int MERGE_FLOATS = QB * DB * 16 + 3 * QB;
@@ -249,13 +233,11 @@ struct Fa2Fwd {
   static constexpr int LDS_BYTES = STREAMS * STREAMB > MERGE_BYTES ? STREAMS * STREAMB : MERGE_BYTES;
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert((BC * CPR) % STAGERS == 0 && CPT >= 1, "staging split");
-  static_assert(SCHED != kSplitKV || NW % 2 == 0, "split-KV needs two equal groups");
   // Every LDS access in the tile loop is a lane base register plus a
-  // compile-time offset; keeping the tile buffers under 64 KiB lets the
-  // offsets ride in the instruction's 16-bit immediate.
-  // The pipelined schedule keeps the start of the V ring in the lanes' V
-  // offsets, so each ring (K, V) only needs its own 64 KiB of immediates.
-  static constexpr int VBASE = SCHED == kPipe ? SLOTS * TILEB : 0;
+  // compile-time offset that must fit the instruction's 16-bit immediate; the
+  // start of the V ring is kept in the lanes' V offsets, so each ring (K, V)
+  // only needs its own 64 KiB of immediates.
+  static constexpr int VBASE = SLOTS * TILEB;
   static_assert(STREAMB - VBASE <= 65536 && VBASE <= 65536, "LDS image must fit the ds immediate offset");
 
   typedef __attribute__((address_space(3))) char lds_char;
@@ -264,9 +246,7 @@ struct Fa2Fwd {
   struct LdsOffsets {
     int k[DK];     // K^T operand of k-step ks for key block 0 (block kb adds kb*32 rows)
     int v[DB];     // V^T operand rows 32*db..: keys 4h+e of a 16-key group (+8 rows: second read)
-    int kst[CPT];  // staging store of chunk j, K layout
-    int vst[CPT];  // staging store of chunk j, V layout
-    int gld[CPT];  // global byte offset of chunk j inside a tile
+    int vst[CPT];  // store of chunk j through VGPRs, V layout (zeroing a V slot)
     int gdk[CPT];  // global byte offset of the K chunk a direct-to-LDS load lands at linear slot j
     int gdv[CPT];  // the same for the V layout
     int dma;       // this wave's first linear slot (bytes) of a direct-to-LDS tile load
@@ -314,96 +294,6 @@ struct Fa2Fwd {
           sc.s[qb][kb][r] = hide ? ninf : sc.s[qb][kb][r];
         }
       }
-    }
-  }
-
-  // Row max of the tile and the online update of the exponent base m: the
-  // base moves (and O and l are rescaled) only when some row's tile max
-  // exceeds it by more than kRebase.
-  static __device__ __forceinline__ void update_base(const Scores& sc, float (&m)[QB], float (&l)[QB],
-                                                     f32x16 (&o)[QB][DB], float c2) {
-    const float ninf = -__builtin_inff();
-    bool rebase = false;
-    float mt[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // Two independent max chains, merged at the end.
-      float ma = ninf, mb = ninf;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          ma = __builtin_fmaxf(__builtin_fmaxf(ma, sc.s[qb][kb][r]), sc.s[qb][kb][r + 1]);
-          mb = __builtin_fmaxf(__builtin_fmaxf(mb, sc.s[qb][kb][r + 2]), sc.s[qb][kb][r + 3]);
-        }
-      }
-      float mx = __builtin_fmaxf(ma, mb);
-      float lo, hi;
-      halves(mx, lo, hi);
-      mx = __builtin_fmaxf(lo, hi);
-      mt[qb] = (mx == ninf) ? ninf : mx * c2;
-      rebase |= mt[qb] > m[qb] + kRebase;
-    }
-    // Wave-uniform decision: move the base of every row whose max grew.
-    if (__builtin_amdgcn_ballot_w64(rebase) != 0) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float m_new = __builtin_fmaxf(m[qb], mt[qb]);
-        // A row that has seen only masked keys keeps -inf (its sums are zero).
-        const float alpha = (m_new == ninf) ? 1.f : __builtin_amdgcn_exp2f(m[qb] - m_new);
-        m[qb] = m_new;
-        l[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
-      }
-    }
-  }
-
-  // Probabilities of one tile relative to the base m, packed as the B
-  // operands of O^T += V^T P^T, and the lane's share of their row sum.
-  template <bool MASK>
-  static __device__ __forceinline__ void exponentiate(Scores& sc, u32x4 (&pb)[QB][KB][2],
-                                                      const float (&m)[QB], float (&l)[QB], float c2) {
-    const float ninf = -__builtin_inff();
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mb = m[qb];
-      float sa = 0.f, sb = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc.s[qb][kb][r], c2, -mb));
-          // Hidden keys give exactly 0 (also when the scale is 0 or the row
-          // has seen only hidden keys, where the exponent would be NaN).
-          if constexpr (MASK) p = (sc.s[qb][kb][r] == ninf) ? 0.f : p;
-          sc.s[qb][kb][r] = p;
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = sc.s[qb][kb][8 * u + 2 * e], p1 = sc.s[qb][kb][8 * u + 2 * e + 1];
-            pb[qb][kb][u][e] = pack2<BF16>(p0, p1);
-            if constexpr (BF16) {
-              // fp32 sum of the unrounded probabilities.
-              sa += p0;
-              sb += p1;
-            } else {
-              // fp16: sum of the rounded probabilities with one dot product
-              // against (1, 1); P V uses the same rounded values.  The packed
-              // word goes through a scalar first: bit-casting a vector element
-              // in place miscompiles (always reads element 0) in this clang.
-              const uint32_t w = pb[qb][kb][u][e];
-              if (e & 1)
-                sb = __builtin_amdgcn_fdot2(as_f16x2(w), ones_f16x2(), sb, false);
-              else
-                sa = __builtin_amdgcn_fdot2(as_f16x2(w), ones_f16x2(), sa, false);
-            }
-          }
-        }
-      }
-      l[qb] += sa + sb;
     }
   }
 
@@ -508,9 +398,7 @@ struct Fa2Fwd {
       for (int j = 0; j < CPT; ++j) {
         const int c = stid + STAGERS * j;
         const int r = c / CPR, col = c % CPR;
-        off.kst[j] = sbase + r * ROWB + ((col ^ swz_k<D>(r)) << 4);
         off.vst[j] = sbase + r * ROWB + ((col ^ swz_v<D>(r)) << 4);
-        off.gld[j] = (r * D + col * 8) * 2;
         // A direct-to-LDS load writes lane L's 16 bytes at the wave's base +
         // 16 L, i.e. linear slot c; that slot of the swizzled K layout holds
         // global chunk col ^ swz(r) (the swizzle is an involution).
@@ -523,7 +411,7 @@ struct Fa2Fwd {
     const int kend = CAUSAL ? min(n, q0 + BR) : n;
     const int ntiles = (kend + BC - 1) / BC;
     const Ctx cx{rk, rv, rsrc_words(p.k, slice * 2, slice_bytes), rsrc_words(p.v, slice * 2, slice_bytes), ones_operand(lane), ones_index(lane), lds, off, p.scale_log2, lane, tid, qw0, n, ntiles};
-    if constexpr (SCHED == kPipe && SPLIT) {
+    if constexpr (SPLIT) {
       // Group 0 takes key tiles [0, T0) with T0 even, group 1 [T0, 2*T0);
       // tiles past the end are fully masked.  Both run T0 sub-iterations, so
       // their barriers pair.
@@ -537,27 +425,18 @@ struct Fa2Fwd {
       }
       merge_groups(cx, st, grp);
       if (grp != 0) return;  // group 1 handed its state to group 0
-    } else if constexpr (SCHED == kPipe) {
+    } else {
       run_pipe<!OPTIMISTIC>(cx, st, 0, ntiles);
       if constexpr (OPTIMISTIC) {
         if (__syncthreads_or(pipe_failed(st))) run_pipe<true>(cx, st, 0, ntiles);
       }
-    } else if constexpr (SCHED == kPingPong) {
-      run_pingpong(cx, st);
-    } else if constexpr (SCHED == kSplitKV) {
-      run_splitkv(cx, st, grp);
-      if (grp != 0) return;  // group 1 handed its state to group 0
-    } else {
-      run_simple(cx, st);
     }
 
-    // Epilogue: combine the two halves' partial sums, divide once, store.
+    // Epilogue: each lane holds its row's whole sum; divide once, store.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int qrow = qw0 + 32 * qb + (lane & 31);
-      float l_lo, l_hi;
-      halves(st.l[qb], l_lo, l_hi);
-      const float l_tot = L_FULL ? st.l[qb] : l_lo + l_hi;
+      const float l_tot = st.l[qb];
       const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -571,7 +450,7 @@ struct Fa2Fwd {
         }
       }
       if (half == 0) {
-        const float l_lse = (L_FULL && LSE_FP32) ? st.lf[qb] : l_tot;
+        const float l_lse = LSE_FP32 ? st.lf[qb] : l_tot;
         const float lse = (l_lse > 0.f) ? (st.m[qb] + __builtin_amdgcn_logf(l_lse)) * 0.69314718055994531f
                                         : __builtin_inff();
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qrow * 4, 0, 0);
@@ -584,10 +463,10 @@ struct Fa2Fwd {
     u32x4 qf[QB][DK];  // Q^T operands
     f32x16 o[QB][DB];  // O^T accumulators
     float m[QB];       // exponent base per row (base-2 domain)
-    float l[QB];       // row sum: this lane's share (or all of it, L_FULL)
-    float lc[QB][2];   // pipelined schedule: row sums of queries lane%16 and 16 + lane%16
-    f32x4 ls[QB];      // unchecked pipeline: running row-sum MFMA results (see tile_sums)
-    float lf[QB];      // pipelined schedule, bf16: this lane's share of the unrounded row sum
+    float l[QB];       // row sum (after the run: the whole sum, in every lane of the row)
+    float lc[QB][2];   // checked run: row sums of queries lane%16 and 16 + lane%16
+    f32x4 ls[QB];      // unchecked run: running row-sum MFMA results (see tile_sums)
+    float lf[QB];      // bf16: this lane's share of the unrounded row sum (the whole sum after the run)
   };
   // bf16 rounds each probability by up to 2^-9: the output is normalised by
   // the sum of the rounded values (those the output MFMA multiplies, so one
@@ -595,8 +474,6 @@ struct Fa2Fwd {
   // unrounded ones, which is the definition.  fp16's 2^-11 keeps the LSE of
   // the rounded sum within 2^-11 (natural-log units) of it.
   static constexpr bool LSE_FP32 = BF16;
-  // The pipelined schedule ends with each lane holding its row's whole sum.
-  static constexpr bool L_FULL = SCHED == kPipe;
   // Pipelined schedule: first an unchecked run, rerun checked only if some row
   // overflowed (see run_pipe).  Measured: 6% faster at d = 64, 12% at d = 256,
   // 5% slower at d = 128 (the second copy of the pipeline crowds its
@@ -621,20 +498,7 @@ struct Fa2Fwd {
     }
   };
 
-  // Global -> register staging of one K or V tile.  The tile offset is part of
-  // the VGPR offset, so the buffer range check covers it: rows past N (and
-  // whole tiles past the end) read as zeros.
-  static __device__ __forceinline__ void stage_load(const Ctx& cx, const __amdgpu_buffer_rsrc_t& r, int j,
-                                                    u32x4 (&reg)[CPT]) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) reg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, cx.off.gld[i] + j * TILEB, 0, 0);
-  }
-  // Register -> LDS store of one staged tile at a compile-time LDS offset.
-  template <int BASE>
-  static __device__ __forceinline__ void stage_store_k(const Ctx& cx, const u32x4 (&reg)[CPT]) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) *(__attribute__((address_space(3))) u32x4*)(cx.lds + BASE + cx.off.kst[i]) = reg[i];
-  }
+  // Register -> LDS store of V-layout chunks at a compile-time LDS offset.
   template <int BASE>
   static __device__ __forceinline__ void stage_store_v(const Ctx& cx, const u32x4 (&reg)[CPT]) {
 #pragma unroll
@@ -664,57 +528,7 @@ struct Fa2Fwd {
   }
   static __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-  // Softmax of tile j: scores -> probabilities (packed) and the online update.
-  static __device__ __forceinline__ void softmax_tile(const Ctx& cx, State& st, Scores& sc, int j,
-                                                      u32x4 (&pb)[QB][KB][2]) {
-    const bool msk = cx.masked(j);
-    if (msk) mask_scores(sc, cx.lane, j * BC, cx.qw0, cx.n);
-    update_base(sc, st.m, st.l, st.o, cx.c2);
-    if (msk)
-      exponentiate<true>(sc, pb, st.m, st.l, cx.c2);
-    else
-      exponentiate<false>(sc, pb, st.m, st.l, cx.c2);
-  }
-
-  // One barrier per tile; tile j lives in K/V buffer j%2.  Its successor is
-  // loaded from global memory at the top of iteration j and written to the
-  // other buffer at the bottom; that buffer was last read in iteration j-1,
-  // before the barrier that ended it.
-  static __device__ __forceinline__ void run_simple(const Ctx& cx, State& st) {
-    u32x4 stk[CPT], stv[CPT];
-    auto step = [&](int j, auto buf) {
-      constexpr int B = decltype(buf)::value;
-      const bool more = j + 1 < cx.ntiles;
-      if (more) {
-        stage_load(cx, cx.rk, j + 1, stk);
-        stage_load(cx, cx.rv, j + 1, stv);
-      }
-      if (cx.active(j)) {
-        Scores sc;
-        scores(cx.lds + B * TILEB, cx.off, st.qf, sc);
-        u32x4 pb[QB][KB][2];
-        softmax_tile(cx, st, sc, j, pb);
-        pv(cx.lds + (2 + B) * TILEB, cx.off, pb, st.o);
-      }
-      if (more) {
-        stage_store_k<(1 - B) * TILEB>(cx, stk);
-        stage_store_v<(3 - B) * TILEB>(cx, stv);
-      }
-      __syncthreads();
-    };
-    stage_load(cx, cx.rk, 0, stk);
-    stage_load(cx, cx.rv, 0, stv);
-    stage_store_k<0>(cx, stk);
-    stage_store_v<2 * TILEB>(cx, stv);
-    __syncthreads();
-    for (int j = 0; j < cx.ntiles; j += 2) {
-      step(j, std::integral_constant<int, 0>{});
-      if (j + 1 < cx.ntiles) step(j + 1, std::integral_constant<int, 1>{});
-    }
-  }
-
-
-  // ---- Pipelined schedule (kPipe) --------------------------------------
+  // ---- Pipelined schedule ------------------------------------------------
   // Iteration j issues the MFMAs of S(j+1) = K(j+1) Q^T and of
   // O^T += V(j-1)^T P(j-1)^T one at a time, each followed by its share of the
   // softmax of tile j on the VALU, so the matrix cores and the vector ALU of a
@@ -1214,120 +1028,12 @@ struct Fa2Fwd {
     }
   }
 
-  // Ping-pong schedule for 8 waves.  Waves 0-3 (group 0) and 4-7 (group 1)
-  // share the SIMDs pairwise and run half a tile apart, two barriers per tile:
-  //   phase 2i   : group 0 issues P V(i-1) and S^T(i) on the matrix cores,
-  //                group 1 runs the softmax of tile i-1 on the VALU;
-  //   phase 2i+1 : group 0 runs the softmax of tile i,
-  //                group 1 issues P V(i-1) and S^T(i).
-  // Tile i lives in K/V buffer i%2.  K(i) is read in phases 2i and 2i+1, V(i)
-  // in phases 2i+2 and 2i+3.  In phase 2i all waves write K(i+1) and V(i)
-  // (loaded from global memory during phase 2i-1) into the buffers that held
-  // K(i-1) and V(i-2), whose last reads were in phase 2i-1.
-  static __device__ __forceinline__ void run_pingpong(const Ctx& cx, State& st) {
-    static_assert(NW == 8, "ping-pong pairs two groups of four waves");
-    const bool g0 = (cx.tid >> 8) == 0;
-    const int T = cx.ntiles;
-    u32x4 stk[CPT], stv[CPT];
-    Scores sc;             // scores waiting for their softmax
-    u32x4 pb[QB][KB][2];   // probabilities waiting for P V
-
-    auto mfma_part = [&](int i, auto kbuf, auto vbuf) {
-      constexpr int KBUF = decltype(kbuf)::value, VBUF = decltype(vbuf)::value;
-      if (i >= 1 && cx.active(i - 1)) pv(cx.lds + (2 + VBUF) * TILEB, cx.off, pb, st.o);
-      if (i < T && cx.active(i)) scores(cx.lds + KBUF * TILEB, cx.off, st.qf, sc);
-    };
-    auto valu_part = [&](int j) {
-      if (j >= 0 && j < T && cx.active(j)) softmax_tile(cx, st, sc, j, pb);
-    };
-    // Iteration i: phases 2i and 2i+1.  PAR = i%2 selects the buffers:
-    // K(i) in K[PAR], V(i-1) in V[1-PAR]; this phase stores K(i+1) to
-    // K[1-PAR] and V(i) to V[PAR].
-    auto iteration = [&](int i, auto par) {
-      constexpr int PAR = decltype(par)::value;
-      if (i + 1 < T) stage_store_k<(1 - PAR) * TILEB>(cx, stk);
-      if (i < T) stage_store_v<(2 + PAR) * TILEB>(cx, stv);
-      if (g0)
-        mfma_part(i, std::integral_constant<int, PAR>{}, std::integral_constant<int, 1 - PAR>{});
-      else
-        valu_part(i - 1);
-      __syncthreads();
-      if (i + 2 < T) stage_load(cx, cx.rk, i + 2, stk);
-      if (i + 1 < T) stage_load(cx, cx.rv, i + 1, stv);
-      if (g0)
-        valu_part(i);
-      else
-        mfma_part(i, std::integral_constant<int, PAR>{}, std::integral_constant<int, 1 - PAR>{});
-      if (i < T) __syncthreads();
-    };
-
-    // Prologue: K(0) into K[0]; K(1) and V(0) staged for phase 0.
-    stage_load(cx, cx.rk, 0, stk);
-    stage_store_k<0>(cx, stk);
-    if (T > 1) stage_load(cx, cx.rk, 1, stk);
-    stage_load(cx, cx.rv, 0, stv);
-    __syncthreads();
-    for (int i = 0; i <= T; i += 2) {
-      iteration(i, std::integral_constant<int, 0>{});
-      if (i + 1 <= T) iteration(i + 1, std::integral_constant<int, 1>{});
-    }
-  }
-
-  // Split-KV: group 0 (waves 0..NW/2-1) takes key tiles [0, T0) and group 1
-  // the tiles [T0, T), T0 = ceil(T/2); waves w and w+NW/2 own the same query
-  // rows, so every SIMD runs one wave of each group and each K/V byte read
-  // from LDS feeds QB = 2 query blocks.  Each group has its own
-  // double-buffered K/V stream; both advance one tile per barrier.  At the
-  // end group 1 leaves (m, l, O) in LDS and group 0 merges them lane by lane
-  // with the same algebra as the online update.
-  static __device__ __forceinline__ void run_splitkv(const Ctx& cx, State& st, int grp) {
-    const int T = cx.ntiles;
-    const int T0 = (T + 1) / 2;
-    const int first = grp == 0 ? 0 : T0;           // first tile of this group
-    const int count = grp == 0 ? T0 : T - T0;      // tiles of this group (count <= T0)
-    u32x4 stk[CPT], stv[CPT];
-    auto step = [&](int s, auto buf) {
-      constexpr int B = decltype(buf)::value;
-      const int j = first + s;
-      const bool mine = s < count;
-      const bool more = s + 1 < count;
-      if (more) {
-        stage_load(cx, cx.rk, j + 1, stk);
-        stage_load(cx, cx.rv, j + 1, stv);
-      }
-      if (mine && cx.active(j)) {
-        Scores sc;
-        scores(cx.lds + B * TILEB, cx.off, st.qf, sc);
-        u32x4 pb[QB][KB][2];
-        softmax_tile(cx, st, sc, j, pb);
-        pv(cx.lds + (2 + B) * TILEB, cx.off, pb, st.o);
-      }
-      if (more) {
-        stage_store_k<(1 - B) * TILEB>(cx, stk);
-        stage_store_v<(3 - B) * TILEB>(cx, stv);
-      }
-      __syncthreads();
-    };
-    if (count > 0) {
-      stage_load(cx, cx.rk, first, stk);
-      stage_load(cx, cx.rv, first, stv);
-      stage_store_k<0>(cx, stk);
-      stage_store_v<2 * TILEB>(cx, stv);
-    }
-    __syncthreads();
-    for (int s = 0; s < T0; s += 2) {
-      step(s, std::integral_constant<int, 0>{});
-      if (s + 1 < T0) step(s + 1, std::integral_constant<int, 1>{});
-    }
-
-    merge_groups(cx, st, grp);
-  }
 };
 
-template <int D, int BC, int NW, int QB, int SCHED, bool BF16, bool CAUSAL>
+template <int D, int BC, int NW, int QB, bool BF16, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64, 1) fa2_fwd_kernel(const Params p) {
   extern __shared__ __attribute__((aligned(16))) char lds_generic[];
-  Fa2Fwd<D, BC, NW, QB, SCHED, BF16, CAUSAL>::run(
+  Fa2Fwd<D, BC, NW, QB, BF16, CAUSAL>::run(
       p, (__attribute__((address_space(3))) char*)(__attribute__((address_space(3))) void*)lds_generic);
 }
 
