@@ -11,7 +11,7 @@
 // over query tiles, grid over query tile x head x batch, deferred 1/l, LSE
 // statistic), §15.3 (skeleton: causal tile bound, ragged-N zero fill and
 // -inf column mask, -inf guards, out-of-range rows not stored), §15.5.1
-// (double-buffered K/V staging with one barrier per tile).
+// (K/V tiles staged through shared memory ahead of their use).
 //
 // gfx950 mapping (a re-design, not a translation of the pages' mma.sync code):
 //   * The score tile is computed transposed, S^T = K Q^T, with
@@ -19,26 +19,30 @@
 //     B = 16 dims x 32 queries (Q^T, resident in VGPRs for the whole kernel).
 //     In the 32x32 accumulator, lane L holds query column L%32 and the 16 keys
 //     8*(r/4) + 4*(L/32) + r%4 (r = accumulator register), so a query's row max
-//     and row sum are in-lane reductions plus one exchange between the two
-//     32-lane halves (v_permlane32_swap).
+//     is an in-lane reduction plus one exchange between the two 32-lane halves
+//     (v_permlane32_swap).
 //   * The probabilities never leave the lane: registers r = 8u..8u+7 of a
 //     32-key accumulator are exactly the B operand (16 keys x 32 queries) of
 //     O^T += V^T P^T for k-step u, with keys ordered {16u+4h+e, 16u+8+4h+e}.
+//     Their row sums come from a sparse MFMA over the same packed words
+//     (tile_sums), so l sums exactly the rounded values the output MFMA uses.
 //   * V^T operands come from LDS with ds_read_b64_tr_b16, which transposes a
 //     4-row x 16-column block of 16-bit values across 16 lanes; the rows each
 //     lane group reads are chosen to match that key order.
-//   * Software pipeline inside each wave: the MFMAs of S^T for tile j+1 are
-//     issued before the softmax of tile j, so the matrix cores run while the
-//     VALU computes exponentials; P V for tile j follows.
-//   * The exponent base m is the running max, but it is only moved (and O and
-//     l rescaled) when a tile's max exceeds it by more than 2^8 in the base-2
-//     domain.  Any base gives the same softmax; this one keeps P <= 256 (exact
-//     in fp16/bf16 up to the usual relative rounding) and drops the rescale
-//     from almost every tile.  The pages rescale on every tile; the result is
-//     the same.
-//   * K and V tiles are staged global -> VGPR -> LDS, double-buffered, with
-//     16-byte-chunk XOR swizzles so the MFMA operand reads do not collide in
-//     LDS banks.  Out-of-range rows come back as zeros from buffer loads with a
+//   * Software pipeline inside each wave (run_pipe): sub-iteration j issues the
+//     MFMAs of S(j+1) and of P(j-1) V(j-1) one at a time, each followed by a
+//     share of the softmax of tile j, so matrix cores and VALU work side by side.
+//   * Lazily moved exponent base: the softmax of a tile uses the current base
+//     without first taking the tile's max.  Checked form: a tile whose row sums
+//     exceed 2^15 (so some probability might overflow 16 bits) goes through
+//     the rebase path (row max, rescale O and l, recompute).  Unchecked form
+//     (d = 64, 256): the base stays at the first tile's row max, and a row sum
+//     that overflowed sends the whole workgroup through the checked form.  Any
+//     base gives the same softmax; the pages move it on every tile.
+//   * K and V tiles go from global memory straight into a 4-slot LDS ring
+//     (buffer_load ... lds), one barrier per two tiles, with 16-byte-chunk XOR
+//     swizzles so the MFMA operand reads do not collide in LDS banks.
+//     Out-of-range rows come back as zeros from buffer loads with a
 //     range-checked resource (the pages' zero fill), and out-of-range stores
 //     are dropped by the same check.
 //   * The grid is one workgroup per (query tile, batch*head); consecutive
@@ -123,8 +127,9 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 // this MFMA are never written by a VALU instruction shortly before it (P is
 // packed a whole sub-iteration earlier, O is only rescaled by the rebase path,
 // which is followed by softmax work before the next output MFMA), dependent
-// MFMAs of one accumulator are always separated by other MFMAs, and nothing
-// else reads O until after an explicit wait (see pipe_sub).
+// MFMAs of one accumulator are always separated by other MFMAs, and the other
+// readers of O (the rebase path, the compiler-issued output MFMA of the last
+// tile) come after an explicit wait (see pipe_rebase, run_pipe).
 template <bool BF16>
 __device__ __forceinline__ void mfma32_acc_agpr(f32x16& c, const u32x4& a, const u32x4& b) {
   if constexpr (BF16)
@@ -227,7 +232,8 @@ struct Fa2Fwd {
   // One K/V stream in LDS: a ring of PIPE_RING tiles each of K and V.
   static constexpr int SLOTS = PIPE_RING;
   static constexpr int STREAMB = 2 * SLOTS * TILEB;
-  // Split-KV merge area: per group-1 lane, O^T (QB*DB*16 floats) then m, l.
+  // Split-KV merge area: per group-1 lane, O^T (QB*DB*16 floats) then m, l
+  // and the unrounded bf16 row sums.
   static constexpr int MERGE_FLOATS = QB * DB * 16 + 3 * QB;
   static constexpr int MERGE_BYTES = SPLIT ? (NW / 2) * 64 * MERGE_FLOATS * 4 : 0;
   static constexpr int LDS_BYTES = STREAMS * STREAMB > MERGE_BYTES ? STREAMS * STREAMB : MERGE_BYTES;
@@ -355,12 +361,11 @@ struct Fa2Fwd {
     const size_t slice = (size_t)bh * (size_t)n * D;  // elements before this head
     const uint32_t slice_bytes = (uint32_t)n * D * 2;
     const auto rq = make_rsrc((const char*)p.q + slice * 2, slice_bytes);
-    const auto rk = make_rsrc((const char*)p.k + slice * 2, slice_bytes);
-    const auto rv = make_rsrc((const char*)p.v + slice * 2, slice_bytes);
     const auto ro = make_rsrc((char*)p.o + slice * 2, slice_bytes);
     const auto rl = make_rsrc(p.lse + (size_t)bh * n, (uint32_t)n * 4);
 
     // Q^T operands: for k-step s, lane holds Q[row][16s + 8*half .. +7].
+    // (run_pipe starts the rest of the state from O = 0 and no keys seen.)
     State st;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -370,10 +375,6 @@ struct Fa2Fwd {
         st.qf[qb][s] = __builtin_amdgcn_raw_buffer_load_b128(rq, (qrow * D + 16 * s + 8 * half) * 2, 0, 0);
         st.qf[qb][s] ^= p.q_sign;
       }
-      st.m[qb] = -__builtin_inff();  // exponent base (base-2 domain)
-      st.l[qb] = 0.f;                // this lane's share of the row sum
-#pragma unroll
-      for (int db = 0; db < DB; ++db) st.o[qb][db] = f32x16{};
     }
 
     // Lane-constant LDS offsets.
@@ -410,7 +411,8 @@ struct Fa2Fwd {
 
     const int kend = CAUSAL ? min(n, q0 + BR) : n;
     const int ntiles = (kend + BC - 1) / BC;
-    const Ctx cx{rk, rv, rsrc_words(p.k, slice * 2, slice_bytes), rsrc_words(p.v, slice * 2, slice_bytes), ones_operand(lane), ones_index(lane), lds, off, p.scale_log2, lane, tid, qw0, n, ntiles};
+    const Ctx cx{rsrc_words(p.k, slice * 2, slice_bytes), rsrc_words(p.v, slice * 2, slice_bytes), ones_operand(lane),
+                 ones_index(lane), lds, off, p.scale_log2, lane, tid, qw0, n, ntiles};
     if constexpr (SPLIT) {
       // Group 0 takes key tiles [0, T0) with T0 even, group 1 [T0, 2*T0);
       // tiles past the end are fully masked.  Both run T0 sub-iterations, so
@@ -482,8 +484,7 @@ struct Fa2Fwd {
 
   // Loop-invariant context.
   struct Ctx {
-    __amdgpu_buffer_rsrc_t rk, rv;
-    u32x4 wk, wv;  // the same K and V buffer descriptors as raw words (for inline asm)
+    u32x4 wk, wv;  // K and V buffer descriptors as raw words (for the inline-asm loads)
     u32x4 ones;    // A operand of the row-sum MFMA (see ones_operand)
     int ones_idx;  // its sparsity index (see ones_operand)
     lds_char* lds;
@@ -537,7 +538,8 @@ struct Fa2Fwd {
   // probabilities could overflow (or whose base is still -inf) is caught by the
   // size of its row sums and redone through the rebase path, which takes the
   // row max, rescales O and l, and recomputes the probabilities.  The result is
-  // the online softmax of the pages with a lazily moved base.
+  // the online softmax of the pages with a lazily moved base.  (The unchecked
+  // form of run_pipe keeps the base fixed and checks once, at the end.)
   //
   // Every iteration runs the same instruction stream: a tile past the wave's
   // causal diagonal is processed as a fully masked tile (its probabilities are
@@ -545,10 +547,9 @@ struct Fa2Fwd {
   // P(-1) is 0 against a zeroed V buffer.  Only the masking of ragged and
   // diagonal tiles and the rare rebase branch off.
   //
-  // LDS: K(t) lives in K buffer t%2 and V(t) in V buffer t%2.  Iteration j
-  // reads K((j+1)%2) and V((j-1)%2), and writes K(j+2) into K(j%2) and V(j)
-  // into V(j%2); both were last read in iteration j-1, which ended with the
-  // barrier.
+  // LDS: K and V each have a ring of PIPE_RING tile slots; tile t (counted
+  // from the first tile of the run) lives in slot t % PIPE_RING.  The
+  // sub-iterations run in groups of PIPE_G with one barrier each (pipe_group).
 
   static constexpr int PIPE_PF = 4;    // positions between an LDS fragment read and its first use
   static constexpr int PIPE_LEAD = 0;  // positions of softmax work before the first MFMA
@@ -579,28 +580,26 @@ struct Fa2Fwd {
     asm volatile("" : "+v"(x));
   }
 
-  // Probabilities of score registers (r0, r0+1) of block (qb, kb) against the
-  // current base, packed into the P operand; returns them for the sums.
-  template <bool GUARD>
-  static __device__ __forceinline__ void prob_pair(const Scores& sc, u32x4 (&pb)[QB][KB][2], const float (&m)[QB],
-                                                   float c2, int qb, int kb, int r0, float& p0, float& p1) {
-    const float s0 = sc.s[qb][kb][r0], s1 = sc.s[qb][kb][r0 + 1];
-    p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c2, -m[qb]));
-    p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c2, -m[qb]));
-    if constexpr (GUARD) {
-      // Hidden keys give exactly 0 (also where the exponent would be NaN:
-      // scale 0, or a row that has seen only hidden keys).
-      const float ninf = -__builtin_inff();
-      p0 = s0 == ninf ? 0.f : p0;
-      p1 = s1 == ninf ? 0.f : p1;
-    }
-    pack_pair(pb, qb, kb, r0, p0, p1);
-  }
-  // Exponentials of score registers (r0, r0+1) of block (qb, kb) against the current base.
+  // Exponentials of score registers (r0, r0+1) of block (qb, kb) against the
+  // current base: exp2(c2 s - m), c2 = scale * log2(e).
   static __device__ __forceinline__ void exp_pair(const Scores& sc, const float (&m)[QB], float c2, int qb, int kb,
                                                   int r0, float& p0, float& p1) {
     p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc.s[qb][kb][r0], c2, -m[qb]));
     p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc.s[qb][kb][r0 + 1], c2, -m[qb]));
+  }
+  // The same pair, packed into the P operand; returns the probabilities.
+  // GUARD: hidden keys give exactly 0 (also where the exponent would be NaN:
+  // scale 0, or a base still at -inf).
+  template <bool GUARD>
+  static __device__ __forceinline__ void prob_pair(const Scores& sc, u32x4 (&pb)[QB][KB][2], const float (&m)[QB],
+                                                   float c2, int qb, int kb, int r0, float& p0, float& p1) {
+    exp_pair(sc, m, c2, qb, kb, r0, p0, p1);
+    if constexpr (GUARD) {
+      const float ninf = -__builtin_inff();
+      p0 = sc.s[qb][kb][r0] == ninf ? 0.f : p0;
+      p1 = sc.s[qb][kb][r0 + 1] == ninf ? 0.f : p1;
+    }
+    pack_pair(pb, qb, kb, r0, p0, p1);
   }
   // Round a pair of probabilities into its word of the P operand.
   static __device__ __forceinline__ void pack_pair(u32x4 (&pb)[QB][KB][2], int qb, int kb, int r0, float p0, float p1) {
