@@ -74,9 +74,12 @@ typedef enum {
  *   Q, K, V   device pointers to [B, H, N, d] `dtype` tensors (read only).
  *   O         device pointer to a [B, H, N, d] `dtype` tensor (written).
  *   LSE       device pointer to a [B, H, N] float32 tensor (written).
- *   B, H, N   batch, heads, sequence length; each >= 1.  Limits: N * d < 2^30
- *             (one head's slice is addressed with 32-bit byte offsets) and
- *             ceil(N / 256) * H * B < 2^31 (grid size).
+ *   B, H, N   batch, heads, sequence length; each >= 1.  Limits, with R the
+ *             query rows per workgroup (256 for d = 64 and 128, 128 for
+ *             d = 256; fa2_launch_info reports it): (N + R) * d * 2 < 2^31
+ *             (one head's slice, with the zero-filled rows of the last query
+ *             tile, is addressed with signed 32-bit byte offsets) and
+ *             ceil(N / R) * H * B < 2^31 (grid size).
  *   d         head dimension: 64, 128 or 256.
  *   scale     softmax scale applied to Q K^T before the row max; any finite value.
  *   is_causal 0: all keys visible; nonzero: key j visible to query i iff j <= i.
