@@ -23,8 +23,14 @@ struct TileCfg {
   int qb;
 };
 
+// d = 32 and 96 use 64-key tiles: with 32 keys their tiles have fewer
+// 16-byte chunks than the threads that load them (d = 32) or a fractional
+// number per thread (d = 96).  d = 96 runs without split-KV so that its ring
+// (96 KiB) fits the LDS.
 constexpr TileCfg cfg_for(int64_t d) {
-  return d == 64    ? TileCfg{32, 8, 2}
+  return d == 32    ? TileCfg{64, 8, 1}
+         : d == 64  ? TileCfg{32, 8, 2}
+         : d == 96  ? TileCfg{64, 4, 1}
          : d == 128 ? TileCfg{32, 4, 2}
                     : TileCfg{32, 4, 1};
 }
@@ -33,12 +39,23 @@ template <int D>
 using KernelFor = fa2::Fa2Fwd<D, cfg_for(D).bc, cfg_for(D).nw, cfg_for(D).qb, false, false>;
 
 constexpr int rows_per_wg(int64_t d) {
-  return d == 64 ? KernelFor<64>::BR : d == 128 ? KernelFor<128>::BR : KernelFor<256>::BR;
+  return d == 32 ? KernelFor<32>::BR : d == 64 ? KernelFor<64>::BR : d == 96 ? KernelFor<96>::BR
+         : d == 128 ? KernelFor<128>::BR : KernelFor<256>::BR;
 }
 
 constexpr int lds_bytes_for(int64_t d) {
-  return d == 64 ? KernelFor<64>::LDS_BYTES : d == 128 ? KernelFor<128>::LDS_BYTES : KernelFor<256>::LDS_BYTES;
+  return d == 32 ? KernelFor<32>::LDS_BYTES : d == 64 ? KernelFor<64>::LDS_BYTES
+         : d == 96 ? KernelFor<96>::LDS_BYTES : d == 128 ? KernelFor<128>::LDS_BYTES : KernelFor<256>::LDS_BYTES;
 }
+
+// Rows past N that a launch may address (see check_shape).
+constexpr int64_t kPadRows = 256;
+static_assert(KernelFor<32>::BR <= kPadRows && KernelFor<64>::BR <= kPadRows && KernelFor<96>::BR <= kPadRows &&
+                  KernelFor<128>::BR <= kPadRows && KernelFor<256>::BR <= kPadRows,
+              "query tile padding");
+static_assert(4 * cfg_for(32).bc <= kPadRows && 4 * cfg_for(64).bc <= kPadRows && 4 * cfg_for(96).bc <= kPadRows &&
+                  4 * cfg_for(128).bc <= kPadRows && 4 * cfg_for(256).bc <= kPadRows,
+              "key tile padding");
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -47,12 +64,14 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 fa2_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int64_t* grid) {
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_UNSUPPORTED_DTYPE;
-  if (d != 64 && d != 128 && d != 256) return FA2_ERR_UNSUPPORTED_HEAD_DIM;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA2_ERR_UNSUPPORTED_HEAD_DIM;
   if (B < 1 || H < 1 || N < 1) return FA2_ERR_BAD_SHAPE;
   const int64_t br = rows_per_wg(d);
   // One head's slice is addressed with signed 32-bit byte offsets, including
-  // the zero-filled rows past N in the last query tile.
-  if ((N + br) * d * 2 >= (int64_t(1) << 31)) return FA2_ERR_BAD_SHAPE;
+  // the rows past N that a workgroup touches: the rest of the last query tile
+  // (fewer than R <= 256 rows) and the fully masked key tiles that round a
+  // split-KV range up (fewer than 4 tiles of at most 64 keys).
+  if ((N + kPadRows) * d * 2 >= (int64_t(1) << 31)) return FA2_ERR_BAD_SHAPE;
   if (B > (int64_t(1) << 31) / H) return FA2_ERR_BAD_SHAPE;
   const int64_t bh = B * H;
   const int64_t tiles = (N + br - 1) / br;
@@ -85,7 +104,9 @@ hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream) {
 template <bool BF16, bool CAUSAL>
 hipError_t launch_dt(int64_t d, const fa2::Params& p, int64_t grid, hipStream_t stream) {
   switch (d) {
+    case 32: return launch_d<32, BF16, CAUSAL>(p, grid, stream);
     case 64: return launch_d<64, BF16, CAUSAL>(p, grid, stream);
+    case 96: return launch_d<96, BF16, CAUSAL>(p, grid, stream);
     case 128: return launch_d<128, BF16, CAUSAL>(p, grid, stream);
     default: return launch_d<256, BF16, CAUSAL>(p, grid, stream);
   }
@@ -100,7 +121,7 @@ const char* fa2_status_string(int status) {
     case FA2_OK: return "ok";
     case FA2_ERR_NULL_POINTER: return "a buffer pointer is NULL";
     case FA2_ERR_BAD_SHAPE: return "bad shape: B, H, N must be >= 1 and within the size limits";
-    case FA2_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension (supported: 64, 128, 256)";
+    case FA2_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension (supported: 32, 64, 96, 128, 256)";
     case FA2_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype (supported: fp16, bf16)";
     case FA2_ERR_BAD_SCALE: return "scale is not a finite number";
     case FA2_ERR_MISALIGNED: return "Q, K, V, O must be 16-byte aligned and LSE 4-byte aligned";

@@ -175,15 +175,21 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 
 // LDS layouts.  A K or V tile is BC rows (keys) of D 16-bit values, stored as
-// 16-byte chunks; chunk c of row r sits at chunk position c ^ swz(r).  The
-// gfx950 LDS serves 256 bytes (64 banks x 4 bytes) per cycle; a 16-byte read
-// by 64 lanes is served 16 lanes at a time, so 16 lanes must hit 16
-// different 16-byte bank groups to go at full rate (measured: the rows-only
-// layout runs at a quarter of that).
-//  * K rows are read 16 bytes per lane by 32 consecutive rows at one chunk.
-//    With 128-byte rows (d = 64) two rows share a 256-byte line, so rows with
-//    equal parity need distinct positions: XOR with (r/2)%8.  With rows of 256
-//    bytes or more every row starts a line: XOR with r%16.
+// 16-byte chunks, rows packed back to back; chunk c of row r sits at a
+// permuted chunk position of its row.  The gfx950 LDS serves 256 bytes (64
+// banks x 4 bytes) per cycle; a 16-byte read by 64 lanes is served 16 lanes
+// at a time, so 16 lanes must hit 16 different 16-byte bank groups to go at
+// full rate (measured: the rows-only layout runs at a quarter of that).
+//  * K rows are read 16 bytes per lane by 32 consecutive rows at one chunk
+//    (kslot: position of chunk c in row r).  With 128-byte rows (d = 64) two
+//    rows share a 256-byte line, so rows with equal parity need distinct
+//    positions: XOR with (r/2)%8.  With 64-byte rows (d = 32) four rows share
+//    a line: XOR with (r/4)%4.  With rows of 256 bytes or more every row
+//    starts a line: XOR with r%16.  192-byte rows (d = 96) start at bank group
+//    12r mod 16, which repeats every 4 rows; an XOR could leave the 12-chunk
+//    row, so the chunks rotate by (r/4)%4 instead.  Every rule depends on r
+//    only through r%32, which the row offsets added as immediates (multiples
+//    of 32 rows) preserve.
 //  * V rows are read 8 bytes per lane by ds_read_b64_tr_b16: 32 lanes at a
 //    time read 4 consecutive rows 4h+e at 64 bytes (chunks 4b..4b+3) each.
 //    With rows of 256 bytes or more the 4 rows meet the same banks (4-way
@@ -192,10 +198,27 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 //    swizzle keeps row%4, which the row offsets added as immediates (multiples
 //    of 8 rows) preserve.  Measured: 3% faster at d = 256, no change at d = 64
 //    and d = 128; the bank-conflict counter of the d = 128 kernel drops to 0.
+//    With 64-byte rows (d = 32) the 4 rows fill one line, and with 192-byte
+//    rows (d = 96) they start at bank groups 0, 12, 8, 4: no swizzle needed.
 template <int D>
-__device__ __forceinline__ int swz_k(int row) { return D == 64 ? ((row >> 1) & 7) : (row & 15); }
+__device__ __forceinline__ int kslot(int row, int c) {
+  if constexpr (D == 32) return c ^ ((row >> 2) & 3);
+  if constexpr (D == 64) return c ^ ((row >> 1) & 7);
+  if constexpr (D == 96) return (c + ((row >> 2) & 3)) % 12;
+  return c ^ (row & 15);
+}
+// Logical chunk stored at position `slot` of row r (the inverse of kslot).
 template <int D>
-__device__ __forceinline__ int swz_v(int row) { return D == 64 ? (((row >> 1) & 1) << 2) : ((row & 3) << 2); }
+__device__ __forceinline__ int klog(int row, int slot) {
+  if constexpr (D == 96) return (slot + 12 - ((row >> 2) & 3)) % 12;
+  return kslot<D>(row, slot);  // the XOR rules are involutions
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (D == 32 || D == 96) return 0;
+  if constexpr (D == 64) return ((row >> 1) & 1) << 2;
+  return (row & 3) << 2;
+}
 
 // Per-lane partial row sums of one tile above this value send the tile to the
 // rebase path: every probability of the tile is then below it, so it is finite
@@ -383,7 +406,7 @@ struct Fa2Fwd {
       const int row = lane & 31;
       const int sbase = grp * STREAMB;  // this wave's K/V stream in LDS
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks) off.k[ks] = sbase + row * ROWB + (((2 * ks + half) ^ swz_k<D>(row)) << 4);
+      for (int ks = 0; ks < DK; ++ks) off.k[ks] = sbase + row * ROWB + (kslot<D>(row, 2 * ks + half) << 4);
       // V^T transposed reads: lane group g = lane/16 serves A rows (dims)
       // 16*(g%2) + lane%16 for key half g/2; as a source, lane 16g + 4e + u
       // reads key row 4*(g/2) + e at dims 16*(g%2) + 4u .. +3.  Rows 32kb+16u
@@ -401,9 +424,10 @@ struct Fa2Fwd {
         const int r = c / CPR, col = c % CPR;
         off.vst[j] = sbase + r * ROWB + ((col ^ swz_v<D>(r)) << 4);
         // A direct-to-LDS load writes lane L's 16 bytes at the wave's base +
-        // 16 L, i.e. linear slot c; that slot of the swizzled K layout holds
-        // global chunk col ^ swz(r) (the swizzle is an involution).
-        off.gdk[j] = (r * D + (col ^ swz_k<D>(r)) * 8) * 2;
+        // 16 L, i.e. linear slot c (row r, position col); that position of the
+        // K layout holds global chunk klog(r, col), of the V layout chunk
+        // col ^ swz_v(r) (an involution).
+        off.gdk[j] = (r * D + klog<D>(r, col) * 8) * 2;
         off.gdv[j] = (r * D + (col ^ swz_v<D>(r)) * 8) * 2;
       }
       off.dma = __builtin_amdgcn_readfirstlane(sbase + (stid & ~63) * 16);

@@ -10,7 +10,7 @@ import pytest
 
 from exact_attention_21_amd import workloads as wl
 from oracle import attention_ref
-from tests.gpu_helpers import TOL, assert_close, run_gpu
+from tests.gpu_helpers import TOL, assert_close, assert_close_stress, p_rounding_bound, run_gpu, spiky_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,7 @@ def test_full_size_workload_sampled_rows(gpu_device, w):
     assert_close(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, w.dtype, w.name)
 
 
-CASES = [(d, dt, c) for d in (64, 128, 256) for dt in (wl.FP16, wl.BF16) for c in (False, True)]
+CASES = [(d, dt, c) for d in (32, 64, 96, 128, 256) for dt in (wl.FP16, wl.BF16) for c in (False, True)]
 
 
 @pytest.mark.parametrize("d,dtype,causal", CASES,
@@ -55,7 +55,7 @@ RAGGED = [1, 2, 17, 31, 33, 63, 64, 65, 127, 255, 256, 257, 513]
 
 
 @pytest.mark.parametrize("n", RAGGED)
-@pytest.mark.parametrize("d,dtype", [(64, wl.FP16), (128, wl.BF16), (256, wl.FP16)])
+@pytest.mark.parametrize("d,dtype", [(32, wl.BF16), (64, wl.FP16), (96, wl.FP16), (128, wl.BF16), (256, wl.FP16)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_lengths(gpu_device, n, d, dtype, causal):
     w = wl.Workload("r", 1, 2, n, d, dtype, causal)
@@ -122,45 +122,37 @@ def test_bad_argument_launches_nothing(gpu_device):
     import torch
     from exact_attention_21_amd import FA2_DTYPE_FP16, fa2_fwd
     from exact_attention_21_amd._binding import FA2_ERR_UNSUPPORTED_HEAD_DIM
-    q = torch.randn(1, 1, 64, 96, device=gpu_device, dtype=torch.float16)
+    q = torch.randn(1, 1, 64, 80, device=gpu_device, dtype=torch.float16)
     o = torch.full_like(q, 7.0)
     lse = torch.full((1, 1, 64), 7.0, device=gpu_device)
     st = fa2_fwd(q.data_ptr(), q.data_ptr(), q.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                 1, 1, 64, 96, 0.1, 0, FA2_DTYPE_FP16, torch.cuda.current_stream().cuda_stream)
+                 1, 1, 64, 80, 0.1, 0, FA2_DTYPE_FP16, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert st == FA2_ERR_UNSUPPORTED_HEAD_DIM
     assert torch.all(o == 7.0) and torch.all(lse == 7.0)
 
 
-def _spiky_inputs(B, H, N, d, dtype, seed, factor, where):
-    """N(0,1) inputs whose keys at the given relative positions are scaled by
-    ``factor``: the running row max jumps in the middle of the key sequence,
-    so the online softmax must move its exponent base (and rescale O and l)
-    after many tiles have already been accumulated."""
-    rng = np.random.default_rng(seed)
-    q = rng.standard_normal((B, H, N, d))
-    k = rng.standard_normal((B, H, N, d))
-    v = rng.standard_normal((B, H, N, d))
-    for frac in where:
-        j = int(frac * N)
-        k[:, :, j:j + 3] *= factor
-    return tuple(wl.round_to_storage(x, dtype) for x in (q, k, v))
+STRESS_DIMS = (32, 64, 96, 128, 256)
 
 
-@pytest.mark.parametrize("d,dtype", [(64, wl.FP16), (128, wl.BF16), (256, wl.FP16)])
+@pytest.mark.parametrize("d", STRESS_DIMS)
+@pytest.mark.parametrize("dtype", [wl.FP16, wl.BF16])
 @pytest.mark.parametrize("causal", [False, True])
 def test_late_score_jumps_rebase(gpu_device, d, dtype, causal):
     """Score jumps of several hundred (base-2 units) half-way through and near
-    the end of the keys; every row with a jump visible must be rescaled."""
+    the end of the keys; every row with a jump visible must be rescaled.  The
+    jumps put most of a row's weight on one or two keys, so the O check allows
+    the rounding of P on top of the tolerance (p_rounding_bound)."""
     B, H, N = 1, 2, 1500
-    q, k, v = _spiky_inputs(B, H, N, d, dtype, seed=31, factor=12.0, where=(0.5, 0.83))
+    q, k, v = spiky_inputs(B, H, N, d, dtype, seed=31, factor=12.0, where=(0.5, 0.83))
     scale = 1 / math.sqrt(d)
     o, lse = run_gpu(q, k, v, dtype, scale, causal, gpu_device)
     o_ref, lse_ref = attention_ref(*(wl.to_float64(x, dtype) for x in (q, k, v)), scale, causal)
-    assert_close(o, lse, o_ref, lse_ref, dtype, f"late jumps d{d} {dtype} causal={causal}")
+    bound = p_rounding_bound(q, k, v, o_ref, dtype, scale, causal)
+    assert_close_stress(o, lse, o_ref, lse_ref, bound, dtype, f"late jumps d{d} {dtype} causal={causal}")
 
 
-@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("d", STRESS_DIMS)
 @pytest.mark.parametrize("dtype", [wl.FP16, wl.BF16])
 @pytest.mark.parametrize("causal", [False, True])
 def test_dominant_first_keys(gpu_device, d, dtype, causal):
@@ -168,11 +160,12 @@ def test_dominant_first_keys(gpu_device, d, dtype, causal):
     an exponent base taken from the first tile stays the row max, and the
     later probabilities are tiny (fp16 subnormal) but still counted."""
     B, H, N = 1, 2, 1800
-    q, k, v = _spiky_inputs(B, H, N, d, dtype, seed=53, factor=4.0, where=(0.0,))
+    q, k, v = spiky_inputs(B, H, N, d, dtype, seed=53, factor=4.0, where=(0.0,))
     scale = 1 / math.sqrt(d)
     o, lse = run_gpu(q, k, v, dtype, scale, causal, gpu_device)
     o_ref, lse_ref = attention_ref(*(wl.to_float64(x, dtype) for x in (q, k, v)), scale, causal)
-    assert_close(o, lse, o_ref, lse_ref, dtype, f"dominant first keys d{d} {dtype} causal={causal}")
+    bound = p_rounding_bound(q, k, v, o_ref, dtype, scale, causal)
+    assert_close_stress(o, lse, o_ref, lse_ref, bound, dtype, f"dominant first keys d{d} {dtype} causal={causal}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -187,4 +180,5 @@ def test_steadily_growing_scores(gpu_device, causal):
     q, k, v = (wl.round_to_storage(x, wl.FP16) for x in (q, k, v))
     o, lse = run_gpu(q, k, v, wl.FP16, 0.125, causal, gpu_device)
     o_ref, lse_ref = attention_ref(*(wl.to_float64(x, wl.FP16) for x in (q, k, v)), 0.125, causal)
-    assert_close(o, lse, o_ref, lse_ref, wl.FP16, f"growing scores causal={causal}")
+    bound = p_rounding_bound(q, k, v, o_ref, wl.FP16, 0.125, causal)
+    assert_close_stress(o, lse, o_ref, lse_ref, bound, wl.FP16, f"growing scores causal={causal}")
