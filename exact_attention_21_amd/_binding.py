@@ -37,6 +37,23 @@ class Fa2Error(RuntimeError):
         super().__init__(f"{where}: status {status} ({fa2_status_string(status)})")
 
 
+def open_library(path: str) -> ctypes.CDLL:
+    """Load a build of the library from `path` with the C signatures declared."""
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                            ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa2_fwd.restype = ctypes.c_int
+    lib.fa2_status_string.argtypes = [ctypes.c_int]
+    lib.fa2_status_string.restype = ctypes.c_char_p
+    lib.fa2_launch_info.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int),
+                                    ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                    ctypes.POINTER(ctypes.c_int)]
+    lib.fa2_launch_info.restype = ctypes.c_int
+    return lib
+
+
 def library() -> ctypes.CDLL:
     """Load libfa2.so once; raise if it is not built."""
     global _lib
@@ -45,19 +62,7 @@ def library() -> ctypes.CDLL:
             if not os.path.exists(LIB_PATH):
                 raise RuntimeError(
                     f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
-            lib = ctypes.CDLL(LIB_PATH)
-            vp, i64 = ctypes.c_void_p, ctypes.c_int64
-            lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
-                                    ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
-            lib.fa2_fwd.restype = ctypes.c_int
-            lib.fa2_status_string.argtypes = [ctypes.c_int]
-            lib.fa2_status_string.restype = ctypes.c_char_p
-            lib.fa2_launch_info.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
-                                            ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int),
-                                            ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
-                                            ctypes.POINTER(ctypes.c_int)]
-            lib.fa2_launch_info.restype = ctypes.c_int
-            _lib = lib
+            _lib = open_library(LIB_PATH)
         return _lib
 
 

@@ -26,10 +26,10 @@ struct TileCfg {
 // d = 32 and 96 use 64-key tiles: with 32 keys their tiles have fewer
 // 16-byte chunks than the threads that load them (d = 32) or a fractional
 // number per thread (d = 96).  d = 96 runs without split-KV so that its ring
-// (96 KiB) fits the LDS.
+// (96 KiB) fits the LDS.  (FA2_SPLIT_KV = 0: d = 32 and 64 without split-KV.)
 constexpr TileCfg cfg_for(int64_t d) {
-  return d == 32    ? TileCfg{64, 8, 1}
-         : d == 64  ? TileCfg{32, 8, 2}
+  return d == 32    ? (FA2_SPLIT_KV ? TileCfg{64, 8, 1} : TileCfg{64, 4, 1})
+         : d == 64  ? (FA2_SPLIT_KV ? TileCfg{32, 8, 2} : TileCfg{32, 4, 2})
          : d == 96  ? TileCfg{64, 4, 1}
          : d == 128 ? TileCfg{32, 4, 2}
                     : TileCfg{32, 4, 1};

@@ -174,6 +174,27 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   }
 }
 
+// Design switches.  The library's own build leaves each at its default, the
+// shipped design; a build that flips one measures what that choice is worth.
+//   FA2_KV_SWIZZLE     1: the K/V chunk permutations below; 0: plain row-major tiles.
+//   FA2_DEEP_RING      0: 4-slot K/V rings; 1: 8 slots where they fit the LDS.
+//   FA2_UNCHECKED_RUN  1: fixed-base unchecked first run (every d but 128);
+//                      0: the checked pipeline only.
+//   FA2_SPLIT_KV       1: two split-KV wave groups at d = 32 and 64 (host side);
+//                      0: one group of 4 waves.
+#ifndef FA2_KV_SWIZZLE
+#define FA2_KV_SWIZZLE 1
+#endif
+#ifndef FA2_DEEP_RING
+#define FA2_DEEP_RING 0
+#endif
+#ifndef FA2_UNCHECKED_RUN
+#define FA2_UNCHECKED_RUN 1
+#endif
+#ifndef FA2_SPLIT_KV
+#define FA2_SPLIT_KV 1
+#endif
+
 // LDS layouts.  A K or V tile is BC rows (keys) of D 16-bit values, stored as
 // 16-byte chunks, rows packed back to back; chunk c of row r sits at a
 // permuted chunk position of its row.  The gfx950 LDS serves 256 bytes (64
@@ -202,6 +223,7 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 //    rows (d = 96) they start at bank groups 0, 12, 8, 4: no swizzle needed.
 template <int D>
 __device__ __forceinline__ int kslot(int row, int c) {
+  if constexpr (!FA2_KV_SWIZZLE) return c;
   if constexpr (D == 32) return c ^ ((row >> 2) & 3);
   if constexpr (D == 64) return c ^ ((row >> 1) & 7);
   if constexpr (D == 96) return (c + ((row >> 2) & 3)) % 12;
@@ -210,12 +232,12 @@ __device__ __forceinline__ int kslot(int row, int c) {
 // Logical chunk stored at position `slot` of row r (the inverse of kslot).
 template <int D>
 __device__ __forceinline__ int klog(int row, int slot) {
-  if constexpr (D == 96) return (slot + 12 - ((row >> 2) & 3)) % 12;
+  if constexpr (D == 96 && FA2_KV_SWIZZLE) return (slot + 12 - ((row >> 2) & 3)) % 12;
   return kslot<D>(row, slot);  // the XOR rules are involutions
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int row) {
-  if constexpr (D == 32 || D == 96) return 0;
+  if constexpr (!FA2_KV_SWIZZLE || D == 32 || D == 96) return 0;
   if constexpr (D == 64) return ((row >> 1) & 1) << 2;
   return (row & 3) << 2;
 }
@@ -233,8 +255,12 @@ template <int D, int BC, int NW, int QB, bool BF16, bool CAUSAL>
 struct Fa2Fwd {
   static constexpr int THREADS = NW * 64;
   // Pipelined schedule: K and V tiles each in a ring of PIPE_RING LDS slots,
-  // one barrier per PIPE_RING / 2 sub-iterations.
-  static constexpr int PIPE_RING = 4;
+  // one barrier per PIPE_RING / 2 sub-iterations.  (An 8-slot ring must fit
+  // the 160 KiB LDS and keep each ring within the 64 KiB of ds immediates.)
+  static constexpr int DEEP_RING_BYTES = 8 * BC * D * 2;
+  static constexpr bool DEEP_RING_FITS =
+      DEEP_RING_BYTES <= 65536 && (NW == 8 ? 2 : 1) * 2 * DEEP_RING_BYTES <= 160 * 1024;
+  static constexpr int PIPE_RING = FA2_DEEP_RING && DEEP_RING_FITS ? 8 : 4;
   static constexpr int PIPE_G = PIPE_RING / 2;
   static constexpr int QW = 32 * QB;             // query rows per wave
   // With 8 waves, two groups of 4 own the same query rows and split the key
@@ -504,7 +530,7 @@ struct Fa2Fwd {
   // overflowed (see run_pipe).  Measured: 6% faster at d = 64, 12% at d = 256,
   // 5% slower at d = 128 (the second copy of the pipeline crowds its
   // registers), which keeps only the checked run.
-  static constexpr bool OPTIMISTIC = D != 128;
+  static constexpr bool OPTIMISTIC = FA2_UNCHECKED_RUN && D != 128;
 
   // Loop-invariant context.
   struct Ctx {
