@@ -16,27 +16,33 @@
 namespace {
 
 // Tile configuration per head dimension: keys per K/V tile, waves per
-// workgroup (8: two split-KV groups of 4), 32-row query blocks per wave.
+// workgroup, 32-row query blocks per wave, split-KV wave groups (2: two
+// groups of 4 waves over the same rows).
 struct TileCfg {
   int bc;
   int nw;
   int qb;
+  int kvg;
 };
 
-// d = 32 and 96 use 64-key tiles: with 32 keys their tiles have fewer
-// 16-byte chunks than the threads that load them (d = 32) or a fractional
-// number per thread (d = 96).  d = 96 runs without split-KV so that its ring
-// (96 KiB) fits the LDS.  (FA2_SPLIT_KV = 0: d = 32 and 64 without split-KV.)
+// Two waves per SIMD (8 per workgroup) let one wave's softmax issue beside
+// the other's MFMAs; d = 32 and 64 get them from split-KV, d = 128 from 8
+// waves of 32 rows on one K/V stream (64 rows per wave, 4 waves, measured
+// 8% slower).  d = 32 and 96 use 64-key tiles: with 32 keys their tiles have
+// fewer 16-byte chunks than the threads that load them (d = 32) or a
+// fractional number per thread (d = 96).  d = 96 runs without split-KV so
+// that its ring (96 KiB) fits the LDS.  (FA2_SPLIT_KV = 0: d = 32 and 64
+// with one group of 4 waves.)
 constexpr TileCfg cfg_for(int64_t d) {
-  return d == 32    ? (FA2_SPLIT_KV ? TileCfg{64, 8, 1} : TileCfg{64, 4, 1})
-         : d == 64  ? (FA2_SPLIT_KV ? TileCfg{32, 8, 2} : TileCfg{32, 4, 2})
-         : d == 96  ? TileCfg{64, 4, 1}
-         : d == 128 ? TileCfg{32, 4, 2}
-                    : TileCfg{32, 4, 1};
+  return d == 32    ? (FA2_SPLIT_KV ? TileCfg{64, 8, 1, 2} : TileCfg{64, 4, 1, 1})
+         : d == 64  ? (FA2_SPLIT_KV ? TileCfg{32, 8, 2, 2} : TileCfg{32, 4, 2, 1})
+         : d == 96  ? TileCfg{64, 4, 1, 1}
+         : d == 128 ? TileCfg{32, 8, 1, 1}
+                    : TileCfg{32, 4, 1, 1};
 }
 
 template <int D>
-using KernelFor = fa2::Fa2Fwd<D, cfg_for(D).bc, cfg_for(D).nw, cfg_for(D).qb, false, false>;
+using KernelFor = fa2::Fa2Fwd<D, cfg_for(D).bc, cfg_for(D).nw, cfg_for(D).qb, cfg_for(D).kvg, false, false>;
 
 constexpr int rows_per_wg(int64_t d) {
   return d == 32 ? KernelFor<32>::BR : d == 64 ? KernelFor<64>::BR : d == 96 ? KernelFor<96>::BR
@@ -80,11 +86,11 @@ fa2_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, 
   return FA2_OK;
 }
 
-template <int D, int BC, int NW, int QB, bool BF16, bool CAUSAL>
+template <int D, int BC, int NW, int QB, int KVG, bool BF16, bool CAUSAL>
 hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
-  constexpr int lds = fa2::Fa2Fwd<D, BC, NW, QB, BF16, CAUSAL>::LDS_BYTES;
+  constexpr int lds = fa2::Fa2Fwd<D, BC, NW, QB, KVG, BF16, CAUSAL>::LDS_BYTES;
   static_assert(lds == lds_bytes_for(D), "LDS size");
-  auto kern = fa2::fa2_fwd_kernel<D, BC, NW, QB, BF16, CAUSAL>;
+  auto kern = fa2::fa2_fwd_kernel<D, BC, NW, QB, KVG, BF16, CAUSAL>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
@@ -98,7 +104,7 @@ hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream) {
   constexpr TileCfg c = cfg_for(D);
-  return launch<D, c.bc, c.nw, c.qb, BF16, CAUSAL>(p, grid, stream);
+  return launch<D, c.bc, c.nw, c.qb, c.kvg, BF16, CAUSAL>(p, grid, stream);
 }
 
 template <bool BF16, bool CAUSAL>

@@ -251,21 +251,23 @@ constexpr float kTileSumLimit = 32768.0f;
 // below any score that a visible key overflows the row sum.
 constexpr float kUnseenBase = 1.0e30f;
 
-template <int D, int BC, int NW, int QB, bool BF16, bool CAUSAL>
+template <int D, int BC, int NW, int QB, int KVG, bool BF16, bool CAUSAL>
 struct Fa2Fwd {
+  static_assert(KVG == 1 || (KVG == 2 && NW == 8), "split-KV runs two groups of 4 waves");
   static constexpr int THREADS = NW * 64;
   // Pipelined schedule: K and V tiles each in a ring of PIPE_RING LDS slots,
   // one barrier per PIPE_RING / 2 sub-iterations.  (An 8-slot ring must fit
   // the 160 KiB LDS and keep each ring within the 64 KiB of ds immediates.)
   static constexpr int DEEP_RING_BYTES = 8 * BC * D * 2;
   static constexpr bool DEEP_RING_FITS =
-      DEEP_RING_BYTES <= 65536 && (NW == 8 ? 2 : 1) * 2 * DEEP_RING_BYTES <= 160 * 1024;
+      DEEP_RING_BYTES <= 65536 && KVG * 2 * DEEP_RING_BYTES <= 160 * 1024;
   static constexpr int PIPE_RING = FA2_DEEP_RING && DEEP_RING_FITS ? 8 : 4;
   static constexpr int PIPE_G = PIPE_RING / 2;
   static constexpr int QW = 32 * QB;             // query rows per wave
-  // With 8 waves, two groups of 4 own the same query rows and split the key
-  // tiles (split-KV), so every SIMD runs two waves.
-  static constexpr bool SPLIT = NW == 8;
+  // KVG = 2 (split-KV): two groups of 4 waves own the same query rows and
+  // split the key tiles.  Otherwise all NW waves own rows of their own and
+  // share one K/V stream.  With 8 waves every SIMD runs two.
+  static constexpr bool SPLIT = KVG == 2;
   static constexpr int QWAVES = SPLIT ? NW / 2 : NW;
   static constexpr int BR = QWAVES * QW;         // query rows per workgroup
   // Threads that stage one K/V stream (split-KV: one stream per group).
@@ -527,9 +529,9 @@ struct Fa2Fwd {
   // the rounded sum within 2^-11 (natural-log units) of it.
   static constexpr bool LSE_FP32 = BF16;
   // Pipelined schedule: first an unchecked run, rerun checked only if some row
-  // overflowed (see run_pipe).  Measured: 6% faster at d = 64, 12% at d = 256,
-  // 5% slower at d = 128 (the second copy of the pipeline crowds its
-  // registers), which keeps only the checked run.
+  // overflowed (see run_pipe).  Measured: 6% faster at d = 64, 12% at d = 256.
+  // At d = 128 the second copy of the pipeline does not fit the registers of
+  // two waves per SIMD (it spills), so d = 128 keeps only the checked run.
   static constexpr bool OPTIMISTIC = FA2_UNCHECKED_RUN && D != 128;
 
   // Loop-invariant context.
@@ -1079,10 +1081,10 @@ struct Fa2Fwd {
 
 };
 
-template <int D, int BC, int NW, int QB, bool BF16, bool CAUSAL>
+template <int D, int BC, int NW, int QB, int KVG, bool BF16, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64, 1) fa2_fwd_kernel(const Params p) {
   extern __shared__ __attribute__((aligned(16))) char lds_generic[];
-  Fa2Fwd<D, BC, NW, QB, BF16, CAUSAL>::run(
+  Fa2Fwd<D, BC, NW, QB, KVG, BF16, CAUSAL>::run(
       p, (__attribute__((address_space(3))) char*)(__attribute__((address_space(3))) void*)lds_generic);
 }
 
