@@ -14,7 +14,10 @@ Sources (page title, then the part of the page followed):
   skeleton: Q, K, V, O are [B, H, N, d], LSE is [B, H, N] fp32, the scale is
   applied to the scores before the row max, the causal mask hides key j from
   query i when j > i, a row with no visible key gives O = 0 and LSE = +inf;
-  §15.4.3: masking happens before the softmax.
+  §15.4.3: masking happens before the softmax; the note after the §15.3
+  skeleton: with sliding-window or padding masks a row can meet only hidden keys
+  in its first tiles, which is what the -inf guards (exponent base 0 while the
+  row max is -inf, O = 0 and LSE = +inf when l = 0) are there for.
 
 Precision: every step is fp64.  Inputs are the already-rounded fp16/bf16 values,
 upcast exactly by the caller.  ``scale`` is rounded to fp32 first, because that
@@ -43,6 +46,22 @@ def _visible_count(i: int, n: int, causal: bool) -> int:
     same sequence (square, top-left aligned).
     """
     return i + 1 if causal else n
+
+
+def _visible_range(i: int, window_left: int, window_right: int, key_len: int):
+    """Keys visible to query row ``i`` under a sliding window and a key length.
+
+    Reading (yangyitao.com ch.15, the note after the §15.3 skeleton, names
+    sliding-window and padding masks without fixing their form): key j is
+    visible to query i iff j < key_len (keys at or past it are padding),
+    j >= i - window_left (no left bound when window_left < 0) and
+    j <= i + window_right (no right bound when window_right < 0).  The visible
+    keys are the range [lo, hi), empty when hi == lo.  window_left < 0 with
+    window_right = 0 is the causal mask.
+    """
+    lo = 0 if window_left < 0 else max(0, i - window_left)
+    hi = key_len if window_right < 0 else min(key_len, i + window_right + 1)
+    return lo, max(lo, hi)
 
 
 def attention_ref(q, k, v, scale: float, causal: bool, rows=None):
@@ -96,7 +115,8 @@ def attention_ref(q, k, v, scale: float, causal: bool, rows=None):
     return out, lse
 
 
-def attention_online_merge(q, k, v, scale: float, causal: bool, block: int, reverse: bool = False):
+def attention_online_merge(q, k, v, scale: float, causal: bool, block: int, reverse: bool = False,
+                           window=None, key_lens=None):
     """The same result through the pages' online (m, l) merge over key blocks, in fp64.
 
     Follows "FlashAttention-2 MMA 代码学习" (chuoer47.github.io) step 1: for
@@ -109,7 +129,10 @@ def attention_online_merge(q, k, v, scale: float, causal: bool, block: int, reve
 
     ``block`` is the number of keys per block; ``reverse`` walks the blocks from
     the last to the first.  The result must not depend on either: the tests use
-    that to pin the algebra against ``attention_ref``.
+    that to pin the algebra against ``attention_ref``.  ``window`` = (left,
+    right) and ``key_lens`` add the masks of ``attention_ref_masked`` (a
+    negative bound is no bound; lengths are clamped to [0, N]); under them a row
+    can see only hidden keys in its first blocks, where the -inf guards act.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -130,9 +153,18 @@ def attention_online_merge(q, k, v, scale: float, causal: bool, block: int, reve
             for k0 in starts:
                 k1 = min(n, k0 + block)
                 s = (q[b, h] @ k[b, h, k0:k1].T) * c
+                kj = np.arange(k0, k1)[None, :]
+                hidden = np.zeros((n, k1 - k0), dtype=bool)
                 if causal:
-                    kj = np.arange(k0, k1)[None, :]
-                    s = np.where(kj <= qi, s, -np.inf)
+                    hidden |= kj > qi
+                if window is not None:
+                    if window[0] >= 0:
+                        hidden |= kj < qi - window[0]
+                    if window[1] >= 0:
+                        hidden |= kj > qi + window[1]
+                if key_lens is not None:
+                    hidden |= kj >= min(max(int(key_lens[b]), 0), n)
+                s = np.where(hidden, -np.inf, s)
                 m_blk = s.max(axis=1)
                 m_new = np.maximum(m_run, m_blk)
                 base = np.where(np.isneginf(m_new), 0.0, m_new)
@@ -145,4 +177,51 @@ def attention_online_merge(q, k, v, scale: float, causal: bool, block: int, reve
             out[b, h] = o_run / safe_l[:, None]
             with np.errstate(divide="ignore"):
                 lse[b, h] = np.where(l_run == 0.0, np.inf, m_run + np.log(safe_l))
+    return out, lse
+
+
+def attention_ref_masked(q, k, v, scale: float, window_left: int, window_right: int,
+                         key_lens=None, rows=None):
+    """attention_ref with a sliding window and per-sequence key lengths.
+
+    Key j is visible to query i as ``_visible_range`` states; ``key_lens`` is
+    None (no padding) or B integers, each clamped to [0, N].  The softmax runs
+    over the visible keys only (masking before the softmax, ch.15 §15.4.3); a
+    row with no visible key gets O = 0 and LSE = +inf (§15.3, final
+    normalisation and LSE store).  Returns (O, LSE) shaped as attention_ref's.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if q.ndim != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    b_, h_, n, d = q.shape
+    c = float(np.float32(scale))
+    lens = [n] * b_ if key_lens is None else [min(max(int(x), 0), n) for x in key_lens]
+    if len(lens) != b_:
+        raise ValueError("key_lens must hold one length per batch")
+    if rows is None:
+        rows = np.arange(n)
+    rows = np.asarray(rows, dtype=np.int64)
+    r_ = rows.size
+    out = np.zeros((b_, h_, r_, d), dtype=np.float64)
+    lse = np.full((b_, h_, r_), np.inf, dtype=np.float64)
+    j = np.arange(n)[None, :]
+    for b in range(b_):
+        bounds = np.array([_visible_range(int(i), window_left, window_right, lens[b]) for i in rows],
+                          dtype=np.int64).reshape(r_, 2)
+        for h in range(h_):
+            for r0 in range(0, r_, _ROW_BLOCK):
+                idx = rows[r0:r0 + _ROW_BLOCK]
+                lo = bounds[r0:r0 + idx.size, :1]
+                hi = bounds[r0:r0 + idx.size, 1:]
+                visible = (j >= lo) & (j < hi)
+                s = np.where(visible, (q[b, h, idx, :] @ k[b, h].T) * c, -np.inf)
+                seen = visible.any(axis=1)
+                m = np.where(seen, s.max(axis=1), 0.0)
+                p = np.where(visible, np.exp(s - m[:, None]), 0.0)
+                l = p.sum(axis=1)
+                safe_l = np.where(seen, l, 1.0)
+                out[b, h, r0:r0 + idx.size, :] = np.where(seen[:, None], (p @ v[b, h]) / safe_l[:, None], 0.0)
+                lse[b, h, r0:r0 + idx.size] = np.where(seen, m + np.log(safe_l), np.inf)
     return out, lse

@@ -253,3 +253,152 @@ def test_pins_catch_planted_mistakes(monkeypatch, mutant):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught >= 1, f"planted mistake {mutant} went unnoticed"
+
+
+# ---- sliding-window and padding masks -------------------------------------
+
+from oracle import attention_ref_masked  # noqa: E402
+
+MASKS = [(-1, -1, None), (0, 0, None), (1, 0, None), (2, 1, None), (0, -1, None), (-1, 0, None),
+         (-1, -1, [0, 1]), (-1, -1, [1, 3]), (3, 2, [2, 17]), (-1, 0, [5, 0])]
+
+
+def brute_force_masked(q, k, v, scale, window_left, window_right, key_lens):
+    """Pure-Python definition with the mask written out: key j counts for
+    query i when j < len, (left bound absent or j >= i - left) and (right
+    bound absent or j <= i + right); no visible key gives O = 0, LSE = inf."""
+    c = float(np.float32(scale))
+    B, H, N, d = q.shape
+    O = np.zeros((B, H, N, d))
+    L = np.full((B, H, N), math.inf)
+    for b in range(B):
+        n_keys = N if key_lens is None else min(max(key_lens[b], 0), N)
+        for h in range(H):
+            for i in range(N):
+                js = [j for j in range(N) if j < n_keys
+                      and (window_left < 0 or j >= i - window_left)
+                      and (window_right < 0 or j <= i + window_right)]
+                if not js:
+                    continue
+                e = {j: math.exp(c * math.fsum(float(q[b, h, i, t]) * float(k[b, h, j, t])
+                                              for t in range(d))) for j in js}
+                z = math.fsum(e.values())
+                for t in range(d):
+                    O[b, h, i, t] = math.fsum(e[j] * float(v[b, h, j, t]) for j in js) / z
+                L[b, h, i] = math.log(z)
+    return O, L
+
+
+def _assert_close_inf(a, b, tol, what):
+    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    assert np.array_equal(np.isinf(a), np.isinf(b)), what
+    assert np.max(np.where(both_inf, 0.0, np.abs(np.where(both_inf, 0.0, a) - np.where(both_inf, 0.0, b)))) <= tol, what
+
+
+def check_brute_force_masked(fn, tol=1e-12):
+    for n_case, shape in enumerate(TINY_SHAPES):
+        for wl, wr, lens in MASKS:
+            lens_b = None if lens is None else (lens * shape[0])[:shape[0]]
+            q, k, v = (_rand(shape, 10 * n_case + t) for t in range(3))
+            scale = 1.0 / math.sqrt(shape[-1])
+            O, L = fn(q, k, v, scale, wl, wr, lens_b)
+            Ob, Lb = brute_force_masked(q, k, v, scale, wl, wr, lens_b)
+            assert np.max(np.abs(O - Ob)) <= tol, (shape, wl, wr, lens_b)
+            _assert_close_inf(L, Lb, tol, (shape, wl, wr, lens_b))
+
+
+def check_closed_forms_masked(fn, tol=1e-12):
+    for case in json.load(open(GOLDEN))["cases"]:
+        q = np.array(case["q"], dtype=np.float64)[None, None]
+        k = np.array(case["k"], dtype=np.float64)[None, None]
+        v = np.array(case["v"], dtype=np.float64)[None, None]
+        for m in case["masked"]:
+            O, L = fn(q, k, v, case["scale"], m["window_left"], m["window_right"], [m["key_len"]])
+            what = (case["name"], m["window_left"], m["window_right"], m["key_len"])
+            assert np.max(np.abs(O[0, 0] - np.array(m["O"]))) <= tol, what
+            _assert_close_inf(L[0, 0], np.array(m["LSE"], dtype=np.float64), tol, what)
+
+
+def test_masked_brute_force():
+    check_brute_force_masked(attention_ref_masked)
+
+
+def test_masked_closed_forms():
+    check_closed_forms_masked(attention_ref_masked)
+
+
+def test_masked_reduces_to_full_and_causal():
+    q, k, v = (_rand((2, 2, 300, 8), s) for s in range(3))
+    for causal, (wl, wr) in ((False, (-1, -1)), (True, (-1, 0))):
+        O, L = attention_ref(q, k, v, 0.4, causal)
+        Om, Lm = attention_ref_masked(q, k, v, 0.4, wl, wr, None)
+        np.testing.assert_allclose(Om, O, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(Lm, L, rtol=0, atol=1e-13)
+    # A key length of N is no padding; a window wider than N is no window.
+    Om, Lm = attention_ref_masked(q, k, v, 0.4, 300, 299, [300, 300])
+    O, L = attention_ref(q, k, v, 0.4, False)
+    np.testing.assert_allclose(Om, O, rtol=0, atol=1e-13)
+
+
+def test_masked_padding_does_not_leak():
+    """Keys and values past the key length may hold anything."""
+    B, H, N, d = 2, 2, 40, 8
+    q, k, v = (_rand((B, H, N, d), s) for s in range(3))
+    lens = [23, 7]
+    k2, v2 = k.copy(), v.copy()
+    for b, n_b in enumerate(lens):
+        k2[b, :, n_b:] = 1e3
+        v2[b, :, n_b:] = -1e6
+    for wl, wr in ((-1, -1), (5, 0), (3, 3)):
+        O, L = attention_ref_masked(q, k, v, 0.3, wl, wr, lens)
+        O2, L2 = attention_ref_masked(q, k2, v2, 0.3, wl, wr, lens)
+        np.testing.assert_array_equal(O, O2)
+        np.testing.assert_array_equal(L, L2)
+
+
+def test_masked_fully_hidden_rows():
+    """Rows that see no key: all keys padding, or a window that lies past the
+    key length."""
+    q, k, v = (_rand((2, 1, 12, 4), s) for s in range(3))
+    O, L = attention_ref_masked(q, k, v, 1.0, 0, 2, [0, 4])
+    assert np.all(O[0] == 0) and np.all(np.isposinf(L[0]))
+    # batch 1: rows 0..3 see their own key; rows >= 4 see none (keys 4.. are padding).
+    np.testing.assert_array_equal(np.isposinf(L[1, 0]), np.arange(12) >= 4)
+    assert np.all(O[1, 0, 4:] == 0)
+
+
+@pytest.mark.parametrize("block", [1, 7, 64])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("mask", [(5, 0, None), (2, 9, [40, 13]), (-1, -1, [0, 70]), (0, 0, None)])
+def test_online_merge_masked_reaches_definition(block, reverse, mask):
+    """Under these masks some rows see only hidden keys in their first blocks
+    (or in every block): the merge's -inf guards decide the result."""
+    wl, wr, lens = mask
+    q, k, v = (_rand((2, 2, 70, 8), s, 2.0) for s in range(3))
+    O, L = attention_ref_masked(q, k, v, 0.5, wl, wr, lens)
+    O2, L2 = attention_online_merge(q, k, v, 0.5, False, block, reverse, window=(wl, wr), key_lens=lens)
+    np.testing.assert_allclose(O2, O, rtol=0, atol=1e-12)
+    _assert_close_inf(L2, L, 1e-12, (block, reverse, mask))
+
+
+MASK_MUTANTS = {
+    "left_bound_off_by_one": lambda i, wl, wr, n: (0 if wl < 0 else max(0, i - wl + 1),
+                                                   n if wr < 0 else min(n, i + wr + 1)),
+    "right_bound_exclusive": lambda i, wl, wr, n: (0 if wl < 0 else max(0, i - wl),
+                                                   n if wr < 0 else min(n, i + wr)),
+    "padding_ignored": lambda i, wl, wr, n: (0 if wl < 0 else max(0, i - wl),
+                                             10 ** 9 if wr < 0 else i + wr + 1),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MASK_MUTANTS))
+def test_masked_pins_catch_planted_mistakes(monkeypatch, mutant):
+    bad = MASK_MUTANTS[mutant]
+    monkeypatch.setattr(oracle_mod, "_visible_range", lambda i, wl, wr, n: (lambda lo, hi: (lo, max(lo, hi)))(*bad(i, wl, wr, n)))
+    caught = 0
+    for check in (check_brute_force_masked, check_closed_forms_masked):
+        try:
+            check(attention_ref_masked)
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"planted mistake {mutant} went unnoticed"
