@@ -25,7 +25,7 @@ FA2_ERR_OVERLAP = 7
 FA2_ERR_HIP = 8
 
 # Every symbol include/fa2.h declares.
-EXPORTED = ("fa2_fwd", "fa2_status_string", "fa2_launch_info")
+EXPORTED = ("fa2_fwd", "fa2_fwd_masked", "fa2_status_string", "fa2_launch_info")
 
 _lock = threading.Lock()
 _lib = None
@@ -44,6 +44,9 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
                             ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
     lib.fa2_fwd.restype = ctypes.c_int
+    lib.fa2_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                                   i64, i64, vp, ctypes.c_int, vp]
+    lib.fa2_fwd_masked.restype = ctypes.c_int
     lib.fa2_status_string.argtypes = [ctypes.c_int]
     lib.fa2_status_string.restype = ctypes.c_char_p
     lib.fa2_launch_info.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
@@ -70,6 +73,14 @@ def fa2_fwd(Q: int, K: int, V: int, O: int, LSE: int, B: int, H: int, N: int, d:
             scale: float, is_causal: int, dtype: int, stream: int) -> int:
     """Same arguments and status as the C function; pointers are integers."""
     return library().fa2_fwd(Q, K, V, O, LSE, B, H, N, d, scale, int(is_causal), int(dtype), stream)
+
+
+def fa2_fwd_masked(Q: int, K: int, V: int, O: int, LSE: int, B: int, H: int, N: int, d: int,
+                   scale: float, window_left: int, window_right: int, key_lens: int | None,
+                   dtype: int, stream: int) -> int:
+    """Same arguments and status as the C function; pointers are integers (key_lens may be None)."""
+    return library().fa2_fwd_masked(Q, K, V, O, LSE, B, H, N, d, scale, int(window_left), int(window_right),
+                                    key_lens, int(dtype), stream)
 
 
 def fa2_status_string(status: int) -> str:

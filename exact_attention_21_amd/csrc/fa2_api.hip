@@ -86,11 +86,11 @@ fa2_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, 
   return FA2_OK;
 }
 
-template <int D, int BC, int NW, int QB, int KVG, bool BF16, bool CAUSAL>
+template <int D, int BC, int NW, int QB, int KVG, bool BF16, int MASK>
 hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
-  constexpr int lds = fa2::Fa2Fwd<D, BC, NW, QB, KVG, BF16, CAUSAL>::LDS_BYTES;
+  constexpr int lds = fa2::Fa2Fwd<D, BC, NW, QB, KVG, BF16, MASK>::LDS_BYTES;
   static_assert(lds == lds_bytes_for(D), "LDS size");
-  auto kern = fa2::fa2_fwd_kernel<D, BC, NW, QB, KVG, BF16, CAUSAL>;
+  auto kern = fa2::fa2_fwd_kernel<D, BC, NW, QB, KVG, BF16, MASK>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
@@ -101,21 +101,76 @@ hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, int MASK>
 hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream) {
   constexpr TileCfg c = cfg_for(D);
-  return launch<D, c.bc, c.nw, c.qb, c.kvg, BF16, CAUSAL>(p, grid, stream);
+  return launch<D, c.bc, c.nw, c.qb, c.kvg, BF16, MASK>(p, grid, stream);
 }
 
-template <bool BF16, bool CAUSAL>
+template <bool BF16, int MASK>
 hipError_t launch_dt(int64_t d, const fa2::Params& p, int64_t grid, hipStream_t stream) {
   switch (d) {
-    case 32: return launch_d<32, BF16, CAUSAL>(p, grid, stream);
-    case 64: return launch_d<64, BF16, CAUSAL>(p, grid, stream);
-    case 96: return launch_d<96, BF16, CAUSAL>(p, grid, stream);
-    case 128: return launch_d<128, BF16, CAUSAL>(p, grid, stream);
-    default: return launch_d<256, BF16, CAUSAL>(p, grid, stream);
+    case 32: return launch_d<32, BF16, MASK>(p, grid, stream);
+    case 64: return launch_d<64, BF16, MASK>(p, grid, stream);
+    case 96: return launch_d<96, BF16, MASK>(p, grid, stream);
+    case 128: return launch_d<128, BF16, MASK>(p, grid, stream);
+    default: return launch_d<256, BF16, MASK>(p, grid, stream);
   }
+}
+
+template <bool BF16>
+hipError_t launch_mask(int mask, int64_t d, const fa2::Params& p, int64_t grid, hipStream_t stream) {
+  switch (mask) {
+    case fa2::kMaskNone: return launch_dt<BF16, fa2::kMaskNone>(d, p, grid, stream);
+    case fa2::kMaskCausal: return launch_dt<BF16, fa2::kMaskCausal>(d, p, grid, stream);
+    default: return launch_dt<BF16, fa2::kMaskGeneral>(d, p, grid, stream);
+  }
+}
+
+// Checks shared by both entry points (everything but the mask arguments),
+// then the launch.  key_lens (general mask only) may be null.
+fa2_status_t checked_launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
+                            int64_t H, int64_t N, int64_t d, float scale, int mask, int64_t wl, int64_t wr,
+                            const int32_t* key_lens, int dtype, void* stream) {
+  if (!Q || !K || !V || !O || !LSE) return FA2_ERR_NULL_POINTER;
+  int64_t grid = 0;
+  const fa2_status_t st = check_shape(B, H, N, d, dtype, &grid);
+  if (st != FA2_OK) return st;
+  if (!std::isfinite(scale)) return FA2_ERR_BAD_SCALE;
+  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u) return FA2_ERR_MISALIGNED;
+  if (((uintptr_t)LSE | (uintptr_t)key_lens) & 3u) return FA2_ERR_MISALIGNED;
+  const size_t tensor_bytes = (size_t)(B * H * N * d) * 2;
+  const size_t lse_bytes = (size_t)(B * H * N) * 4;
+  const size_t len_bytes = key_lens ? (size_t)B * 4 : 0;
+  if (overlaps(O, tensor_bytes, Q, tensor_bytes) || overlaps(O, tensor_bytes, K, tensor_bytes) ||
+      overlaps(O, tensor_bytes, V, tensor_bytes) || overlaps(LSE, lse_bytes, Q, tensor_bytes) ||
+      overlaps(LSE, lse_bytes, K, tensor_bytes) || overlaps(LSE, lse_bytes, V, tensor_bytes) ||
+      overlaps(LSE, lse_bytes, O, tensor_bytes) || overlaps(O, tensor_bytes, key_lens, len_bytes) ||
+      overlaps(LSE, lse_bytes, key_lens, len_bytes))
+    return FA2_ERR_OVERLAP;
+
+  const int br = rows_per_wg(d);
+  fa2::Params p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = LSE;
+  p.n = (int)N;
+  p.bh = (int)(B * H);
+  p.n_qtiles = (int)((N + br - 1) / br);
+  p.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+  p.q_sign = std::signbit(scale) && scale != 0.f ? 0x80008000u : 0u;
+  // A bound of N or more hides nothing (N < kNoBound by the size limits).
+  p.wl = (wl < 0 || wl >= N) ? fa2::kNoBound : (int)wl;
+  p.wr = (wr < 0 || wr >= N) ? fa2::kNoBound : (int)wr;
+  p.key_lens = key_lens;
+  p.heads = (int)H;
+
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t err = dtype == FA2_DTYPE_BF16 ? launch_mask<true>(mask, d, p, grid, s)
+                                                 : launch_mask<false>(mask, d, p, grid, s);
+  return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
 }
 
 }  // namespace
@@ -156,43 +211,23 @@ fa2_status_t fa2_launch_info(int64_t B, int64_t H, int64_t N, int64_t d, int is_
 fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale, int is_causal,
                      int dtype, void* stream) {
-  if (!Q || !K || !V || !O || !LSE) return FA2_ERR_NULL_POINTER;
-  int64_t grid = 0;
-  const fa2_status_t st = check_shape(B, H, N, d, dtype, &grid);
-  if (st != FA2_OK) return st;
-  if (!std::isfinite(scale)) return FA2_ERR_BAD_SCALE;
-  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u) return FA2_ERR_MISALIGNED;
-  if ((uintptr_t)LSE & 3u) return FA2_ERR_MISALIGNED;
-  const size_t tensor_bytes = (size_t)(B * H * N * d) * 2;
-  const size_t lse_bytes = (size_t)(B * H * N) * 4;
-  if (overlaps(O, tensor_bytes, Q, tensor_bytes) || overlaps(O, tensor_bytes, K, tensor_bytes) ||
-      overlaps(O, tensor_bytes, V, tensor_bytes) || overlaps(LSE, lse_bytes, Q, tensor_bytes) ||
-      overlaps(LSE, lse_bytes, K, tensor_bytes) || overlaps(LSE, lse_bytes, V, tensor_bytes) ||
-      overlaps(LSE, lse_bytes, O, tensor_bytes))
-    return FA2_ERR_OVERLAP;
+  return checked_launch(Q, K, V, O, LSE, B, H, N, d, scale, is_causal ? fa2::kMaskCausal : fa2::kMaskNone, -1,
+                        is_causal ? 0 : -1, nullptr, dtype, stream);
+}
 
-  const int br = rows_per_wg(d);
-  fa2::Params p;
-  p.q = Q;
-  p.k = K;
-  p.v = V;
-  p.o = O;
-  p.lse = LSE;
-  p.n = (int)N;
-  p.bh = (int)(B * H);
-  p.n_qtiles = (int)((N + br - 1) / br);
-  p.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
-  p.q_sign = std::signbit(scale) && scale != 0.f ? 0x80008000u : 0u;
-
-  hipStream_t s = (hipStream_t)stream;
-  const bool bf16 = dtype == FA2_DTYPE_BF16;
-  hipError_t err;
-  if (bf16) {
-    err = is_causal ? launch_dt<true, true>(d, p, grid, s) : launch_dt<true, false>(d, p, grid, s);
-  } else {
-    err = is_causal ? launch_dt<false, true>(d, p, grid, s) : launch_dt<false, false>(d, p, grid, s);
-  }
-  return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
+fa2_status_t fa2_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            int64_t B, int64_t H, int64_t N, int64_t d, float scale, int64_t window_left,
+                            int64_t window_right, const int32_t* key_lens, int dtype, void* stream) {
+  // Without padding, no window is the unmasked kernel and a window with no
+  // left bound and right bound 0 is the causal one (the same results, and the
+  // faster unchecked first run); anything else runs the general mask.
+  const bool no_left = window_left < 0 || window_left >= N;
+  const bool no_right = window_right < 0 || window_right >= N;
+  int mask = fa2::kMaskGeneral;
+  if (!key_lens && no_left && no_right) mask = fa2::kMaskNone;
+  if (!key_lens && no_left && window_right == 0) mask = fa2::kMaskCausal;
+  return checked_launch(Q, K, V, O, LSE, B, H, N, d, scale, mask, window_left, window_right, key_lens, dtype,
+                        stream);
 }
 
 }  // extern "C"

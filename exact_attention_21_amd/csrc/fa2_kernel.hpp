@@ -3,7 +3,9 @@
 // What it computes (per batch b, head h, query row i):
 //   O[i]   = sum_j P[i,j] V[j] / l_i,  P[i,j] = exp(scale * q_i.k_j - m_i),
 //   l_i    = sum_j P[i,j],             LSE[i] = m_i + ln l_i
-// over the keys visible to i (all keys, or j <= i when causal).  Method:
+// over the keys visible to i: all keys, j <= i (causal), or the keys of a
+// sliding window i - wl <= j <= i + wr below a per-sequence key length
+// (general mask).  Method:
 // "FlashAttention-2 MMA 代码学习" (chuoer47.github.io) step 1 (online (m, l)
 // merge over key tiles), step 2 (split-Q: each wave owns whole query rows),
 // step 3 (P stays in registers and feeds the second matrix product); and
@@ -79,7 +81,19 @@ struct Params {
   int n_qtiles;      // ceil(N / rows per workgroup)
   float scale_log2;  // |scale| * log2(e): scores go to the base-2 exponent domain
   uint32_t q_sign;   // 0x80008000 when scale < 0: Q is negated on load, |scale| used
+  // General mask only: key j is visible to query i iff j < key_len(b),
+  // j >= i - wl and j <= i + wr (kNoBound: no bound).
+  int wl;
+  int wr;
+  const int* key_lens;  // B lengths (clamped to [0, N]) or null: no padding
+  int heads;            // H, to find the batch of a (batch*head) slice
 };
+
+// Mask modes (template argument MASK).
+enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskGeneral = 2 };
+// A window bound that never hides a key (larger than any N the library
+// accepts, small enough that row +- bound stays in int range).
+constexpr int kNoBound = 1 << 29;
 
 // Buffer resource word 3 for gfx9-family raw buffers (32-bit data format,
 // no swizzle, offsets range-checked against num_records).
@@ -251,8 +265,10 @@ constexpr float kTileSumLimit = 32768.0f;
 // below any score that a visible key overflows the row sum.
 constexpr float kUnseenBase = 1.0e30f;
 
-template <int D, int BC, int NW, int QB, int KVG, bool BF16, bool CAUSAL>
+template <int D, int BC, int NW, int QB, int KVG, bool BF16, int MASK>
 struct Fa2Fwd {
+  static constexpr bool CAUSAL = MASK == kMaskCausal;
+  static constexpr bool GENERAL = MASK == kMaskGeneral;
   static_assert(KVG == 1 || (KVG == 2 && NW == 8), "split-KV runs two groups of 4 waves");
   static constexpr int THREADS = NW * 64;
   // Pipelined schedule: K and V tiles each in a ring of PIPE_RING LDS slots,
@@ -334,9 +350,11 @@ struct Fa2Fwd {
     }
   }
 
-  // Per-element mask of one tile (ragged tail and causal diagonal): hidden
-  // scores become -inf before the row max, as the pages require.
-  static __device__ __forceinline__ void mask_scores(Scores& sc, int lane, int k0, int qw0, int n) {
+  // Per-element mask of one tile (ragged tail, causal diagonal, window edges,
+  // padding): hidden scores become -inf before the row max, as the pages
+  // require.  n: keys present (N, or the sequence's key length).
+  static __device__ __forceinline__ void mask_scores(Scores& sc, int lane, int k0, int qw0, int n, int wl,
+                                                     int wr) {
     const int half = lane >> 5;
     const float ninf = -__builtin_inff();
 #pragma unroll
@@ -347,7 +365,7 @@ struct Fa2Fwd {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool hide = (key >= n) || (CAUSAL && key > qrow);
+          const bool hide = (key >= n) || (CAUSAL && key > qrow) || (GENERAL && (key > qrow + wr || key < qrow - wl));
           sc.s[qb][kb][r] = hide ? ninf : sc.s[qb][kb][r];
         }
       }
@@ -395,11 +413,12 @@ struct Fa2Fwd {
     const int wave = tid >> 6;
     const int half = lane >> 5;
 
-    // Work item: heads vary fastest; causal grids take the longest tiles first.
+    // Work item: heads vary fastest; masked grids take the last query tiles
+    // (the longest under a causal mask) first.
     const int wg = blockIdx.x;
     const int bh = wg % p.bh;
     const int t = wg / p.bh;
-    const int qtile = CAUSAL ? (p.n_qtiles - 1 - t) : t;
+    const int qtile = MASK != kMaskNone ? (p.n_qtiles - 1 - t) : t;
     const int n = p.n;
     const int q0 = qtile * BR;
     // Query rows of this wave.  Split-KV: waves w and w+NW/2 own the same rows.
@@ -461,16 +480,32 @@ struct Fa2Fwd {
       off.dma = __builtin_amdgcn_readfirstlane(sbase + (stid & ~63) * 16);
     }
 
-    const int kend = CAUSAL ? min(n, q0 + BR) : n;
-    const int ntiles = (kend + BC - 1) / BC;
-    const Ctx cx{rsrc_words(p.k, slice * 2, slice_bytes), rsrc_words(p.v, slice * 2, slice_bytes), ones_operand(lane),
-                 ones_index(lane), lds, off, p.scale_log2, lane, tid, qw0, n, ntiles};
+    // Key tiles the workgroup's rows can see: [tfirst, tfirst + ntiles).  A
+    // workgroup whose rows see no key at all still runs one fully masked tile,
+    // which leaves O = 0 and LSE = +inf.
+    int klen = n, wl = kNoBound, wr = CAUSAL ? 0 : kNoBound, kbeg = 0, kend = n;
+    if constexpr (CAUSAL) kend = min(n, q0 + BR);
+    if constexpr (GENERAL) {
+      if (p.key_lens) klen = min(max(p.key_lens[bh / p.heads], 0), n);
+      wl = p.wl;
+      wr = p.wr;
+      kbeg = max(0, q0 - wl);
+      kend = min(klen, q0 + BR + wr);
+    }
+    const int tfirst = kbeg / BC;
+    const int ntiles = kend > kbeg ? (kend + BC - 1) / BC - tfirst : 1;
+    // K and V are range-checked at the keys present: rows past N, or past the
+    // sequence's key length (padding, whose contents may be anything), load as
+    // zeros, so a hidden key's 0 probability never meets a non-finite value.
+    const uint32_t kv_bytes = (uint32_t)klen * D * 2;
+    const Ctx cx{rsrc_words(p.k, slice * 2, kv_bytes), rsrc_words(p.v, slice * 2, kv_bytes), ones_operand(lane),
+                 ones_index(lane), lds, off, p.scale_log2, lane, tid, qw0, klen, wl, wr};
     if constexpr (SPLIT) {
-      // Group 0 takes key tiles [0, T0) with T0 even, group 1 [T0, 2*T0);
-      // tiles past the end are fully masked.  Both run T0 sub-iterations, so
-      // their barriers pair.
+      // Group 0 takes key tiles [tfirst, tfirst + T0) with T0 even, group 1
+      // the next T0; tiles past the end are fully masked.  Both run T0
+      // sub-iterations, so their barriers pair.
       const int t0 = 2 * ((ntiles + 3) / 4);
-      const int first = grp == 0 ? 0 : t0;
+      const int first = grp == 0 ? tfirst : tfirst + t0;
       // The LDS tiles are loaded by all waves together: a rerun is the whole
       // workgroup's.
       run_pipe<!OPTIMISTIC>(cx, st, first, t0);
@@ -480,9 +515,9 @@ struct Fa2Fwd {
       merge_groups(cx, st, grp);
       if (grp != 0) return;  // group 1 handed its state to group 0
     } else {
-      run_pipe<!OPTIMISTIC>(cx, st, 0, ntiles);
+      run_pipe<!OPTIMISTIC>(cx, st, tfirst, ntiles);
       if constexpr (OPTIMISTIC) {
-        if (__syncthreads_or(pipe_failed(st))) run_pipe<true>(cx, st, 0, ntiles);
+        if (__syncthreads_or(pipe_failed(st))) run_pipe<true>(cx, st, tfirst, ntiles);
       }
     }
 
@@ -532,7 +567,10 @@ struct Fa2Fwd {
   // overflowed (see run_pipe).  Measured: 6% faster at d = 64, 12% at d = 256.
   // At d = 128 the second copy of the pipeline does not fit the registers of
   // two waves per SIMD (it spills), so d = 128 keeps only the checked run.
-  static constexpr bool OPTIMISTIC = FA2_UNCHECKED_RUN && D != 128;
+  // The general mask runs checked only: a wave whose window starts after the
+  // workgroup's first tile would take its fixed base from a tile it cannot
+  // see, and nearly every workgroup would rerun.
+  static constexpr bool OPTIMISTIC = FA2_UNCHECKED_RUN && D != 128 && !GENERAL;
 
   // Loop-invariant context.
   struct Ctx {
@@ -542,11 +580,20 @@ struct Fa2Fwd {
     lds_char* lds;
     LdsOffsets off;
     float c2;
-    int lane, tid, qw0, n, ntiles;
+    int lane, tid, qw0;
+    int n;       // keys present: N, or the sequence's key length (general mask)
+    int wl, wr;  // window bounds (general mask; kNoBound: none)
     // A wave takes part in tile j if some key of it is visible to some of its rows.
-    __device__ __forceinline__ bool active(int j) const { return !CAUSAL || j * BC <= qw0 + QW - 1; }
-    // Tile j needs per-element masking (ragged tail or causal diagonal).
+    __device__ __forceinline__ bool active(int j) const {
+      if constexpr (CAUSAL) return j * BC <= qw0 + QW - 1;
+      if constexpr (GENERAL) return j * BC < n && j * BC <= qw0 + QW - 1 + wr && j * BC + BC - 1 >= qw0 - wl;
+      return true;
+    }
+    // Tile j needs per-element masking (ragged tail or padding, causal
+    // diagonal, window edges).
     __device__ __forceinline__ bool masked(int j) const {
+      if constexpr (GENERAL)
+        return (j * BC + BC > n) || (j * BC + BC - 1 > qw0 + wr) || (j * BC < qw0 + QW - 1 - wl);
       return (j * BC + BC > n) || (CAUSAL && j * BC + BC - 1 > qw0);
     }
   };
@@ -889,7 +936,8 @@ struct Fa2Fwd {
   static __device__ __forceinline__ void pipe_sub(const Ctx& cx, State& st, Scores (&sc)[2],
                                                   u32x4 (&pb)[2][QB][KB][2], int j) {
     constexpr int B = S4 % 2;
-    if (__builtin_expect(!cx.active(j) || cx.masked(j), 0)) mask_scores(sc[B], cx.lane, j * BC, cx.qw0, cx.n);
+    if (__builtin_expect(!cx.active(j) || cx.masked(j), 0))
+      mask_scores(sc[B], cx.lane, j * BC, cx.qw0, cx.n, cx.wl, cx.wr);
     f32x4 ct[QB];
     float lt[QB];
     pipe_body<S4, CHECKED>(cx, st, sc, pb, CHECKED ? ct : st.ls, lt);
@@ -991,7 +1039,7 @@ struct Fa2Fwd {
     __syncthreads();  // K slot 0 is rewritten by the first group's loads
     if constexpr (!CHECKED) {
       // Fixed base: the row max of the first tile (both lane halves), scaled.
-      if (!cx.active(first) || cx.masked(first)) mask_scores(sc[0], cx.lane, first * BC, cx.qw0, cx.n);
+      if (!cx.active(first) || cx.masked(first)) mask_scores(sc[0], cx.lane, first * BC, cx.qw0, cx.n, cx.wl, cx.wr);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         float mx = -__builtin_inff();
@@ -1081,10 +1129,10 @@ struct Fa2Fwd {
 
 };
 
-template <int D, int BC, int NW, int QB, int KVG, bool BF16, bool CAUSAL>
+template <int D, int BC, int NW, int QB, int KVG, bool BF16, int MASK>
 __global__ void __launch_bounds__(NW * 64, 1) fa2_fwd_kernel(const Params p) {
   extern __shared__ __attribute__((aligned(16))) char lds_generic[];
-  Fa2Fwd<D, BC, NW, QB, KVG, BF16, CAUSAL>::run(
+  Fa2Fwd<D, BC, NW, QB, KVG, BF16, MASK>::run(
       p, (__attribute__((address_space(3))) char*)(__attribute__((address_space(3))) void*)lds_generic);
 }
 

@@ -9,19 +9,25 @@ import math
 
 import torch
 
-from ._binding import FA2_DTYPE_BF16, FA2_DTYPE_FP16, FA2_OK, Fa2Error, fa2_fwd
+from ._binding import FA2_DTYPE_BF16, FA2_DTYPE_FP16, FA2_OK, Fa2Error, fa2_fwd, fa2_fwd_masked
 
 _DTYPES = {torch.float16: FA2_DTYPE_FP16, torch.bfloat16: FA2_DTYPE_BF16}
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
             causal: bool = False, out: torch.Tensor | None = None,
-            lse: torch.Tensor | None = None):
+            lse: torch.Tensor | None = None, window: tuple[int, int] | None = None,
+            key_lens: torch.Tensor | None = None):
     """Attention forward on [B, H, N, d] fp16/bf16 CUDA(HIP) tensors.
 
     Returns (O, LSE): O has q's shape and dtype, LSE is float32 [B, H, N].
     ``scale`` defaults to 1/sqrt(d).  ``out``/``lse`` may be given to reuse
     buffers.  The kernel is enqueued on torch's current stream.
+
+    ``window`` = (left, right) keeps key j for query i only when
+    i - left <= j <= i + right (a negative bound is none; ``causal`` sets
+    right = 0), and ``key_lens`` (int32 [B] on the same GPU) hides the keys at
+    or past each sequence's length; either one calls ``fa2_fwd_masked``.
     """
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {tuple(q.shape)}, "
@@ -44,10 +50,25 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | No
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
             or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    masked = window is not None or key_lens is not None
+    if masked:
+        left, right = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+        if causal:
+            right = 0 if right < 0 else min(right, 0)
+        lens_ptr = None
+        if key_lens is not None:
+            if key_lens.shape != (B,) or key_lens.dtype != torch.int32 or not key_lens.is_contiguous() \
+                    or key_lens.device != q.device:
+                raise ValueError("key_lens must be a contiguous int32 [B] tensor on q's device")
+            lens_ptr = key_lens.data_ptr()
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        st = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                     B, H, N, d, float(scale), int(bool(causal)), _DTYPES[q.dtype], stream)
+        if masked:
+            st = fa2_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                B, H, N, d, float(scale), left, right, lens_ptr, _DTYPES[q.dtype], stream)
+        else:
+            st = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         B, H, N, d, float(scale), int(bool(causal)), _DTYPES[q.dtype], stream)
     if st != FA2_OK:
-        raise Fa2Error(st, "fa2_fwd")
+        raise Fa2Error(st, "fa2_fwd_masked" if masked else "fa2_fwd")
     return out, lse

@@ -63,8 +63,8 @@ typedef enum {
   FA2_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d is not 32, 64, 96, 128 or 256                       */
   FA2_ERR_UNSUPPORTED_DTYPE = 4,    /* dtype is not FA2_DTYPE_FP16 or FA2_DTYPE_BF16         */
   FA2_ERR_BAD_SCALE = 5,            /* scale is NaN or infinite                              */
-  FA2_ERR_MISALIGNED = 6,           /* Q, K, V, O not 16-byte aligned, or LSE not 4-byte     */
-  FA2_ERR_OVERLAP = 7,              /* O or LSE overlaps Q, K, V or each other               */
+  FA2_ERR_MISALIGNED = 6,           /* Q, K, V, O not 16-byte aligned, LSE or key_lens not 4 */
+  FA2_ERR_OVERLAP = 7,              /* O or LSE overlaps Q, K, V, key_lens or each other     */
   FA2_ERR_HIP = 8                   /* the HIP runtime reported an error at launch           */
 } fa2_status_t;
 
@@ -90,6 +90,40 @@ typedef enum {
 fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale, int is_causal,
                      int dtype, void* stream);
+
+/*
+ * fa2_fwd_masked - fa2_fwd under a sliding window and per-sequence key
+ * lengths (right padding).  The pages name sliding-window and padding masks
+ * as the masks under which a row can see only hidden keys in its first key
+ * tiles, which is what the kernel's -inf guards are for ("第 15 章 FA2 前向：
+ * Tiling 与 Online Softmax", the note after the §15.3 kernel skeleton); their
+ * form here is this library's reading:
+ *
+ *   key j is visible to query i of batch b iff
+ *       j <  key_lens[b]            (when key_lens is not NULL)
+ *       j >= i - window_left        (when window_left >= 0)
+ *       j <= i + window_right       (when window_right >= 0)
+ *
+ * and the softmax runs over the visible keys only.  A row with no visible
+ * key gets O = 0 and LSE = +inf.  window_left < 0 with window_right = 0 is
+ * the causal mask of fa2_fwd; a bound >= N hides nothing.
+ *
+ *   window_left, window_right  window bounds in keys; negative: no bound.
+ *   key_lens  NULL (no padding) or a device pointer to B int32 lengths, read
+ *             by the kernel (4-byte aligned; must not overlap O or LSE);
+ *             values outside [0, N] are clamped to it.  K and V rows at or
+ *             past the length are never read (they may hold anything, NaN
+ *             included); keys hidden by the window are read and must be
+ *             finite, as every key of fa2_fwd must.
+ *   All other arguments, checks, limits and status codes are those of
+ *   fa2_fwd.  Without key_lens, a call with no window runs fa2_fwd's
+ *   unmasked kernel and a call with window (<0, 0) its causal kernel
+ *   (bit-identical results); every other call runs the general-mask kernel.
+ */
+fa2_status_t fa2_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                            int64_t window_left, int64_t window_right, const int32_t* key_lens,
+                            int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa2_status_string(int status);

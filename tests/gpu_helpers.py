@@ -15,16 +15,22 @@ def to_device(x, dtype, device):
     return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
 
 
-def run_gpu(q, k, v, dtype, scale, causal, device, stream=None):
-    """Run fa2_fwd on storage arrays; return (O, LSE) as float64 numpy arrays."""
+def run_gpu(q, k, v, dtype, scale, causal, device, stream=None, window=None, key_lens=None):
+    """Run fa2_fwd (fa2_fwd_masked when a window or key lengths are given) on
+    storage arrays; return (O, LSE) as float64 numpy arrays."""
     import torch
     from exact_attention_21_amd import forward
     tq, tk, tv = (to_device(x, dtype, device) for x in (q, k, v))
+    kw = dict(scale=scale, causal=causal)
+    if window is not None:
+        kw["window"] = window
+    if key_lens is not None:
+        kw["key_lens"] = torch.tensor(key_lens, dtype=torch.int32, device=device)
     if stream is None:
-        o, lse = forward(tq, tk, tv, scale=scale, causal=causal)
+        o, lse = forward(tq, tk, tv, **kw)
     else:
         with torch.cuda.stream(stream):
-            o, lse = forward(tq, tk, tv, scale=scale, causal=causal)
+            o, lse = forward(tq, tk, tv, **kw)
     torch.cuda.synchronize(device)
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -139,3 +145,16 @@ def assert_close_stress(o_gpu, lse_gpu, o_ref, lse_ref, p_bound, dtype, label=""
     if dtype == wl.FP16:
         assert raw <= to, f"{label}: O error beyond P rounding {raw:.3e} > {to}"
     assert el <= tl, f"{label}: LSE error {el:.3e} > {tl}"
+
+
+def assert_close_masked(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label=""):
+    """assert_close for masked attention: a row the oracle marks fully hidden
+    (LSE = +inf) must come back as O = 0 and LSE = +inf exactly; the other
+    rows are held to the usual tolerances."""
+    hidden = np.isposinf(lse_ref)
+    assert np.array_equal(np.isposinf(lse_gpu), hidden), f"{label}: fully hidden rows differ"
+    assert np.all(o_gpu[hidden] == 0.0), f"{label}: O of a fully hidden row is not 0"
+    seen = ~hidden
+    if seen.any():
+        assert_close(o_gpu[seen], lse_gpu[seen], o_ref[seen], lse_ref[seen], dtype, label)
+    print(f"  {label}: {int(hidden.sum())} fully hidden rows", flush=True)

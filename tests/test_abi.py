@@ -126,3 +126,39 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(bd, "LIB_PATH", str(tmp_path / "libfa2.so"))
     with pytest.raises(RuntimeError, match="not built"):
         bd.library()
+
+
+# ---- fa2_fwd_masked --------------------------------------------------------
+
+LENS = 0x60000000  # fake, 4-byte aligned key-length array
+
+
+def call_masked(**kw):
+    args = dict(Q=Q, K=K, V=V, O=O, LSE=L, B=2, H=2, N=100, d=64, scale=0.125, window_left=16,
+                window_right=0, key_lens=LENS, dtype=fa.FA2_DTYPE_FP16, stream=0)
+    args.update(kw)
+    return fa.fa2_fwd_masked(**args)
+
+
+@pytest.mark.parametrize("name", ["Q", "K", "V", "O", "LSE"])
+def test_masked_null_pointer(name):
+    assert call_masked(**{name: 0}) == bd.FA2_ERR_NULL_POINTER
+
+
+@pytest.mark.parametrize("kw", [dict(key_lens=LENS + 2), dict(key_lens=LENS + 1), dict(Q=Q + 8), dict(LSE=L + 2)])
+def test_masked_misaligned(kw):
+    assert call_masked(**kw) == bd.FA2_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("kw", [dict(key_lens=O + 64), dict(key_lens=L), dict(key_lens=L + 4 * 2 * 2 * 100 - 4),
+                                dict(O=Q)])
+def test_masked_overlap(kw):
+    assert call_masked(**kw) == bd.FA2_ERR_OVERLAP
+
+
+def test_masked_shares_fwd_checks():
+    assert call_masked(d=80) == bd.FA2_ERR_UNSUPPORTED_HEAD_DIM
+    assert call_masked(N=0) == bd.FA2_ERR_BAD_SHAPE
+    assert call_masked(dtype=5) == bd.FA2_ERR_UNSUPPORTED_DTYPE
+    assert call_masked(scale=math.nan) == bd.FA2_ERR_BAD_SCALE
+
