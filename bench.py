@@ -69,14 +69,23 @@ def cpu_baseline(w, q, k, v, target_s: float = 10.0):
     from threadpoolctl import threadpool_info
 
     from exact_attention_21_amd import workloads as wl
-    from oracle import attention_ref
+    from oracle import attention_ref, attention_ref_masked
 
     qf, kf, vf = (wl.to_float64(x, w.dtype) for x in (q, k, v))
+
+    def oracle_rows(idx):
+        if not w.masked:
+            return attention_ref(qf, kf, vf, w.softmax_scale(), w.causal, rows=idx)
+        left, right = w.window if w.window is not None else (-1, -1)
+        if w.causal:
+            right = 0 if right < 0 else min(right, 0)
+        return attention_ref_masked(qf, kf, vf, w.softmax_scale(), left, right, w.key_lens, rows=idx)
+
     rows = 64
     while True:
         idx = np.arange(min(rows, w.N))
         t0 = time.perf_counter()
-        attention_ref(qf, kf, vf, w.softmax_scale(), w.causal, rows=idx)
+        oracle_rows(idx)
         dt = time.perf_counter() - t0
         if dt >= target_s / 8 or rows >= w.N:
             break
@@ -84,13 +93,12 @@ def cpu_baseline(w, q, k, v, target_s: float = 10.0):
     passes, total = 1, dt
     while total < target_s:
         t0 = time.perf_counter()
-        attention_ref(qf, kf, vf, w.softmax_scale(), w.causal, rows=idx)
+        oracle_rows(idx)
         total += time.perf_counter() - t0
         passes += 1
     dt = total / passes
-    # FLOPs of the sampled rows under the metric's count (visible keys only when causal).
-    keys = (idx + 1).sum() if w.causal else idx.size * w.N
-    flops = 4.0 * w.B * w.H * float(keys) * w.d
+    # FLOPs of the sampled rows under the metric's count (visible keys only).
+    flops = 4.0 * w.H * float(w.visible_keys(idx).sum()) * w.d
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads),
             "kind": "oracle",
@@ -148,7 +156,7 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
-    w = {x.name: x for x in wl.WORKLOADS}[args.workload]
+    w = {x.name: x for x in wl.ALL_WORKLOADS}[args.workload]
     dev = torch.device("cuda:0")
     q, k, v = wl.make_inputs(w, seed=0)
 
@@ -163,8 +171,14 @@ def main() -> int:
     scale = w.softmax_scale()
     stream = torch.cuda.current_stream(dev)
 
+    mask_kw = {}
+    if w.window is not None:
+        mask_kw["window"] = w.window
+    if w.key_lens is not None:
+        mask_kw["key_lens"] = torch.tensor(w.key_lens, dtype=torch.int32, device=dev)
+
     def step():
-        forward(tq, tk, tv, scale=scale, causal=w.causal, out=out, lse=lse)
+        forward(tq, tk, tv, scale=scale, causal=w.causal, out=out, lse=lse, **mask_kw)
 
     settle = settle_clock(step, stream)
     for _ in range(args.warmup):

@@ -29,7 +29,7 @@ def main() -> int:
     from exact_attention_21_amd import workloads as wl
 
     library()
-    w = {x.name: x for x in wl.WORKLOADS}[args.workload]
+    w = {x.name: x for x in wl.ALL_WORKLOADS}[args.workload]
     dev = torch.device("cuda:0")
     q, k, v = wl.make_inputs(w, seed=0)
 
@@ -41,8 +41,13 @@ def main() -> int:
     tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
     out = torch.empty_like(tq)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    mask_kw = {}
+    if w.window is not None:
+        mask_kw["window"] = w.window
+    if w.key_lens is not None:
+        mask_kw["key_lens"] = torch.tensor(w.key_lens, dtype=torch.int32, device=dev)
     for _ in range(args.launches):
-        forward(tq, tk, tv, scale=w.softmax_scale(), causal=w.causal, out=out, lse=lse)
+        forward(tq, tk, tv, scale=w.softmax_scale(), causal=w.causal, out=out, lse=lse, **mask_kw)
     torch.cuda.synchronize(dev)
     n = args.copy_mb * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device=dev)

@@ -7,7 +7,9 @@ what it returns.  It imports numpy only.
 The five workloads are the attention-forward shapes the method is measured on:
 a tiny correctness case, the 8-head N=8192 d=64 fp16 headline shape, a causal
 training-style d=128 bf16 shape, a long-context causal N=32768 shape and a
-d=256 bf16 shape with a ragged length and a wide score range.
+d=256 bf16 shape with a ragged length and a wide score range.  Two masked
+workloads exercise fa2_fwd_masked: a 4096-key causal sliding window over a
+long sequence, and a causal batch of right-padded sequences of mixed lengths.
 
 Draw recipe (one generator per call): ``numpy.random.default_rng(seed)``
 (PCG64); Q, then K, then V, each drawn as one float64 array of shape
@@ -40,18 +42,51 @@ class Workload:
     k_dist: tuple = ("normal", 1.0)
     v_dist: tuple = ("normal", 1.0)
     scale: float = field(default=None)
+    # fa2_fwd_masked arguments: (left, right) window bounds (negative: none)
+    # and per-sequence key lengths; None for the unmasked workloads.
+    window: tuple = None
+    key_lens: tuple = None
+
+    @property
+    def masked(self) -> bool:
+        return self.window is not None or self.key_lens is not None
 
     def softmax_scale(self) -> float:
         return self.scale if self.scale is not None else 1.0 / float(np.sqrt(self.d))
 
+    def visible_keys(self, rows=None) -> np.ndarray:
+        """Number of keys each query row sees, [B, R] (R: all rows, or `rows`):
+        j < key length, i - left <= j <= i + right (a negative bound is none;
+        causal adds right = 0)."""
+        i = np.arange(self.N) if rows is None else np.asarray(rows)
+        left, right = self.window if self.window is not None else (-1, -1)
+        if self.causal:
+            right = 0 if right < 0 else min(right, 0)
+        lens = self.key_lens if self.key_lens is not None else (self.N,) * self.B
+        lo = np.zeros_like(i) if left < 0 else np.maximum(0, i - left)
+        out = []
+        for n_b in lens:
+            hi = np.full_like(i, n_b) if right < 0 else np.minimum(n_b, i + right + 1)
+            out.append(np.maximum(hi - lo, 0))
+        return np.array(out)
+
     def flops(self) -> float:
-        """Nominal forward FLOPs of the metric: 4*B*H*N^2*d, halved when causal."""
-        f = 4.0 * self.B * self.H * self.N * self.N * self.d
-        return f / 2.0 if self.causal else f
+        """Forward FLOPs of the metric: 4*d per visible (query, key) pair and
+        head, i.e. 4*B*H*N^2*d, halved when causal; masked workloads count
+        their visible pairs exactly."""
+        if not self.masked:
+            f = 4.0 * self.B * self.H * self.N * self.N * self.d
+            return f / 2.0 if self.causal else f
+        return 4.0 * self.H * self.d * float(self.visible_keys().sum())
 
     def describe(self) -> dict:
-        return {"B": self.B, "H": self.H, "N": self.N, "d": self.d, "dtype": self.dtype,
-                "causal": self.causal, "scale": self.softmax_scale()}
+        out = {"B": self.B, "H": self.H, "N": self.N, "d": self.d, "dtype": self.dtype,
+               "causal": self.causal, "scale": self.softmax_scale()}
+        if self.window is not None:
+            out["window"] = list(self.window)
+        if self.key_lens is not None:
+            out["key_lens"] = list(self.key_lens)
+        return out
 
 
 TINY = Workload("tiny_b1h1n128d64_fp16", 1, 1, 128, 64, FP16, False)
@@ -62,6 +97,12 @@ WIDE_RAGGED = Workload("wide_ragged_b4h8n2047d256_bf16", 4, 8, 2047, 256, BF16, 
                        q_dist=("normal", 3.0), k_dist=("normal", 3.0), v_dist=("uniform", 1.0))
 
 WORKLOADS = [TINY, HEADLINE, CAUSAL_TRAIN, LONG_CAUSAL, WIDE_RAGGED]
+
+WINDOW = Workload("window4096_b1h8n32768d64_fp16", 1, 8, 32768, 64, FP16, False, window=(4095, 0))
+PADDED_CAUSAL = Workload("padded_causal_b8h16n4096d128_bf16", 8, 16, 4096, 128, BF16, True,
+                         key_lens=(4096, 3001, 2048, 517, 4096, 1290, 3777, 64))
+MASKED_WORKLOADS = [WINDOW, PADDED_CAUSAL]
+ALL_WORKLOADS = WORKLOADS + MASKED_WORKLOADS
 
 
 def _draw(rng: np.random.Generator, shape, dist) -> np.ndarray:

@@ -113,3 +113,20 @@ def test_masked_stress_late_window_start(gpu_device):
     o, lse = run_gpu(q, k, v, wl.FP16, scale, False, gpu_device, window=(3, 0))
     o_ref, lse_ref = attention_ref_masked(*(wl.to_float64(x, wl.FP16) for x in (q, k, v)), scale, 3, 0, None)
     assert_close_masked(o, lse, o_ref, lse_ref, wl.FP16, "window (3, 0)")
+
+
+@pytest.mark.parametrize("w", wl.MASKED_WORKLOADS, ids=[w.name for w in wl.MASKED_WORKLOADS])
+def test_masked_workload_full_size_sampled_rows(gpu_device, w):
+    """The masked benchmark workloads at full size, in the launch the benchmark
+    times; the oracle evaluates both ends of the sequence and random rows."""
+    q, k, v = wl.make_inputs(w, seed=0)
+    left, right = w.window if w.window is not None else (-1, -1)
+    if w.causal:
+        right = 0 if right < 0 else min(right, 0)
+    o, lse = run_gpu(q, k, v, w.dtype, w.softmax_scale(), w.causal, gpu_device, window=w.window,
+                     key_lens=list(w.key_lens) if w.key_lens is not None else None)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(w.N - 64, w.N), rng.choice(w.N, 128, replace=False)]))
+    o_ref, lse_ref = attention_ref_masked(*(wl.to_float64(x, w.dtype) for x in (q, k, v)), w.softmax_scale(),
+                                          left, right, w.key_lens, rows=rows)
+    assert_close_masked(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, w.dtype, w.name)

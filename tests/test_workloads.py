@@ -46,3 +46,15 @@ def test_wide_ragged_distributions():
     assert q.shape == (1, 1, 2047, 256)
     assert 2.8 < qf.std() < 3.2
     assert vf.min() >= -1.0 and vf.max() <= 1.0
+
+
+def test_masked_workload_flops_count_visible_pairs():
+    w = wl.WINDOW
+    n, left = w.N, w.window[0]
+    pairs = sum(min(i, left) + 1 for i in range(n))
+    assert w.flops() == 4.0 * w.H * w.d * pairs
+    p = wl.PADDED_CAUSAL
+    pairs = sum(sum(min(i + 1, n_b) for i in range(p.N)) for n_b in p.key_lens)
+    assert p.flops() == 4.0 * p.H * p.d * pairs
+    # The unmasked count is unchanged: causal halves the square.
+    assert wl.CAUSAL_TRAIN.flops() == 4 * 2 * 16 * 4096 ** 2 * 128 / 2
