@@ -498,8 +498,9 @@ struct Fa2Fwd {
     // sequence's key length (padding, whose contents may be anything), load as
     // zeros, so a hidden key's 0 probability never meets a non-finite value.
     const uint32_t kv_bytes = (uint32_t)klen * D * 2;
+    const int late = GENERAL ? max(0, qw0 + QW - 1 - wl) / BC : -1;
     const Ctx cx{rsrc_words(p.k, slice * 2, kv_bytes), rsrc_words(p.v, slice * 2, kv_bytes), ones_operand(lane),
-                 ones_index(lane), lds, off, p.scale_log2, lane, tid, qw0, klen, wl, wr};
+                 ones_index(lane), lds, off, p.scale_log2, lane, tid, qw0, klen, wl, wr, late};
     if constexpr (SPLIT) {
       // Group 0 takes key tiles [tfirst, tfirst + T0) with T0 even, group 1
       // the next T0; tiles past the end are fully masked.  Both run T0
@@ -567,10 +568,10 @@ struct Fa2Fwd {
   // overflowed (see run_pipe).  Measured: 6% faster at d = 64, 12% at d = 256.
   // At d = 128 the second copy of the pipeline does not fit the registers of
   // two waves per SIMD (it spills), so d = 128 keeps only the checked run.
-  // The general mask runs checked only: a wave whose window starts after the
-  // workgroup's first tile would take its fixed base from a tile it cannot
-  // see, and nearly every workgroup would rerun.
-  static constexpr bool OPTIMISTIC = FA2_UNCHECKED_RUN && D != 128 && !GENERAL;
+  // Under the general mask a row's window can start after the run's first
+  // tile: its fixed base is taken at the first tile in which it sees a key
+  // (fix_late_bases).
+  static constexpr bool OPTIMISTIC = FA2_UNCHECKED_RUN && D != 128;
 
   // Loop-invariant context.
   struct Ctx {
@@ -583,6 +584,7 @@ struct Fa2Fwd {
     int lane, tid, qw0;
     int n;       // keys present: N, or the sequence's key length (general mask)
     int wl, wr;  // window bounds (general mask; kNoBound: none)
+    int late;    // general mask: last tile in which a row of the wave can see its first key
     // A wave takes part in tile j if some key of it is visible to some of its rows.
     __device__ __forceinline__ bool active(int j) const {
       if constexpr (CAUSAL) return j * BC <= qw0 + QW - 1;
@@ -927,6 +929,24 @@ struct Fa2Fwd {
     }
   }
 
+  // Unchecked run under the general mask: a row that has seen no key yet
+  // (base still -kUnseenBase) takes its fixed base from this tile's row max
+  // if it sees a key here; its probabilities of the tiles before were 0.
+  static __device__ __forceinline__ void fix_late_bases(const Ctx& cx, const Scores& sc, State& st) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sc.s[qb][kb][r]);
+      float lo, hi;
+      halves(mx, lo, hi);
+      mx = __builtin_fmaxf(lo, hi);
+      if (st.m[qb] == -kUnseenBase && mx != -__builtin_inff()) st.m[qb] = mx * cx.c2;
+    }
+  }
+
   // Sub-iteration j (S4 = (j - first) % PIPE_RING): S(j+1), softmax(j), P(j-1)V(j-1).
   // Tiles past a wave's causal diagonal run as fully masked tiles (P = 0);
   // skipping them with a branch measured no faster.  CHECKED: each tile's sums
@@ -938,6 +958,9 @@ struct Fa2Fwd {
     constexpr int B = S4 % 2;
     if (__builtin_expect(!cx.active(j) || cx.masked(j), 0))
       mask_scores(sc[B], cx.lane, j * BC, cx.qw0, cx.n, cx.wl, cx.wr);
+    if constexpr (GENERAL && !CHECKED) {
+      if (__builtin_expect(j <= cx.late, 0)) fix_late_bases(cx, sc[B], st);
+    }
     f32x4 ct[QB];
     float lt[QB];
     pipe_body<S4, CHECKED>(cx, st, sc, pb, CHECKED ? ct : st.ls, lt);

@@ -95,7 +95,7 @@ _U_P = {wl.FP16: 2.0 ** -11, wl.BF16: 2.0 ** -8}
 _FP16_SUB_HALF = 2.0 ** -25
 
 
-def p_rounding_bound(q, k, v, o_ref, dtype, scale, causal):
+def p_rounding_bound(q, k, v, o_ref, dtype, scale, causal, mask=None):
     """First-order bound, per element of O, of rounding P once to the input
     dtype before P.V (the pages round P to the input type and accumulate O in
     fp32; O is normalised by the sum of the rounded P).
@@ -113,14 +113,19 @@ def p_rounding_bound(q, k, v, o_ref, dtype, scale, causal):
     tolerance holds on its own; inputs built to put the weight on a few keys
     with different V rows reach this bound.
     """
-    from oracle import attention_ref
+    from oracle import attention_ref, attention_ref_masked
     n = q.shape[2]
     v64 = wl.to_float64(v, dtype)
-    ev2, _ = attention_ref(wl.to_float64(q, dtype), wl.to_float64(k, dtype), v64 * v64, scale, causal)
+    q64, k64 = wl.to_float64(q, dtype), wl.to_float64(k, dtype)
+    if mask is None:
+        ev2, _ = attention_ref(q64, k64, v64 * v64, scale, causal)
+    else:  # (window_left, window_right, key_lens) of attention_ref_masked
+        ev2, _ = attention_ref_masked(q64, k64, v64 * v64, scale, *mask)
     sigma = np.sqrt(np.maximum(ev2 - o_ref * o_ref, 0.0))
     u = _U_P[dtype]
     bound = u / (1.0 - u) * sigma
     if dtype == wl.FP16:
+        # (n visible keys at most: the whole row length bounds every mask)
         n_vis = (np.arange(n) + 1.0) if causal else np.full(n, float(n))
         vmax = np.abs(v64).max(axis=2, keepdims=True)  # [B, H, 1, d]
         bound = bound + n_vis[None, None, :, None] * _FP16_SUB_HALF * (vmax + np.abs(o_ref))

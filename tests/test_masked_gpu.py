@@ -12,7 +12,8 @@ import pytest
 
 from exact_attention_21_amd import workloads as wl
 from oracle import attention_ref_masked
-from tests.gpu_helpers import assert_close_masked, run_gpu
+from tests.gpu_helpers import (assert_close_masked, assert_close_stress, p_rounding_bound, run_gpu,
+                               spiky_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -130,3 +131,24 @@ def test_masked_workload_full_size_sampled_rows(gpu_device, w):
     o_ref, lse_ref = attention_ref_masked(*(wl.to_float64(x, w.dtype) for x in (q, k, v)), w.softmax_scale(),
                                           left, right, w.key_lens, rows=rows)
     assert_close_masked(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, w.dtype, w.name)
+
+
+@pytest.mark.parametrize("d", (32, 64, 96, 256))
+@pytest.mark.parametrize("dtype", [wl.FP16, wl.BF16])
+@pytest.mark.parametrize("mask", [(300, 0, None), (-1, 40, [1500, 900])], ids=["window", "padded"])
+def test_masked_late_score_jumps(gpu_device, d, dtype, mask):
+    """Score jumps half-way through the keys under a mask: the fixed base of
+    the first (unchecked) run overflows and the workgroup reruns its keys
+    through the checked pipeline.  O allows the P-rounding bound, as in the
+    unmasked stress tests."""
+    wleft, wright, lens = mask
+    q, k, v = spiky_inputs(2, 2, 1500, d, dtype, seed=41, factor=12.0, where=(0.5, 0.83))
+    scale = 1 / math.sqrt(d)
+    o, lse = run_gpu(q, k, v, dtype, scale, False, gpu_device, window=(wleft, wright), key_lens=lens)
+    o_ref, lse_ref = attention_ref_masked(*(wl.to_float64(x, dtype) for x in (q, k, v)), scale, wleft, wright, lens)
+    hidden = np.isposinf(lse_ref)
+    assert np.array_equal(np.isposinf(lse), hidden) and np.all(o[hidden] == 0)
+    bound = p_rounding_bound(q, k, v, o_ref, dtype, scale, False, mask=(wleft, wright, lens))
+    seen = ~hidden
+    assert_close_stress(o[seen], lse[seen], o_ref[seen], lse_ref[seen], bound[seen], dtype,
+                        f"masked late jumps d{d} {dtype} window=({wleft},{wright}) lens={lens}")
