@@ -29,7 +29,7 @@ MFMA_PEAK_TFLOPS = 2516.6
 # 0.740 ms, which is 185.7 TFLOPS under this metric's 4*B*H*N^2*d count.
 PAGE_BEST_TFLOPS = 4 * 8 * 8192 ** 2 * 64 / 0.740e-3 / 1e12
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_21_amd", "csrc", f)
-                  for f in ("fa2_kernel.hpp", "fa2_api.hip")]
+                  for f in ("fa2_kernel.hpp", "fa2_wide.hpp", "fa2_api.hip")]
 
 
 def kernel_hash() -> str:

@@ -12,6 +12,7 @@
 #include <mutex>
 
 #include "fa2_kernel.hpp"
+#include "fa2_wide.hpp"
 
 namespace {
 
@@ -43,22 +44,34 @@ constexpr TileCfg cfg_for(int64_t d) {
 
 template <int D>
 using KernelFor = fa2::Fa2Fwd<D, cfg_for(D).bc, cfg_for(D).nw, cfg_for(D).qb, cfg_for(D).kvg, false, false>;
+// Head dims 512 and 1024 run the chunked kernel (fa2_wide.hpp).
+template <int D>
+using WideFor = fa2::Fa2Wide<D, false, fa2::kMaskNone>;
 
 constexpr int rows_per_wg(int64_t d) {
   return d == 32 ? KernelFor<32>::BR : d == 64 ? KernelFor<64>::BR : d == 96 ? KernelFor<96>::BR
-         : d == 128 ? KernelFor<128>::BR : KernelFor<256>::BR;
+         : d == 128 ? KernelFor<128>::BR : d == 256 ? KernelFor<256>::BR
+         : d == 512 ? WideFor<512>::BR : WideFor<1024>::BR;
 }
 
 constexpr int lds_bytes_for(int64_t d) {
   return d == 32 ? KernelFor<32>::LDS_BYTES : d == 64 ? KernelFor<64>::LDS_BYTES
-         : d == 96 ? KernelFor<96>::LDS_BYTES : d == 128 ? KernelFor<128>::LDS_BYTES : KernelFor<256>::LDS_BYTES;
+         : d == 96 ? KernelFor<96>::LDS_BYTES : d == 128 ? KernelFor<128>::LDS_BYTES
+         : d == 256 ? KernelFor<256>::LDS_BYTES : d == 512 ? WideFor<512>::LDS_BYTES : WideFor<1024>::LDS_BYTES;
+}
+
+constexpr int threads_for(int64_t d) {
+  return d == 512 ? WideFor<512>::THREADS : d == 1024 ? WideFor<1024>::THREADS : cfg_for(d).nw * 64;
 }
 
 // Rows past N that a launch may address (see check_shape).
 constexpr int64_t kPadRows = 256;
 static_assert(KernelFor<32>::BR <= kPadRows && KernelFor<64>::BR <= kPadRows && KernelFor<96>::BR <= kPadRows &&
-                  KernelFor<128>::BR <= kPadRows && KernelFor<256>::BR <= kPadRows,
+                  KernelFor<128>::BR <= kPadRows && KernelFor<256>::BR <= kPadRows &&
+                  WideFor<512>::BR <= kPadRows && WideFor<1024>::BR <= kPadRows,
               "query tile padding");
+// The chunked kernel loads one key tile past its range.
+static_assert(WideFor<512>::BC <= kPadRows && WideFor<1024>::BC <= kPadRows, "key tile padding (chunked)");
 static_assert(4 * cfg_for(32).bc <= kPadRows && 4 * cfg_for(64).bc <= kPadRows && 4 * cfg_for(96).bc <= kPadRows &&
                   4 * cfg_for(128).bc <= kPadRows && 4 * cfg_for(256).bc <= kPadRows,
               "key tile padding");
@@ -70,7 +83,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 fa2_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int64_t* grid) {
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_UNSUPPORTED_DTYPE;
-  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA2_ERR_UNSUPPORTED_HEAD_DIM;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256 && d != 512 && d != 1024)
+    return FA2_ERR_UNSUPPORTED_HEAD_DIM;
   if (B < 1 || H < 1 || N < 1) return FA2_ERR_BAD_SHAPE;
   const int64_t br = rows_per_wg(d);
   // One head's slice is addressed with signed 32-bit byte offsets, including
@@ -102,9 +116,28 @@ hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
 }
 
 template <int D, bool BF16, int MASK>
+hipError_t launch_wide(const fa2::Params& p, int64_t grid, hipStream_t stream) {
+  using W = fa2::Fa2Wide<D, BF16, MASK>;
+  static_assert(W::LDS_BYTES == lds_bytes_for(D) && W::BR == rows_per_wg(D), "chunked kernel shape");
+  auto kern = fa2::fa2_wide_kernel<D, BF16, MASK>;
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, W::LDS_BYTES);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(W::THREADS), W::LDS_BYTES, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16, int MASK>
 hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream) {
-  constexpr TileCfg c = cfg_for(D);
-  return launch<D, c.bc, c.nw, c.qb, c.kvg, BF16, MASK>(p, grid, stream);
+  if constexpr (D >= 512) {
+    return launch_wide<D, BF16, MASK>(p, grid, stream);
+  } else {
+    constexpr TileCfg c = cfg_for(D);
+    return launch<D, c.bc, c.nw, c.qb, c.kvg, BF16, MASK>(p, grid, stream);
+  }
 }
 
 template <bool BF16, int MASK>
@@ -114,7 +147,9 @@ hipError_t launch_dt(int64_t d, const fa2::Params& p, int64_t grid, hipStream_t 
     case 64: return launch_d<64, BF16, MASK>(p, grid, stream);
     case 96: return launch_d<96, BF16, MASK>(p, grid, stream);
     case 128: return launch_d<128, BF16, MASK>(p, grid, stream);
-    default: return launch_d<256, BF16, MASK>(p, grid, stream);
+    case 256: return launch_d<256, BF16, MASK>(p, grid, stream);
+    case 512: return launch_d<512, BF16, MASK>(p, grid, stream);
+    default: return launch_d<1024, BF16, MASK>(p, grid, stream);
   }
 }
 
@@ -182,7 +217,7 @@ const char* fa2_status_string(int status) {
     case FA2_OK: return "ok";
     case FA2_ERR_NULL_POINTER: return "a buffer pointer is NULL";
     case FA2_ERR_BAD_SHAPE: return "bad shape: B, H, N must be >= 1 and within the size limits";
-    case FA2_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension (supported: 32, 64, 96, 128, 256)";
+    case FA2_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension (supported: 32, 64, 96, 128, 256, 512, 1024)";
     case FA2_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype (supported: fp16, bf16)";
     case FA2_ERR_BAD_SCALE: return "scale is not a finite number";
     case FA2_ERR_MISALIGNED: return "Q, K, V, O must be 16-byte aligned and LSE 4-byte aligned";
@@ -201,7 +236,7 @@ fa2_status_t fa2_launch_info(int64_t B, int64_t H, int64_t N, int64_t d, int is_
   if (st != FA2_OK) return st;
   const TileCfg c = cfg_for(d);
   if (workgroups) *workgroups = grid;
-  if (threads) *threads = c.nw * 64;
+  if (threads) *threads = threads_for(d);
   if (rows_per_wg) *rows_per_wg = ::rows_per_wg(d);
   if (keys_per_tile) *keys_per_tile = c.bc;
   if (lds_bytes) *lds_bytes = lds_bytes_for(d);

@@ -60,7 +60,7 @@ typedef enum {
   FA2_OK = 0,
   FA2_ERR_NULL_POINTER = 1,         /* a buffer pointer is NULL                            */
   FA2_ERR_BAD_SHAPE = 2,            /* B, H or N < 1, or a size limit below is exceeded      */
-  FA2_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d is not 32, 64, 96, 128 or 256                       */
+  FA2_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d is not 32, 64, 96, 128, 256, 512 or 1024            */
   FA2_ERR_UNSUPPORTED_DTYPE = 4,    /* dtype is not FA2_DTYPE_FP16 or FA2_DTYPE_BF16         */
   FA2_ERR_BAD_SCALE = 5,            /* scale is NaN or infinite                              */
   FA2_ERR_MISALIGNED = 6,           /* Q, K, V, O not 16-byte aligned, LSE or key_lens not 4 */
@@ -76,12 +76,13 @@ typedef enum {
  *   LSE       device pointer to a [B, H, N] float32 tensor (written).
  *   B, H, N   batch, heads, sequence length; each >= 1.  Limits, with R the
  *             query rows per workgroup (256 for d = 64 and 128, 128 for
- *             d = 32, 96 and 256; fa2_launch_info reports it):
+ *             d = 32, 96, 256 and 512, 64 for d = 1024; fa2_launch_info
+ *             reports it):
  *             (N + 256) * d * 2 < 2^31 (one head's slice, with the rows past
  *             N that the last query tile and the last key tiles touch, is
  *             addressed with signed 32-bit byte offsets) and
  *             ceil(N / R) * H * B < 2^31 (grid size).
- *   d         head dimension: 32, 64, 96, 128 or 256.
+ *   d         head dimension: 32, 64, 96, 128, 256, 512 or 1024.
  *   scale     softmax scale applied to Q K^T before the row max; any finite value.
  *   is_causal 0: all keys visible; nonzero: key j visible to query i iff j <= i.
  *   dtype     element type of Q, K, V and O (fa2_dtype_t).

@@ -67,7 +67,7 @@ def test_bad_shape(kw):
     assert call(**kw) == bd.FA2_ERR_BAD_SHAPE
 
 
-@pytest.mark.parametrize("d", [0, 1, 16, 31, 48, 63, 65, 80, 160, 192, 512])
+@pytest.mark.parametrize("d", [0, 1, 16, 31, 48, 63, 65, 80, 160, 192, 384, 768, 2048])
 def test_unsupported_head_dim(d):
     assert call(d=d) == bd.FA2_ERR_UNSUPPORTED_HEAD_DIM
 
@@ -99,13 +99,13 @@ def test_launch_info_headline_shape():
     assert info["rows_per_wg"] * math.ceil(8192 / info["rows_per_wg"]) * 8 \
         == info["workgroups"] * info["rows_per_wg"]
     assert info["threads"] % 64 == 0 and info["lds_bytes"] <= 160 * 1024
-    for d in (32, 64, 96, 128, 256):
+    for d in (32, 64, 96, 128, 256, 512, 1024):
         i = fa.fa2_launch_info(4, 8, 2047, d, 1, fa.FA2_DTYPE_BF16)
         assert i["workgroups"] == 32 * math.ceil(2047 / i["rows_per_wg"])
         assert i["lds_bytes"] <= 160 * 1024
 
 
-@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256, 512, 1024])
 def test_slice_size_limit(d):
     """(N + 256) * d * 2 bytes must stay below 2^31."""
     n_max = -(-(1 << 31) // (2 * d)) - 256 - 1  # largest N with (N + 256) * 2d < 2^31

@@ -28,7 +28,7 @@ MASKS = [
     (50, -1, [512, 17]),     # left window and padding: rows past the keys see nothing
     (7, 3, [1, 650]),        # narrow window and a one-key sequence
 ]
-DIMS = (32, 64, 96, 128, 256)
+DIMS = (32, 64, 96, 128, 256, 512, 1024)
 
 
 def _ids(m):
@@ -133,7 +133,7 @@ def test_masked_workload_full_size_sampled_rows(gpu_device, w):
     assert_close_masked(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, w.dtype, w.name)
 
 
-@pytest.mark.parametrize("d", (32, 64, 96, 256))
+@pytest.mark.parametrize("d", (32, 64, 96, 256, 512, 1024))
 @pytest.mark.parametrize("dtype", [wl.FP16, wl.BF16])
 @pytest.mark.parametrize("mask", [(300, 0, None), (-1, 40, [1500, 900])], ids=["window", "padded"])
 def test_masked_late_score_jumps(gpu_device, d, dtype, mask):

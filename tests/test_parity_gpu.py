@@ -36,7 +36,7 @@ def test_full_size_workload_sampled_rows(gpu_device, w):
     assert_close(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, w.dtype, w.name)
 
 
-CASES = [(d, dt, c) for d in (32, 64, 96, 128, 256) for dt in (wl.FP16, wl.BF16) for c in (False, True)]
+CASES = [(d, dt, c) for d in (32, 64, 96, 128, 256, 512, 1024) for dt in (wl.FP16, wl.BF16) for c in (False, True)]
 
 
 @pytest.mark.parametrize("d,dtype,causal", CASES,
@@ -55,7 +55,8 @@ RAGGED = [1, 2, 17, 31, 33, 63, 64, 65, 127, 255, 256, 257, 513]
 
 
 @pytest.mark.parametrize("n", RAGGED)
-@pytest.mark.parametrize("d,dtype", [(32, wl.BF16), (64, wl.FP16), (96, wl.FP16), (128, wl.BF16), (256, wl.FP16)])
+@pytest.mark.parametrize("d,dtype", [(32, wl.BF16), (64, wl.FP16), (96, wl.FP16), (128, wl.BF16), (256, wl.FP16),
+                                     (512, wl.BF16), (1024, wl.FP16)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_lengths(gpu_device, n, d, dtype, causal):
     w = wl.Workload("r", 1, 2, n, d, dtype, causal)
@@ -132,7 +133,7 @@ def test_bad_argument_launches_nothing(gpu_device):
     assert torch.all(o == 7.0) and torch.all(lse == 7.0)
 
 
-STRESS_DIMS = (32, 64, 96, 128, 256)
+STRESS_DIMS = (32, 64, 96, 128, 256, 512, 1024)
 
 
 @pytest.mark.parametrize("d", STRESS_DIMS)
