@@ -217,7 +217,8 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5),
-                     "kernel": "fa2_fwd_kernel", "flops_per_launch": flops},
+                     "kernel": "fa2_wide_kernel" if w.d >= 512 else "fa2_fwd_kernel",
+                     "flops_per_launch": flops},
         "clock_settle": {"launches": settle[0], "ms": round(settle[1], 1),
                          "note": "untimed launches before the warmup, until the per-launch time is steady"},
         "baseline_note": "vs_baseline divides by 185.7 TFLOPS: the leetCUDA notes page's best "

@@ -226,10 +226,13 @@ struct Fa2Wide {
       for (int ks = 0; ks < KS; ++ks)
         st.s = mfma32<BF16>(a[ks], st.qf[S * KS + ks], (S == 0 && ks == 0) ? f32x16{} : st.s);
       if constexpr (PAIR && S == C - 1) {
-        // This wave's partial scores, for the other wave of the pair.
-        auto* x = (__attribute__((address_space(3))) f32x4*)(xch + (threadIdx.x >> 6) * 4096 + cx.lane * 64);
+        // This wave's partial scores, for the other wave of the pair, as
+        // [register group][lane] so that each 16-lane quarter of a write
+        // covers 256 contiguous bytes (all 64 banks once).
+        auto* x = (__attribute__((address_space(3))) f32x4*)(xch + (threadIdx.x >> 6) * 4096);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = f32x4{st.s[4 * i], st.s[4 * i + 1], st.s[4 * i + 2], st.s[4 * i + 3]};
+        for (int i = 0; i < 4; ++i)
+          x[i * 64 + cx.lane] = f32x4{st.s[4 * i], st.s[4 * i + 1], st.s[4 * i + 2], st.s[4 * i + 3]};
       }
     } else {
       // O^T += V^T (chunk S - C) . P^T for this wave's output blocks of the chunk.
@@ -254,11 +257,10 @@ struct Fa2Wide {
     __syncthreads();
     if constexpr (S == C - 1) {
       if constexpr (PAIR) {
-        const auto* x =
-            (const __attribute__((address_space(3))) f32x4*)(xch + ((threadIdx.x >> 6) ^ 1) * 4096 + cx.lane * 64);
+        const auto* x = (const __attribute__((address_space(3))) f32x4*)(xch + ((threadIdx.x >> 6) ^ 1) * 4096);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const f32x4 y = x[i];
+          const f32x4 y = x[i * 64 + cx.lane];
 #pragma unroll
           for (int e = 0; e < 4; ++e) st.s[4 * i + e] += y[e];
         }

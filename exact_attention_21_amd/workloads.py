@@ -10,6 +10,7 @@ training-style d=128 bf16 shape, a long-context causal N=32768 shape and a
 d=256 bf16 shape with a ragged length and a wide score range.  Two masked
 workloads exercise fa2_fwd_masked: a 4096-key causal sliding window over a
 long sequence, and a causal batch of right-padded sequences of mixed lengths.
+Two more run the chunked kernel of head dims 512 and 1024.
 
 Draw recipe (one generator per call): ``numpy.random.default_rng(seed)``
 (PCG64); Q, then K, then V, each drawn as one float64 array of shape
@@ -102,7 +103,12 @@ WINDOW = Workload("window4096_b1h8n32768d64_fp16", 1, 8, 32768, 64, FP16, False,
 PADDED_CAUSAL = Workload("padded_causal_b8h16n4096d128_bf16", 8, 16, 4096, 128, BF16, True,
                          key_lens=(4096, 3001, 2048, 517, 4096, 1290, 3777, 64))
 MASKED_WORKLOADS = [WINDOW, PADDED_CAUSAL]
-ALL_WORKLOADS = WORKLOADS + MASKED_WORKLOADS
+
+# Head dims past 256 (the chunked kernel).
+D512 = Workload("d512_b2h4n8192_fp16", 2, 4, 8192, 512, FP16, False)
+D1024_CAUSAL = Workload("d1024_causal_b2h2n8192_bf16", 2, 2, 8192, 1024, BF16, True)
+HEADDIM_WORKLOADS = [D512, D1024_CAUSAL]
+ALL_WORKLOADS = WORKLOADS + MASKED_WORKLOADS + HEADDIM_WORKLOADS
 
 
 def _draw(rng: np.random.Generator, shape, dist) -> np.ndarray:

@@ -22,7 +22,8 @@ def sampled_rows(n, seed=0, edge=64, inner=128):
     return np.unique(rows)
 
 
-@pytest.mark.parametrize("w", wl.WORKLOADS, ids=[w.name for w in wl.WORKLOADS])
+@pytest.mark.parametrize("w", wl.WORKLOADS + wl.HEADDIM_WORKLOADS,
+                         ids=[w.name for w in wl.WORKLOADS + wl.HEADDIM_WORKLOADS])
 def test_full_size_workload_sampled_rows(gpu_device, w):
     """Every workload at its full size, in the launch configuration the benchmark
     times; the oracle evaluates a sample of rows (both ends of the sequence,
