@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <unordered_map>
 
 #include "fa2_kernel.hpp"
 #include "fa2_wide.hpp"
@@ -26,24 +27,31 @@ struct TileCfg {
   int kvg;
 };
 
-// Two waves per SIMD (8 per workgroup) let one wave's softmax issue beside
-// the other's MFMAs; d = 32 and 64 get them from split-KV, d = 128 from 8
-// waves of 32 rows on one K/V stream (64 rows per wave, 4 waves, measured
-// 8% slower).  d = 32 and 96 use 64-key tiles: with 32 keys their tiles have
+// Two waves per SIMD let one wave's softmax issue beside the other's MFMAs.
+// d = 32 and 64 have two forms with the same rows per workgroup: 8 waves in
+// two split-KV groups (one workgroup per CU, two waves per SIMD), or 4 waves
+// on one K/V stream, of which two workgroups share a CU and hide each other's
+// prologue and epilogue (choose_split picks by grid size).  d = 128 runs 8
+// waves of 32 rows on one K/V stream (64 rows per wave, 4 waves, measured 8%
+// slower).  d = 32 and 96 use 64-key tiles: with 32 keys their tiles have
 // fewer 16-byte chunks than the threads that load them (d = 32) or a
 // fractional number per thread (d = 96).  d = 96 runs without split-KV so
-// that its ring (96 KiB) fits the LDS.  (FA2_SPLIT_KV = 0: d = 32 and 64
-// with one group of 4 waves.)
-constexpr TileCfg cfg_for(int64_t d) {
-  return d == 32    ? (FA2_SPLIT_KV ? TileCfg{64, 8, 1, 2} : TileCfg{64, 4, 1, 1})
-         : d == 64  ? (FA2_SPLIT_KV ? TileCfg{32, 8, 2, 2} : TileCfg{32, 4, 2, 1})
+// that its ring (96 KiB) fits the LDS.
+constexpr bool has_split_form(int64_t d) { return d == 32 || d == 64; }
+
+constexpr TileCfg cfg_for(int64_t d, bool split = true) {
+  return d == 32    ? (split ? TileCfg{64, 8, 1, 2} : TileCfg{64, 4, 1, 1})
+         : d == 64  ? (split ? TileCfg{32, 8, 2, 2} : TileCfg{32, 4, 2, 1})
          : d == 96  ? TileCfg{64, 4, 1, 1}
          : d == 128 ? TileCfg{32, 8, 1, 1}
                     : TileCfg{32, 4, 1, 1};
 }
 
-template <int D>
-using KernelFor = fa2::Fa2Fwd<D, cfg_for(D).bc, cfg_for(D).nw, cfg_for(D).qb, cfg_for(D).kvg, false, false>;
+template <int D, bool SPLIT = true>
+using KernelFor = fa2::Fa2Fwd<D, cfg_for(D, SPLIT).bc, cfg_for(D, SPLIT).nw, cfg_for(D, SPLIT).qb,
+                              cfg_for(D, SPLIT).kvg, false, false>;
+static_assert(KernelFor<32, false>::BR == KernelFor<32>::BR && KernelFor<64, false>::BR == KernelFor<64>::BR,
+              "both forms of d = 32 and 64 cover the same rows, so the grid does not depend on the choice");
 // Head dims 512 and 1024 run the chunked kernel (fa2_wide.hpp).
 template <int D>
 using WideFor = fa2::Fa2Wide<D, false, fa2::kMaskNone>;
@@ -54,14 +62,43 @@ constexpr int rows_per_wg(int64_t d) {
          : d == 512 ? WideFor<512>::BR : WideFor<1024>::BR;
 }
 
-constexpr int lds_bytes_for(int64_t d) {
-  return d == 32 ? KernelFor<32>::LDS_BYTES : d == 64 ? KernelFor<64>::LDS_BYTES
+constexpr int lds_bytes_for(int64_t d, bool split = true) {
+  return d == 32 ? (split ? KernelFor<32>::LDS_BYTES : KernelFor<32, false>::LDS_BYTES)
+         : d == 64 ? (split ? KernelFor<64>::LDS_BYTES : KernelFor<64, false>::LDS_BYTES)
          : d == 96 ? KernelFor<96>::LDS_BYTES : d == 128 ? KernelFor<128>::LDS_BYTES
          : d == 256 ? KernelFor<256>::LDS_BYTES : d == 512 ? WideFor<512>::LDS_BYTES : WideFor<1024>::LDS_BYTES;
 }
 
-constexpr int threads_for(int64_t d) {
-  return d == 512 ? WideFor<512>::THREADS : d == 1024 ? WideFor<1024>::THREADS : cfg_for(d).nw * 64;
+constexpr int threads_for(int64_t d, bool split = true) {
+  return d == 512 ? WideFor<512>::THREADS : d == 1024 ? WideFor<1024>::THREADS : cfg_for(d, split).nw * 64;
+}
+
+// Compute units of the current device (256, MI355X's count, when no device
+// can be queried), looked up once per device.
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static std::mutex mu;
+  static std::unordered_map<int, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev] = n;
+  return n;
+}
+
+// Split-KV form for d = 32 and 64 (see cfg_for) unless the grid gives every
+// CU two workgroups of the 4-wave form; under a causal or general mask the
+// query tiles differ in length, and two workgroups per CU balance only over
+// several rounds (measured: 6 workgroups per CU and more win, 2 lose 10%).
+// Measured on the 4-wave form against split-KV: +2% to +4% from 2 workgroups
+// per CU, +35% at N = 512 (d = 64), -1.5% with one workgroup per CU.
+bool choose_split(int64_t d, int64_t grid, int mask) {
+  if (!has_split_form(d) || !FA2_SPLIT_KV) return false;
+  const int64_t per_cu = mask == fa2::kMaskNone ? 2 : 6;
+  return grid < per_cu * device_cus();
 }
 
 // Rows past N that a launch may address (see check_shape).
@@ -103,7 +140,7 @@ fa2_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, 
 template <int D, int BC, int NW, int QB, int KVG, bool BF16, int MASK>
 hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
   constexpr int lds = fa2::Fa2Fwd<D, BC, NW, QB, KVG, BF16, MASK>::LDS_BYTES;
-  static_assert(lds == lds_bytes_for(D), "LDS size");
+  static_assert(lds == lds_bytes_for(D, KVG == 2 || !has_split_form(D)), "LDS size");
   auto kern = fa2::fa2_fwd_kernel<D, BC, NW, QB, KVG, BF16, MASK>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
@@ -131,9 +168,13 @@ hipError_t launch_wide(const fa2::Params& p, int64_t grid, hipStream_t stream) {
 }
 
 template <int D, bool BF16, int MASK>
-hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream) {
+hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream, bool split) {
   if constexpr (D >= 512) {
     return launch_wide<D, BF16, MASK>(p, grid, stream);
+  } else if constexpr (has_split_form(D)) {
+    constexpr TileCfg s = cfg_for(D, true), u = cfg_for(D, false);
+    return split ? launch<D, s.bc, s.nw, s.qb, s.kvg, BF16, MASK>(p, grid, stream)
+                 : launch<D, u.bc, u.nw, u.qb, u.kvg, BF16, MASK>(p, grid, stream);
   } else {
     constexpr TileCfg c = cfg_for(D);
     return launch<D, c.bc, c.nw, c.qb, c.kvg, BF16, MASK>(p, grid, stream);
@@ -141,24 +182,24 @@ hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream) {
 }
 
 template <bool BF16, int MASK>
-hipError_t launch_dt(int64_t d, const fa2::Params& p, int64_t grid, hipStream_t stream) {
+hipError_t launch_dt(int64_t d, const fa2::Params& p, int64_t grid, hipStream_t stream, bool split) {
   switch (d) {
-    case 32: return launch_d<32, BF16, MASK>(p, grid, stream);
-    case 64: return launch_d<64, BF16, MASK>(p, grid, stream);
-    case 96: return launch_d<96, BF16, MASK>(p, grid, stream);
-    case 128: return launch_d<128, BF16, MASK>(p, grid, stream);
-    case 256: return launch_d<256, BF16, MASK>(p, grid, stream);
-    case 512: return launch_d<512, BF16, MASK>(p, grid, stream);
-    default: return launch_d<1024, BF16, MASK>(p, grid, stream);
+    case 32: return launch_d<32, BF16, MASK>(p, grid, stream, split);
+    case 64: return launch_d<64, BF16, MASK>(p, grid, stream, split);
+    case 96: return launch_d<96, BF16, MASK>(p, grid, stream, split);
+    case 128: return launch_d<128, BF16, MASK>(p, grid, stream, split);
+    case 256: return launch_d<256, BF16, MASK>(p, grid, stream, split);
+    case 512: return launch_d<512, BF16, MASK>(p, grid, stream, split);
+    default: return launch_d<1024, BF16, MASK>(p, grid, stream, split);
   }
 }
 
 template <bool BF16>
-hipError_t launch_mask(int mask, int64_t d, const fa2::Params& p, int64_t grid, hipStream_t stream) {
+hipError_t launch_mask(int mask, int64_t d, const fa2::Params& p, int64_t grid, hipStream_t stream, bool split) {
   switch (mask) {
-    case fa2::kMaskNone: return launch_dt<BF16, fa2::kMaskNone>(d, p, grid, stream);
-    case fa2::kMaskCausal: return launch_dt<BF16, fa2::kMaskCausal>(d, p, grid, stream);
-    default: return launch_dt<BF16, fa2::kMaskGeneral>(d, p, grid, stream);
+    case fa2::kMaskNone: return launch_dt<BF16, fa2::kMaskNone>(d, p, grid, stream, split);
+    case fa2::kMaskCausal: return launch_dt<BF16, fa2::kMaskCausal>(d, p, grid, stream, split);
+    default: return launch_dt<BF16, fa2::kMaskGeneral>(d, p, grid, stream, split);
   }
 }
 
@@ -203,8 +244,9 @@ fa2_status_t checked_launch(const void* Q, const void* K, const void* V, void* O
   p.heads = (int)H;
 
   hipStream_t s = (hipStream_t)stream;
-  const hipError_t err = dtype == FA2_DTYPE_BF16 ? launch_mask<true>(mask, d, p, grid, s)
-                                                 : launch_mask<false>(mask, d, p, grid, s);
+  const bool split = choose_split(d, grid, mask);
+  const hipError_t err = dtype == FA2_DTYPE_BF16 ? launch_mask<true>(mask, d, p, grid, s, split)
+                                                 : launch_mask<false>(mask, d, p, grid, s, split);
   return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
 }
 
@@ -230,16 +272,16 @@ const char* fa2_status_string(int status) {
 fa2_status_t fa2_launch_info(int64_t B, int64_t H, int64_t N, int64_t d, int is_causal, int dtype,
                              int64_t* workgroups, int* threads, int* rows_per_wg,
                              int* keys_per_tile, int* lds_bytes) {
-  (void)is_causal;
   int64_t grid = 0;
   const fa2_status_t st = check_shape(B, H, N, d, dtype, &grid);
   if (st != FA2_OK) return st;
-  const TileCfg c = cfg_for(d);
+  const bool split = choose_split(d, grid, is_causal ? fa2::kMaskCausal : fa2::kMaskNone);
+  const TileCfg c = cfg_for(d, split);
   if (workgroups) *workgroups = grid;
-  if (threads) *threads = threads_for(d);
+  if (threads) *threads = threads_for(d, split);
   if (rows_per_wg) *rows_per_wg = ::rows_per_wg(d);
   if (keys_per_tile) *keys_per_tile = c.bc;
-  if (lds_bytes) *lds_bytes = lds_bytes_for(d);
+  if (lds_bytes) *lds_bytes = lds_bytes_for(d, split);
   return FA2_OK;
 }
 

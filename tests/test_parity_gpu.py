@@ -184,3 +184,27 @@ def test_steadily_growing_scores(gpu_device, causal):
     o_ref, lse_ref = attention_ref(*(wl.to_float64(x, wl.FP16) for x in (q, k, v)), 0.125, causal)
     bound = p_rounding_bound(q, k, v, o_ref, wl.FP16, 0.125, causal)
     assert_close_stress(o, lse, o_ref, lse_ref, bound, wl.FP16, f"growing scores causal={causal}")
+
+
+FORM_CASES = [(d, dt, c) for d in (32, 64) for dt in (wl.FP16, wl.BF16) for c in (False, True)]
+
+
+@pytest.mark.parametrize("d,dtype,causal", FORM_CASES,
+                         ids=[f"d{d}-{dt}-{'causal' if c else 'full'}" for d, dt, c in FORM_CASES])
+def test_four_wave_form_on_large_grids(gpu_device, d, dtype, causal):
+    """d = 32 and 64 switch from split-KV (8 waves) to the 4-wave form when the
+    grid gives every compute unit several workgroups: parity of that form on
+    such a grid (sampled rows: both ends of every sequence and random rows)."""
+    import exact_attention_21_amd as fa
+    B, H, N = (32, 16, 1024) if causal else (16, 16, 1000)
+    info = fa.fa2_launch_info(B, H, N, d, int(causal), 1 if dtype == wl.BF16 else 0)
+    assert info["threads"] == 256, info  # the 4-wave form was chosen
+    small = fa.fa2_launch_info(1, 2, 300, d, int(causal), 0)
+    assert small["threads"] == 512, small  # and split-KV on a small grid
+    w = wl.Workload("f", B, H, N, d, dtype, causal)
+    q, k, v = wl.make_inputs(w, seed=17)
+    o, lse = run_gpu(q, k, v, dtype, w.softmax_scale(), causal, gpu_device)
+    rows = sampled_rows(N, seed=3, edge=32, inner=32)
+    o_ref, lse_ref = attention_ref(*(wl.to_float64(x, dtype) for x in (q, k, v)), w.softmax_scale(), causal,
+                                   rows=rows)
+    assert_close(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, dtype, f"4-wave form d{d} {dtype} causal={causal}")
