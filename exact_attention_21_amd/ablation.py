@@ -37,10 +37,12 @@ VARIANTS = [
     ("checked_only", {"FA2_UNCHECKED_RUN": 0}, "every tile's row sums checked; no fixed-base unchecked run"),
     ("no_split_kv", {"FA2_SPLIT_KV": 0}, "4 waves per workgroup with one K/V stream (no split-KV wave groups)"),
     ("deep_ring", {"FA2_DEEP_RING": 1}, "8-slot K/V rings, one barrier per 4 tiles (instead of 4 slots, per 2)"),
+    ("no_xcd_groups", {"FA2_XCD_GROUPS": 0}, "work order over all heads at once (no XCD-sized head groups)"),
 ]
-# Switches that only move data in LDS or change the barrier cadence: the
-# arithmetic is the same, so the output must be bit-identical.
-LAYOUT_ONLY = {"no_kv_swizzle", "deep_ring"}
+# Switches that only move data in LDS, change the barrier cadence or the order
+# of the workgroups: the arithmetic is the same, so the output must be
+# bit-identical.
+LAYOUT_ONLY = {"no_kv_swizzle", "deep_ring", "no_xcd_groups"}
 
 
 def lib_path(name: str) -> str:
@@ -74,7 +76,7 @@ def main() -> int:
     from exact_attention_21_amd import _binding as bd
     from exact_attention_21_amd import workloads as wl
 
-    w = {x.name: x for x in wl.WORKLOADS}[args.workload]
+    w = {x.name: x for x in wl.ALL_WORKLOADS}[args.workload]
     dev = torch.device("cuda:0")
     q, k, v = wl.make_inputs(w, seed=0)
 
@@ -99,15 +101,28 @@ def main() -> int:
     outs = {n: (torch.empty_like(tq), torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev))
             for n in names}
 
+    # Masked workloads: fa2_fwd_masked with the workload's window and lengths.
+    left, right = w.window if w.window is not None else (-1, -1)
+    if w.causal:
+        right = 0 if right < 0 else min(right, 0)
+    lens = torch.tensor(w.key_lens, dtype=torch.int32, device=dev) if w.key_lens is not None else None
+
     def launcher(n):
         lib, (o, lse) = libs[n], outs[n]
-        args_ = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                 w.B, w.H, w.N, w.d, scale, int(w.causal), dt, stream.cuda_stream)
+        if w.masked:
+            args_ = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     w.B, w.H, w.N, w.d, scale, left, right, lens.data_ptr() if lens is not None else None, dt,
+                     stream.cuda_stream)
+            fn, fname = lib.fa2_fwd_masked, "fa2_fwd_masked"
+        else:
+            args_ = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     w.B, w.H, w.N, w.d, scale, int(w.causal), dt, stream.cuda_stream)
+            fn, fname = lib.fa2_fwd, "fa2_fwd"
 
         def run():
-            st = lib.fa2_fwd(*args_)
+            st = fn(*args_)
             if st != bd.FA2_OK:
-                raise bd.Fa2Error(st, f"fa2_fwd ({n})")
+                raise bd.Fa2Error(st, f"{fname} ({n})")
         return run
 
     runs = {n: launcher(n) for n in names}
@@ -122,14 +137,27 @@ def main() -> int:
     if not args.no_torch:
         kt = tk.transpose(-1, -2).contiguous()
 
+        hidden = None
+        if w.causal or w.masked:
+            i = torch.arange(w.N, device=dev)[:, None]
+            j = torch.arange(w.N, device=dev)[None, :]
+            hidden = torch.zeros(w.N, w.N, dtype=torch.bool, device=dev)
+            if right >= 0:
+                hidden |= j > i + right
+            if left >= 0:
+                hidden |= j < i - left
+            hidden = hidden[None, None]
+            if lens is not None:
+                hidden = hidden | (j[None, None] >= lens[:, None, None, None])
+
         def unfused():
             s = torch.matmul(tq, kt) * scale
-            if w.causal:
-                s = s.masked_fill(torch.ones(w.N, w.N, dtype=torch.bool, device=dev).triu(1), float("-inf"))
+            if hidden is not None:
+                s = s.masked_fill(hidden, float("-inf"))
             p = torch.softmax(s.float(), dim=-1).to(tq.dtype)
             return torch.matmul(p, tv)
         runs["torch_unfused"] = unfused
-        if w.dtype == wl.FP16:
+        if w.dtype == wl.FP16 and not w.masked:
             from torch.nn.attention import SDPBackend, sdpa_kernel
             import torch.nn.functional as F
 

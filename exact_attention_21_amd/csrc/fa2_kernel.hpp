@@ -48,10 +48,10 @@
 //     range-checked resource (the pages' zero fill), and out-of-range stores
 //     are dropped by the same check.
 //   * The grid is one workgroup per (query tile, batch*head); consecutive
-//     workgroup ids walk the heads first, so with B*H a multiple of 8 every
-//     head stays on one XCD (workgroups are dealt to the 8 XCDs round robin)
-//     and its K/V stay in that XCD's L2.  Causal grids issue the longest query
-//     tiles first.
+//     workgroup ids walk the heads first, within groups of heads sized so that
+//     an XCD (workgroups are dealt to the 8 XCDs round robin) runs all query
+//     tiles of its few heads together and their K/V stay in its L2
+//     (work_item).  Causal grids issue the longest query tiles first.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -87,7 +87,32 @@ struct Params {
   int wr;
   const int* key_lens;  // B lengths (clamped to [0, N]) or null: no padding
   int heads;            // H, to find the batch of a (batch*head) slice
+  int group;            // slices per group of the work order (1..bh; see work_item)
 };
+
+// Work item of workgroup wg: its (batch*head) slice and its query-tile step
+// (the step counts from the longest query tile under a mask, see the
+// kernels).  The slices are taken in groups of p.group: every query tile of a
+// group comes before the next group, and inside a group the step varies
+// slowest and the slice fastest.  Workgroups are dealt to the XCDs round robin
+// by index; with p.group a multiple of their count each XCD holds the same
+// slices of a group throughout, and a group small enough that its query tiles
+// are about one XCD's worth of resident workgroups keeps each slice's
+// workgroups walking its keys at nearly the same time, so K and V come from
+// that XCD's L2 instead of HBM.  p.group = bh is the plain order (slice
+// fastest over all slices).
+struct WorkItem {
+  int bh;
+  int step;
+};
+__device__ __forceinline__ WorkItem work_item(const Params& p, int wg) {
+  const int span = p.group * p.n_qtiles;
+  const int g = wg / span;
+  const int r = wg - g * span;
+  const int size = min(p.group, p.bh - g * p.group);  // the last group may be smaller
+  const int step = r / size;
+  return {g * p.group + (r - step * size), step};
+}
 
 // Mask modes (template argument MASK).
 enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskGeneral = 2 };
@@ -196,6 +221,9 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 //                      0: the checked pipeline only.
 //   FA2_SPLIT_KV       1: two split-KV wave groups at d = 32 and 64 (host side);
 //                      0: one group of 4 waves.
+//   FA2_XCD_GROUPS     1: slices taken in groups whose query tiles fill one
+//                      round of an XCD's resident workgroups (host side, see
+//                      work_item); k: k rounds; 0: one group of all slices.
 #ifndef FA2_KV_SWIZZLE
 #define FA2_KV_SWIZZLE 1
 #endif
@@ -207,6 +235,9 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 #endif
 #ifndef FA2_SPLIT_KV
 #define FA2_SPLIT_KV 1
+#endif
+#ifndef FA2_XCD_GROUPS
+#define FA2_XCD_GROUPS 1
 #endif
 
 // LDS layouts.  A K or V tile is BC rows (keys) of D 16-bit values, stored as
@@ -413,12 +444,11 @@ struct Fa2Fwd {
     const int wave = tid >> 6;
     const int half = lane >> 5;
 
-    // Work item: heads vary fastest; masked grids take the last query tiles
-    // (the longest under a causal mask) first.
-    const int wg = blockIdx.x;
-    const int bh = wg % p.bh;
-    const int t = wg / p.bh;
-    const int qtile = MASK != kMaskNone ? (p.n_qtiles - 1 - t) : t;
+    // Work item (work_item); masked grids take the last query tiles (the
+    // longest under a causal mask) first.
+    const WorkItem item = work_item(p, blockIdx.x);
+    const int bh = item.bh;
+    const int qtile = MASK != kMaskNone ? (p.n_qtiles - 1 - item.step) : item.step;
     const int n = p.n;
     const int q0 = qtile * BR;
     // Query rows of this wave.  Split-KV: waves w and w+NW/2 own the same rows.

@@ -284,10 +284,9 @@ struct Fa2Wide {
     const int pw = PAIR ? (wave & 1) : 0;   // the wave's half of each chunk (pairs)
     const int rw = PAIR ? (wave >> 1) : wave;
 
-    const int wg = blockIdx.x;
-    const int bh = wg % p.bh;
-    const int tq = wg / p.bh;
-    const int qtile = MASK != kMaskNone ? (p.n_qtiles - 1 - tq) : tq;
+    const WorkItem item = work_item(p, blockIdx.x);
+    const int bh = item.bh;
+    const int qtile = MASK != kMaskNone ? (p.n_qtiles - 1 - item.step) : item.step;
     const int n = p.n;
     const int q0 = qtile * BR;
     const int qw0 = q0 + rw * 32;
