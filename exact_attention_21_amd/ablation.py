@@ -10,8 +10,9 @@ variant's output is compared with the shipped build's on the same inputs
 summation order or the exponent base and must stay within 1e-3).
 
 Two PyTorch rows give context, as the ablation table on the MMA notes page
-does: attention in three steps (S = Q K^T into HBM, softmax, P V), and
-torch's scaled_dot_product_attention (fp16 only, and never its math backend).
+does: attention in three steps (S = Q K^T into HBM, the mask, softmax, P V),
+and torch's scaled_dot_product_attention (fp16 unmasked or causal only, and
+never its math backend).  Masked workloads run fa2_fwd_masked.
 
     python exact_attention_21_amd/ablation.py --build        # compile the variant builds (no GPU needed)
     python exact_attention_21_amd/ablation.py [--workload NAME] [--rounds 5]
