@@ -91,14 +91,21 @@ int device_cus() {
 }
 
 // Split-KV form for d = 32 and 64 (see cfg_for) unless the grid gives every
-// CU two workgroups of the 4-wave form; under a causal or general mask the
-// query tiles differ in length, and two workgroups per CU balance only over
-// several rounds (measured: 6 workgroups per CU and more win, 2 lose 10%).
-// Measured on the 4-wave form against split-KV: +2% to +4% from 2 workgroups
-// per CU, +35% at N = 512 (d = 64), -1.5% with one workgroup per CU.
-bool choose_split(int64_t d, int64_t grid, int mask) {
+// CU enough workgroups of the 4-wave form (two of which share a CU).
+// Measured, same-process A/B of the two forms:
+//   no mask: split-KV +1% to +2% at one workgroup per CU, even at two, the
+//     4-wave form +2% to +4% beyond and +35% at N = 512 (d = 64);
+//   causal, fp16 d = 64: split-KV +11% at two per CU (the query tiles differ
+//     in length, and two per CU balance only over several rounds), the 4-wave
+//     form +3% to +13% from three;
+//   bf16 d = 64 under any mask: the 4-wave form +11% to +32% at every grid
+//     tried (one to five per CU): the split-KV form's 8 waves spill there;
+//   windows (fp16 d = 64) and d = 32 under a mask: the 4-wave form +4% to
+//     +23% at two per CU, even at three.
+bool choose_split(int64_t d, int64_t grid, int mask, int dtype) {
   if (!has_split_form(d) || !FA2_SPLIT_KV) return false;
-  const int64_t per_cu = mask == fa2::kMaskNone ? 2 : 6;
+  if (mask != fa2::kMaskNone && d == 64 && dtype == FA2_DTYPE_BF16) return false;
+  const int64_t per_cu = (mask == fa2::kMaskCausal && d == 64) ? 3 : 2;
   return grid < per_cu * device_cus();
 }
 
@@ -287,7 +294,7 @@ fa2_status_t checked_launch(const void* Q, const void* K, const void* V, void* O
   p.group = p.bh;  // set per kernel at launch (slice_group)
 
   hipStream_t s = (hipStream_t)stream;
-  const bool split = choose_split(d, grid, mask);
+  const bool split = choose_split(d, grid, mask, dtype);
   const hipError_t err = dtype == FA2_DTYPE_BF16 ? launch_mask<true>(mask, d, p, grid, s, split)
                                                  : launch_mask<false>(mask, d, p, grid, s, split);
   return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
@@ -318,7 +325,7 @@ fa2_status_t fa2_launch_info(int64_t B, int64_t H, int64_t N, int64_t d, int is_
   int64_t grid = 0;
   const fa2_status_t st = check_shape(B, H, N, d, dtype, &grid);
   if (st != FA2_OK) return st;
-  const bool split = choose_split(d, grid, is_causal ? fa2::kMaskCausal : fa2::kMaskNone);
+  const bool split = choose_split(d, grid, is_causal ? fa2::kMaskCausal : fa2::kMaskNone, dtype);
   const TileCfg c = cfg_for(d, split);
   if (workgroups) *workgroups = grid;
   if (threads) *threads = threads_for(d, split);

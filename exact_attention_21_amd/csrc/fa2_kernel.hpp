@@ -221,6 +221,8 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 //                      0: the checked pipeline only.
 //   FA2_SPLIT_KV       1: two split-KV wave groups at d = 32 and 64 (host side);
 //                      0: one group of 4 waves.
+//   FA2_W4_TWO_PER_SIMD 1: the 4-wave form of d = 64 held to two waves per
+//                      SIMD (256 registers); 0: no register bound.
 //   FA2_XCD_GROUPS     1: slices taken in groups whose query tiles fill one
 //                      round of an XCD's resident workgroups (host side, see
 //                      work_item); k: k rounds; 0: one group of all slices.
@@ -238,6 +240,9 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 #endif
 #ifndef FA2_XCD_GROUPS
 #define FA2_XCD_GROUPS 1
+#endif
+#ifndef FA2_W4_TWO_PER_SIMD
+#define FA2_W4_TWO_PER_SIMD 1
 #endif
 
 // LDS layouts.  A K or V tile is BC rows (keys) of D 16-bit values, stored as
@@ -1182,8 +1187,15 @@ struct Fa2Fwd {
 
 };
 
+// The 4-wave form of d = 64 is held to 256 registers (two waves per SIMD) so
+// that two of its workgroups share a CU and hide each other's prologue,
+// epilogue and barrier waits; unbounded it takes 260 to 276 with bf16 or the
+// general mask, one wave per SIMD.  The other forms fill a CU with one
+// workgroup (8 waves, or LDS- and register-bound d = 96 and 256).
 template <int D, int BC, int NW, int QB, int KVG, bool BF16, int MASK>
-__global__ void __launch_bounds__(NW * 64, 1) fa2_fwd_kernel(const Params p) {
+__global__ void __launch_bounds__(NW * 64)
+    __attribute__((amdgpu_waves_per_eu((FA2_W4_TWO_PER_SIMD && NW == 4 && D == 64) ? 2 : 1)))
+    fa2_fwd_kernel(const Params p) {
   extern __shared__ __attribute__((aligned(16))) char lds_generic[];
   Fa2Fwd<D, BC, NW, QB, KVG, BF16, MASK>::run(
       p, (__attribute__((address_space(3))) char*)(__attribute__((address_space(3))) void*)lds_generic);
