@@ -38,7 +38,8 @@
 //     without first taking the tile's max.  Checked form: a tile whose row sums
 //     exceed 2^15 (so some probability might overflow 16 bits) goes through
 //     the rebase path (row max, rescale O and l, recompute).  Unchecked form
-//     (d = 64, 256): the base stays at the first tile's row max, and a row sum
+//     (every d but 128 under the general mask): the base stays at the first
+//     tile's row max, and a row sum
 //     that overflowed sends the whole workgroup through the checked form.  Any
 //     base gives the same softmax; the pages move it on every tile.
 //   * K and V tiles go from global memory straight into a 4-slot LDS ring
@@ -217,7 +218,8 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 // shipped design; a build that flips one measures what that choice is worth.
 //   FA2_KV_SWIZZLE     1: the K/V chunk permutations below; 0: plain row-major tiles.
 //   FA2_DEEP_RING      0: 4-slot K/V rings; 1: 8 slots where they fit the LDS.
-//   FA2_UNCHECKED_RUN  1: fixed-base unchecked first run (every d but 128);
+//   FA2_UNCHECKED_RUN  1: fixed-base unchecked first run (not at d = 128
+//                      under the general mask);
 //                      0: the checked pipeline only.
 //   FA2_SPLIT_KV       1: two split-KV wave groups at d = 32 and 64 (host side);
 //                      0: one group of 4 waves.
@@ -600,13 +602,14 @@ struct Fa2Fwd {
   // the rounded sum within 2^-11 (natural-log units) of it.
   static constexpr bool LSE_FP32 = BF16;
   // Pipelined schedule: first an unchecked run, rerun checked only if some row
-  // overflowed (see run_pipe).  Measured: 6% faster at d = 64, 12% at d = 256.
-  // At d = 128 the second copy of the pipeline does not fit the registers of
-  // two waves per SIMD (it spills), so d = 128 keeps only the checked run.
-  // Under the general mask a row's window can start after the run's first
-  // tile: its fixed base is taken at the first tile in which it sees a key
-  // (fix_late_bases).
-  static constexpr bool OPTIMISTIC = FA2_UNCHECKED_RUN && D != 128;
+  // overflowed (see run_pipe).  Measured: 6% faster at d = 64, 12% at d = 256,
+  // 1% to 5% at d = 128.  Under the general mask d = 128 keeps only the
+  // checked run: with both copies of the pipeline it does not fit the
+  // registers of two waves per SIMD (it spills about 100 bytes and ran 10%
+  // slower).  Under the general mask a row's window can start after the run's
+  // first tile: its fixed base is taken at the first tile in which it sees a
+  // key (fix_late_bases).
+  static constexpr bool OPTIMISTIC = FA2_UNCHECKED_RUN && !(D == 128 && GENERAL);
 
   // Loop-invariant context.
   struct Ctx {
