@@ -345,14 +345,15 @@ fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float
 fa2_status_t fa2_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, int64_t window_left,
                             int64_t window_right, const int32_t* key_lens, int dtype, void* stream) {
-  // Without padding, no window is the unmasked kernel and a window with no
-  // left bound and right bound 0 is the causal one (the same results, and the
-  // faster unchecked first run); anything else runs the general mask.
+  // No window is the unmasked kernel and a window with no left bound and
+  // right bound 0 the causal one, with or without key lengths (the same
+  // results as the general mask, whose extra work is for windows); anything
+  // else runs the general mask.
   const bool no_left = window_left < 0 || window_left >= N;
   const bool no_right = window_right < 0 || window_right >= N;
   int mask = fa2::kMaskGeneral;
-  if (!key_lens && no_left && no_right) mask = fa2::kMaskNone;
-  if (!key_lens && no_left && window_right == 0) mask = fa2::kMaskCausal;
+  if (no_left && no_right) mask = fa2::kMaskNone;
+  if (no_left && window_right == 0) mask = fa2::kMaskCausal;
   return checked_launch(Q, K, V, O, LSE, B, H, N, d, scale, mask, window_left, window_right, key_lens, dtype,
                         stream);
 }

@@ -82,8 +82,8 @@ struct Params {
   int n_qtiles;      // ceil(N / rows per workgroup)
   float scale_log2;  // |scale| * log2(e): scores go to the base-2 exponent domain
   uint32_t q_sign;   // 0x80008000 when scale < 0: Q is negated on load, |scale| used
-  // General mask only: key j is visible to query i iff j < key_len(b),
-  // j >= i - wl and j <= i + wr (kNoBound: no bound).
+  // Key j is visible to query i iff j < key_len(b) (every mode) and, under
+  // the general mask, j >= i - wl and j <= i + wr (kNoBound: no bound).
   int wl;
   int wr;
   const int* key_lens;  // B lengths (clamped to [0, N]) or null: no padding
@@ -520,10 +520,14 @@ struct Fa2Fwd {
     // Key tiles the workgroup's rows can see: [tfirst, tfirst + ntiles).  A
     // workgroup whose rows see no key at all still runs one fully masked tile,
     // which leaves O = 0 and LSE = +inf.
-    int klen = n, wl = kNoBound, wr = CAUSAL ? 0 : kNoBound, kbeg = 0, kend = n;
-    if constexpr (CAUSAL) kend = min(n, q0 + BR);
+    // Key lengths apply in every mode: without a window a row's visible keys
+    // are a prefix of the sequence, so a row that sees no key in the first
+    // tile of a key range sees none later in it either.
+    int klen = n, wl = kNoBound, wr = CAUSAL ? 0 : kNoBound, kbeg = 0;
+    if (p.key_lens) klen = min(max(p.key_lens[bh / p.heads], 0), n);
+    int kend = klen;
+    if constexpr (CAUSAL) kend = min(klen, q0 + BR);
     if constexpr (GENERAL) {
-      if (p.key_lens) klen = min(max(p.key_lens[bh / p.heads], 0), n);
       wl = p.wl;
       wr = p.wr;
       kbeg = max(0, q0 - wl);
@@ -620,7 +624,7 @@ struct Fa2Fwd {
     LdsOffsets off;
     float c2;
     int lane, tid, qw0;
-    int n;       // keys present: N, or the sequence's key length (general mask)
+    int n;       // keys present: N, or the sequence's key length
     int wl, wr;  // window bounds (general mask; kNoBound: none)
     int late;    // general mask: last tile in which a row of the wave can see its first key
     // A wave takes part in tile j if some key of it is visible to some of its rows.

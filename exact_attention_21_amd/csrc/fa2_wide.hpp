@@ -311,10 +311,14 @@ struct Fa2Wide {
     st.lr = st.lu = 0.f;
 
     // Key tiles the workgroup's rows can see (as in the main kernel).
-    int klen = n, wl = kNoBound, wr = CAUSAL ? 0 : kNoBound, kbeg = 0, kend = n;
-    if constexpr (CAUSAL) kend = min(n, q0 + BR);
+    // Key lengths apply in every mode: without a window a row's visible keys
+    // are a prefix of the sequence, so a row that sees no key in the first
+    // tile of a key range sees none later in it either.
+    int klen = n, wl = kNoBound, wr = CAUSAL ? 0 : kNoBound, kbeg = 0;
+    if (p.key_lens) klen = min(max(p.key_lens[bh / p.heads], 0), n);
+    int kend = klen;
+    if constexpr (CAUSAL) kend = min(klen, q0 + BR);
     if constexpr (GENERAL) {
-      if (p.key_lens) klen = min(max(p.key_lens[bh / p.heads], 0), n);
       wl = p.wl;
       wr = p.wr;
       kbeg = max(0, q0 - wl);

@@ -117,9 +117,10 @@ fa2_status_t fa2_fwd(const void* Q, const void* K, const void* V, void* O, float
  *             included); keys hidden by the window are read and must be
  *             finite, as every key of fa2_fwd must.
  *   All other arguments, checks, limits and status codes are those of
- *   fa2_fwd.  Without key_lens, a call with no window runs fa2_fwd's
- *   unmasked kernel and a call with window (<0, 0) its causal kernel
- *   (bit-identical results); every other call runs the general-mask kernel.
+ *   fa2_fwd.  A call with no window runs fa2_fwd's unmasked kernel and a
+ *   call with window (<0, 0) its causal kernel, with or without key_lens
+ *   (without them the results are bit-identical to fa2_fwd's); every other
+ *   call runs the general-mask kernel.
  */
 fa2_status_t fa2_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale,
