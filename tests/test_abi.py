@@ -105,6 +105,29 @@ def test_launch_info_headline_shape():
         assert i["lds_bytes"] <= 160 * 1024
 
 
+# (B, H, N, d, causal, dtype) -> threads per workgroup the launch picks for
+# d = 32 and 64 (512: 8-wave split-KV form, 256: 4-wave form).  Without a GPU
+# the library assumes 256 compute units, so the grid sizes below are 1, 2 and
+# 3 workgroups per CU (256 query rows per workgroup at d = 64, 128 at d = 32).
+FORM_CHOICES = [
+    ((1, 8, 8192, 64, 0, 0), 512),  # no mask, one per CU: split-KV
+    ((2, 8, 8192, 64, 0, 0), 256),  # no mask, two per CU: 4-wave
+    ((2, 8, 8192, 64, 0, 1), 256),
+    ((2, 8, 8192, 64, 1, 0), 512),  # fp16 causal d = 64 keeps split-KV at two per CU
+    ((3, 8, 8192, 64, 1, 0), 256),  # and takes the 4-wave form from three
+    ((1, 8, 8192, 64, 1, 1), 256),  # bf16 d = 64 under a mask: 4-wave at every grid size
+    ((1, 2, 300, 64, 1, 1), 256),
+    ((1, 8, 4096, 32, 1, 0), 512),  # d = 32 causal, one per CU: split-KV
+    ((2, 8, 4096, 32, 1, 0), 256),  # two per CU: 4-wave
+    ((4, 8, 8192, 128, 1, 1), 512),  # d = 128: one form (8 waves)
+]
+
+
+@pytest.mark.parametrize("args,threads", FORM_CHOICES, ids=[str(a) for a, _ in FORM_CHOICES])
+def test_launch_form_choice_without_gpu(args, threads):
+    assert fa.fa2_launch_info(*args)["threads"] == threads
+
+
 @pytest.mark.parametrize("d", [32, 64, 96, 128, 256, 512, 1024])
 def test_slice_size_limit(d):
     """(N + 256) * d * 2 bytes must stay below 2^31."""
