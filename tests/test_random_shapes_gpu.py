@@ -1,10 +1,11 @@
 """Seeded random shapes through both entry points, every element against the
 fp64 oracle: batch, heads, length (1..900, so ragged tails of every kind),
 head dim (every supported one), dtype, scale (either sign), and the mask
-(none, causal, a random window, random key lengths, or both).  Unmasked and
-causal cases use the stated tolerances; masked ones add the P-rounding bound
-(a window can leave a row only one or two keys, where the rounding of P does
-not average out; see gpu_helpers.p_rounding_bound)."""
+(none, causal, a random window, random key lengths, window and lengths,
+causal and lengths).  Unmasked and causal cases use the stated tolerances;
+masked ones add the P-rounding bound (a window can leave a row only one or
+two keys, where the rounding of P does not average out; see
+gpu_helpers.p_rounding_bound)."""
 import math
 
 import numpy as np
@@ -28,8 +29,8 @@ def draw_case(i):
     N = int(rng.integers(1, n_max + 1))
     dtype = wl.FP16 if rng.random() < 0.5 else wl.BF16
     scale = float(rng.choice([1.0, -1.0]) * rng.uniform(0.3, 1.5) / math.sqrt(d))
-    kind = ["none", "causal", "window", "lens", "window+lens"][int(rng.integers(0, 5))]
-    window = None
+    kind = ["none", "causal", "window", "lens", "window+lens", "causal+lens"][int(rng.integers(0, 6))]
+    window = (-1, 0) if kind == "causal+lens" else None
     lens = None
     if "window" in kind:
         left = int(rng.integers(-1, N + 2))
