@@ -1,14 +1,16 @@
 """Grids whose workgroups take their (slice, query tile) in groups of slices.
 
 A launch takes the batch*head slices in groups whose query tiles fill one
-round of an XCD's resident workgroups (8 XCDs); with no mask whenever the grid
-has more slices than one group, under a mask only when the plain order would
-run at most 2 query tiles of a slice at once per XCD (slices >= 4 x resident
-per XCD).  The last group may hold fewer slices than the others.  With one
+round of an XCD's resident workgroups (8 XCDs); with no mask or a window
+bounded on both sides whenever the grid has more slices than one group, under
+other masks only when the plain order would run at most 2 query tiles of a
+slice at once per XCD (slices >= 4 x resident per XCD).  The last group may hold fewer slices than the others.  With one
 workgroup per compute unit (32 resident per XCD) these shapes give: 21 slices
 of 16 query tiles at d = 128, no mask (groups of 16 and 5); 36 slices of 8 at
 d = 64, no mask (32 and 4); 136 causal slices of 4 at d = 64 (64, 64, 8); 132
-padded causal slices of 5 at d = 96 (48, 48, 36).  O and LSE start as NaN, so
+padded causal slices of 5 at d = 96 (48, 48, 36); 36 slices of 8 at d = 64
+under a window bounded on both sides, which is grouped like no mask (32 and
+4).  O and LSE start as NaN, so
 a tile that no workgroup writes fails, and every element is compared with the
 fp64 oracle.
 """
@@ -27,6 +29,7 @@ CASES = [
     (4, 9, 2048, 64, wl.FP16, False, None),
     (8, 17, 1024, 64, wl.BF16, True, None),
     (4, 33, 640, 96, wl.FP16, False, (-1, 0, [640, 401, 77, 639])),
+    (4, 9, 2048, 64, wl.FP16, False, (100, 20, None)),
 ]
 
 
@@ -42,7 +45,9 @@ def test_grouped_order_writes_every_tile(gpu_device, case):
     lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=gpu_device)
     kw = {}
     if mask is not None:
-        kw = dict(window=mask[:2], key_lens=torch.tensor(mask[2], dtype=torch.int32, device=gpu_device))
+        kw = dict(window=mask[:2])
+        if mask[2] is not None:
+            kw["key_lens"] = torch.tensor(mask[2], dtype=torch.int32, device=gpu_device)
     forward(tq, tk, tv, scale=w.softmax_scale(), causal=causal, out=out, lse=lse, **kw)
     torch.cuda.synchronize(gpu_device)
     o = out.float().cpu().numpy().astype(np.float64)
