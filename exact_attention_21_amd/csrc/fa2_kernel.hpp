@@ -1056,12 +1056,31 @@ struct Fa2Fwd {
     }
   }
 
-  // Whether an unchecked run left some row of this lane with a row sum that
-  // is not finite.
+  // Whether an unchecked run left some row of this lane with a row sum, or an
+  // output accumulator, that is not finite.
+  //
+  // The row sum alone is enough for fp16: a finite sum means every packed
+  // probability is at most 65504, so |O| stays below l * max|v| < 2^62.  A
+  // bf16 probability can be as large as 2^128 (a score up to 128 base-2 units
+  // above the fixed base) with l still finite, and then sum p v overflows the
+  // fp32 accumulator as soon as |v| > 2^128 / p (e.g. p = 2^121 and |v| = 300);
+  // so for bf16 every accumulator is tested as well: x * 0 is 0 for a finite x
+  // and NaN for an infinite or NaN one.  This runs once per workgroup, after
+  // the last output MFMA (compiler-issued, so it orders the reads of O).
   static __device__ __forceinline__ bool pipe_failed(const State& st) {
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) bad |= !(st.l[qb] <= 3.0e38f);  // infinite or NaN
+    if constexpr (BF16) {
+      float z = 0.f;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z = __builtin_fmaf(st.o[qb][db][r], 0.f, z);
+      bad |= !(z == 0.f);
+    }
     return bad;
   }
   // Tiles first .. first+count-1 (count >= 1) through the pipeline, in groups

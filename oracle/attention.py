@@ -115,6 +115,17 @@ def attention_ref(q, k, v, scale: float, causal: bool, rows=None):
     return out, lse
 
 
+def _rescale_factor(m_old, m_new):
+    """Factor that moves sums taken against the exponent base m_old onto the
+    base m_new: exp(m_old - m_new), which multiplies the old O and l.
+
+    "FlashAttention-2 MMA 代码学习" (chuoer47.github.io) step 1 points out that
+    the paper's printed update has this factor inverted, and both pages' code
+    multiply the old O by exp(m_old - m_new).
+    """
+    return np.exp(m_old - m_new)
+
+
 def attention_online_merge(q, k, v, scale: float, causal: bool, block: int, reverse: bool = False,
                            window=None, key_lens=None):
     """The same result through the pages' online (m, l) merge over key blocks, in fp64.
@@ -168,7 +179,7 @@ def attention_online_merge(q, k, v, scale: float, causal: bool, block: int, reve
                 m_blk = s.max(axis=1)
                 m_new = np.maximum(m_run, m_blk)
                 base = np.where(np.isneginf(m_new), 0.0, m_new)
-                alpha = np.exp(m_run - base)
+                alpha = _rescale_factor(m_run, base)
                 p = np.exp(s - base[:, None])
                 l_run = alpha * l_run + p.sum(axis=1)
                 o_run = alpha[:, None] * o_run + p @ v[b, h, k0:k1]

@@ -1,5 +1,7 @@
 """Shared helpers for the GPU parity tests: move seeded storage arrays to the
 GPU, run the HIP library, and compare against the fp64 oracle."""
+import math
+
 import numpy as np
 
 from exact_attention_21_amd import workloads as wl
@@ -144,8 +146,10 @@ def assert_close_stress(o_gpu, lse_gpu, o_ref, lse_ref, p_bound, dtype, label=""
     net = float(np.max(d - half_ulp(o_ref, dtype) - p_bound))
     raw = float(np.max(d - p_bound))
     el = float(np.max(np.abs(lse_gpu - lse_ref)))
+    share = bound_share(o_gpu, o_ref, p_bound, dtype)
     print(f"  {label}: max|dO| = {float(d.max()):.3e}, beyond half-ulp and P-rounding bound = {net:.3e} "
-          f"(tol {to:.0e}; bound max {float(p_bound.max()):.2e}), max|dLSE| = {el:.3e} (tol {tl:.0e})", flush=True)
+          f"(tol {to:.0e}; bound max {float(p_bound.max()):.2e}, largest share of it needed {share:.2f}), "
+          f"max|dLSE| = {el:.3e} (tol {tl:.0e})", flush=True)
     assert net <= to, f"{label}: O error beyond output rounding and P rounding {net:.3e} > {to}"
     if dtype == wl.FP16:
         assert raw <= to, f"{label}: O error beyond P rounding {raw:.3e} > {to}"
@@ -163,3 +167,111 @@ def assert_close_masked(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label=""):
     if seen.any():
         assert_close(o_gpu[seen], lse_gpu[seen], o_ref[seen], lse_ref[seen], dtype, label)
     print(f"  {label}: {int(hidden.sum())} fully hidden rows", flush=True)
+
+
+def jump_inputs(B, H, N, d, dtype, seed, scale, jumps, v_spike=None):
+    """N(0,1) inputs with a few keys whose scores stand a fixed number of
+    base-2 units above zero for every query.
+
+    Every query gets q[0] = 4; key j = int(frac * N) of ``jumps`` = [(frac,
+    units), ...] becomes units / (4 * scale * log2(e)) in dimension 0 and 0
+    elsewhere, so its score is ``units`` (base 2) for every row, far above the
+    N(0,1) scores (a few units).  ``v_spike`` (if given) replaces those keys'
+    value rows by +-v_spike with random signs.  Returns the storage arrays and
+    the key indices."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    q[..., 0] = 4.0
+    c2 = float(np.float32(scale)) * math.log2(math.e)
+    idx = []
+    for frac, units in jumps:
+        j = min(N - 1, int(frac * N))
+        k[:, :, j, :] = 0.0
+        k[:, :, j, 0] = units / (4.0 * c2)
+        if v_spike is not None:
+            v[:, :, j, :] = v_spike * rng.choice([-1.0, 1.0], size=(B, H, d))
+        idx.append(j)
+    return tuple(wl.round_to_storage(x, dtype) for x in (q, k, v)) + (idx,)
+
+
+def jump_above_rest(q, k, dtype, scale, spikes, visible):
+    """Per row: the largest base-2 score among the spike keys it sees minus the
+    largest score among the other keys it sees (NaN for rows that see no spike
+    or nothing else).  ``visible`` is a [B, N, N] (or [N, N]) boolean mask."""
+    qf, kf = wl.to_float64(q, dtype), wl.to_float64(k, dtype)
+    s = (qf @ np.swapaxes(kf, -1, -2)) * float(np.float32(scale)) * math.log2(math.e)
+    vis = np.broadcast_to(visible if visible.ndim == 3 else visible[None], (s.shape[0],) + s.shape[2:])[:, None]
+    is_spike = np.zeros(s.shape[-1], dtype=bool)
+    is_spike[spikes] = True
+    top = np.where(vis & is_spike, s, -np.inf).max(axis=-1)
+    rest = np.where(vis & ~is_spike, s, -np.inf).max(axis=-1)
+    with np.errstate(invalid="ignore"):
+        out = top - rest
+    return np.where(np.isfinite(out), out, np.nan)
+
+
+def visible_matrix(N, causal=False, window=None, key_lens=None, B=1):
+    """[B, N, N] mask of the keys each query sees (the masks' definition, for
+    building test inputs; the oracle applies its own)."""
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    vis = np.ones((N, N), dtype=bool)
+    if causal:
+        vis &= j <= i
+    if window is not None:
+        if window[0] >= 0:
+            vis &= j >= i - window[0]
+        if window[1] >= 0:
+            vis &= j <= i + window[1]
+    out = np.broadcast_to(vis, (B, N, N)).copy()
+    if key_lens is not None:
+        for b, n_b in enumerate(key_lens):
+            out[b] &= j < min(max(int(n_b), 0), N)
+    return out
+
+
+def bound_share(o_gpu, o_ref, p_bound, dtype):
+    """Largest share of the P-rounding bound an element needed: the error
+    beyond half an output ulp and the plain tolerance, over the bound (0 when
+    the plain tolerance covers every element)."""
+    to = TOL[dtype][0]
+    extra = np.abs(o_gpu - o_ref) - half_ulp(o_ref, dtype) - to
+    with np.errstate(divide="ignore", invalid="ignore"):
+        share = np.where(extra > 0, extra / p_bound, 0.0)
+    return float(np.max(share)) if share.size else 0.0
+
+
+def oracle_all_rows(q64, k64, v64, scale, causal, chunk=2048):
+    """attention_ref over every row, evaluated as independent (batch, head,
+    row range) calls on a thread pool (BLAS held to one thread per call), so
+    that the full-size workloads finish in seconds; the pieces are the
+    oracle's own rows= evaluations, put back in place."""
+    import os
+    import time
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention_ref
+    B, H, N, d = q64.shape
+    o = np.empty((B, H, N, d))
+    lse = np.empty((B, H, N))
+    tasks = [(b, h, r0) for b in range(B) for h in range(H) for r0 in range(0, N, chunk)]
+
+    def one(t):
+        b, h, r0 = t
+        rows = np.arange(r0, min(N, r0 + chunk))
+        ob, lb = attention_ref(q64[b:b + 1, h:h + 1], k64[b:b + 1, h:h + 1], v64[b:b + 1, h:h + 1],
+                               scale, causal, rows=rows)
+        o[b, h, rows] = ob[0, 0]
+        lse[b, h, rows] = lb[0, 0]
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        for _ in ex.map(one, tasks):
+            pass
+    print(f"  oracle: {len(tasks)} pieces on {workers} threads, {time.perf_counter() - t0:.1f} s", flush=True)
+    return o, lse

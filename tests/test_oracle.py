@@ -11,7 +11,12 @@
 * the method's own algebra: the online (m, l) merge over key blocks of any
   size, in either order, reaches the same result;
 * planted mistakes in the oracle are caught by the brute-force and
-  closed-form pins.
+  closed-form pins: LSE in the wrong log base, a perturbed exponential, the
+  causal diagonal excluded, the scale dropped, keys weighted unevenly, the
+  scores transposed, the causal mask missing, the merge's rescale factor
+  inverted, and (masked oracle) window bounds off by
+  one, an exclusive right bound and the padding ignored;
+* the row-subset evaluation (rows=) equals the matching rows of the full one.
 """
 import json
 import math
@@ -255,6 +260,52 @@ def test_pins_catch_planted_mistakes(monkeypatch, mutant):
     assert caught >= 1, f"planted mistake {mutant} went unnoticed"
 
 
+# Mistakes in how the definition is assembled: the scores transposed (K Q^T
+# where Q K^T belongs, so each softmax runs over queries), and the causal mask
+# left out.
+CALL_MUTANTS = {
+    "scores_transposed": lambda q, k, v, s, c: attention_ref(k, q, v, s, c),
+    "causal_mask_missing": lambda q, k, v, s, c: attention_ref(q, k, v, s, False),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(CALL_MUTANTS))
+def test_pins_catch_planted_call_mistakes(mutant):
+    caught = 0
+    for check in (check_brute_force, check_closed_forms):
+        try:
+            check(CALL_MUTANTS[mutant])
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"planted mistake {mutant} went unnoticed"
+
+
+# A mistake in the online merge: the rescale factor inverted (the slip in the
+# paper's printed formula that the MMA notes point out).  (A base that is not
+# moved is no mistake: any base gives the same softmax while nothing
+# overflows, which is what the kernel's lazily moved base relies on.)
+MERGE_MUTANTS = {
+    "rescale_inverted": {"_rescale_factor": lambda m_old, m_new: np.exp(m_new - m_old)},
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MERGE_MUTANTS))
+def test_merge_pins_catch_planted_mistakes(monkeypatch, mutant):
+    for name, val in MERGE_MUTANTS[mutant].items():
+        monkeypatch.setattr(oracle_mod, name, val)
+    caught = 0
+    checks = (lambda: check_brute_force(lambda q, k, v, s, c: attention_online_merge(q, k, v, s, c, 3)),
+              lambda: check_closed_forms(lambda q, k, v, s, c: attention_online_merge(q, k, v, s, c, 1, True)),
+              lambda: test_online_merge_reaches_definition(7, False, False))
+    for check in checks:
+        try:
+            with np.errstate(all="ignore"):
+                check()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"planted mistake {mutant} went unnoticed"
+
+
 # ---- sliding-window and padding masks -------------------------------------
 
 from oracle import attention_ref_masked  # noqa: E402
@@ -402,3 +453,25 @@ def test_masked_pins_catch_planted_mistakes(monkeypatch, mutant):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught >= 1, f"planted mistake {mutant} went unnoticed"
+
+
+@pytest.mark.parametrize("mask", [(-1, -1, None), (40, 0, None), (100, 37, None), (0, 0, None), (31, -1, None),
+                                  (-1, -1, [600, 0]), (-1, 0, [333, 590]), (50, -1, [300, 17]), (7, 3, [1, 560])])
+def test_masked_rows_subset_matches_full(mask):
+    """attention_ref_masked(rows=...) returns exactly the matching rows of the
+    full evaluation: unsorted rows, rows on both sides of the 256-row block
+    boundaries, repeated rows and fully hidden rows (all padding, or a window
+    past the key length)."""
+    left, right, lens = mask
+    B, H, N, d = 2, 2, 600, 8
+    q, k, v = (_rand((B, H, N, d), s) for s in range(3))
+    O, L = attention_ref_masked(q, k, v, 0.3, left, right, lens)
+    rng = np.random.default_rng(17)
+    for rows in (np.array([599, 0, 255, 256, 257, 511, 512, 513, 300, 300, 1]),
+                 np.arange(250, 520), rng.choice(N, size=300, replace=False), np.array([42])):
+        Os, Ls = attention_ref_masked(q, k, v, 0.3, left, right, lens, rows=rows)
+        assert Os.shape == (B, H, rows.size, d) and Ls.shape == (B, H, rows.size)
+        np.testing.assert_allclose(Os, O[:, :, rows], rtol=0, atol=1e-13)
+        _assert_close_inf(Ls, L[:, :, rows], 1e-13, (mask, rows[:3]))
+    if lens is not None and 0 in lens:
+        assert np.all(np.isposinf(L[lens.index(0)]))

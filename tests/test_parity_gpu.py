@@ -10,7 +10,8 @@ import pytest
 
 from exact_attention_21_amd import workloads as wl
 from oracle import attention_ref
-from tests.gpu_helpers import TOL, assert_close, assert_close_stress, p_rounding_bound, run_gpu, spiky_inputs
+from tests.gpu_helpers import (TOL, assert_close, assert_close_stress, oracle_all_rows, p_rounding_bound,
+                               run_gpu, spiky_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,13 +23,24 @@ def sampled_rows(n, seed=0, edge=64, inner=128):
     return np.unique(rows)
 
 
-@pytest.mark.parametrize("w", wl.WORKLOADS + wl.HEADDIM_WORKLOADS,
-                         ids=[w.name for w in wl.WORKLOADS + wl.HEADDIM_WORKLOADS])
+@pytest.mark.parametrize("w", wl.WORKLOADS, ids=[w.name for w in wl.WORKLOADS])
+def test_workload_every_element(gpu_device, w):
+    """The five benchmark workloads at their full size, in the launch
+    configuration the benchmark times: every element of O and LSE against the
+    oracle, with the stated tolerances."""
+    q, k, v = wl.make_inputs(w, seed=0)
+    o, lse = run_gpu(q, k, v, w.dtype, w.softmax_scale(), w.causal, gpu_device)
+    print(f"  {w.name}: oracle over all {w.B * w.H * w.N} rows", flush=True)
+    o_ref, lse_ref = oracle_all_rows(wl.to_float64(q, w.dtype), wl.to_float64(k, w.dtype),
+                                     wl.to_float64(v, w.dtype), w.softmax_scale(), w.causal)
+    assert_close(o, lse, o_ref, lse_ref, w.dtype, w.name)
+
+
+@pytest.mark.parametrize("w", wl.HEADDIM_WORKLOADS, ids=[w.name for w in wl.HEADDIM_WORKLOADS])
 def test_full_size_workload_sampled_rows(gpu_device, w):
-    """Every workload at its full size, in the launch configuration the benchmark
-    times; the oracle evaluates a sample of rows (both ends of the sequence,
-    which include the ragged tail and the causal extremes, plus random rows) for
-    every batch and head."""
+    """The d = 512 and 1024 workloads at full size, in the benchmark's launch;
+    the oracle evaluates a sample of rows (both ends of the sequence, which
+    include the causal extremes, plus random rows) of every batch and head."""
     q, k, v = wl.make_inputs(w, seed=0)
     o, lse = run_gpu(q, k, v, w.dtype, w.softmax_scale(), w.causal, gpu_device)
     rows = sampled_rows(w.N)
@@ -70,14 +82,23 @@ def test_ragged_lengths(gpu_device, n, d, dtype, causal):
 
 @pytest.mark.parametrize("scale", [0.0, -0.125, 1.0, 1e-3])
 @pytest.mark.parametrize("causal", [False, True])
-def test_scale_values(gpu_device, scale, causal):
+@pytest.mark.parametrize("d,dtype", [(64, wl.FP16), (64, wl.BF16), (128, wl.BF16), (256, wl.BF16), (32, wl.FP16)])
+def test_scale_values(gpu_device, scale, causal, d, dtype):
     """Scale 0 gives the mean of the visible values; a negative scale is applied
-    before the row max."""
-    w = wl.Workload("s", 1, 2, 300, 64, wl.FP16, causal)
+    before the row max.  A scale well above 1/sqrt(d) (1.0 at d >= 64: scores
+    of standard deviation sqrt(d)) puts a row's weight on one to three keys,
+    where the one rounding of P to the input type does not average out, so O
+    there allows the P-rounding bound as the other stress inputs do."""
+    w = wl.Workload("s", 1, 2, 300, d, dtype, causal)
     q, k, v = wl.make_inputs(w, seed=11)
-    o, lse = run_gpu(q, k, v, wl.FP16, scale, causal, gpu_device)
-    o_ref, lse_ref = attention_ref(*(wl.to_float64(x, wl.FP16) for x in (q, k, v)), scale, causal)
-    assert_close(o, lse, o_ref, lse_ref, wl.FP16, f"scale={scale} causal={causal}")
+    o, lse = run_gpu(q, k, v, dtype, scale, causal, gpu_device)
+    o_ref, lse_ref = attention_ref(*(wl.to_float64(x, dtype) for x in (q, k, v)), scale, causal)
+    label = f"d{d} {dtype} scale={scale} causal={causal}"
+    if abs(scale) * math.sqrt(d) > 1.5:
+        bound = p_rounding_bound(q, k, v, o_ref, dtype, scale, causal)
+        assert_close_stress(o, lse, o_ref, lse_ref, bound, dtype, label)
+    else:
+        assert_close(o, lse, o_ref, lse_ref, dtype, label)
 
 
 @pytest.mark.parametrize("dtype", [wl.FP16, wl.BF16])
@@ -141,8 +162,9 @@ STRESS_DIMS = (32, 64, 96, 128, 256, 512, 1024)
 @pytest.mark.parametrize("dtype", [wl.FP16, wl.BF16])
 @pytest.mark.parametrize("causal", [False, True])
 def test_late_score_jumps_rebase(gpu_device, d, dtype, causal):
-    """Score jumps of several hundred (base-2 units) half-way through and near
-    the end of the keys; every row with a jump visible must be rescaled.  The
+    """Score jumps half-way through and near the end of the keys (keys scaled
+    x12: on these seeds about 60 to 80 base-2 units above the first tile's row
+    max); every row with a jump visible must be rescaled.  The
     jumps put most of a row's weight on one or two keys, so the O check allows
     the rounding of P on top of the tolerance (p_rounding_bound)."""
     B, H, N = 1, 2, 1500
