@@ -169,7 +169,7 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 // which is followed by softmax work before the next output MFMA), dependent
 // MFMAs of one accumulator are always separated by other MFMAs, and the other
 // readers of O (the rebase path, the compiler-issued output MFMA of the last
-// tile) come after an explicit wait (see pipe_rebase, run_pipe).
+// tile) come after an explicit wait (settle_o).
 template <bool BF16>
 __device__ __forceinline__ void mfma32_acc_agpr(f32x16& c, const u32x4& a, const u32x4& b) {
   if constexpr (BF16)
@@ -810,6 +810,19 @@ struct Fa2Fwd {
     }
   }
 
+  // Wait states after the inline-asm output MFMAs before anything the
+  // compiler issues reads their accumulators (the compiler's hazard checks do
+  // not see inside inline asm): 20 wait states cover the result latency of a
+  // 32x32x16 MFMA, and the empty statements after them claim to modify every
+  // accumulator, so that no read of O is scheduled above the wait.
+  static __device__ __forceinline__ void settle_o(State& st) {
+    asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(st.o[qb][db]));
+  }
+
   // Value of `x` held by lane `src` (every lane reads).
   static __device__ __forceinline__ float lane_value(float x, int src) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
@@ -821,7 +834,7 @@ struct Fa2Fwd {
                                                      u32x4 (&pb)[QB][KB][2], f32x4 (&ct)[QB], float (&lt)[QB]) {
     // With O in AGPRs the output MFMAs are inline asm the compiler does not
     // track: keep the reads of O below an MFMA result latency after them.
-    if constexpr (O_AGPR) asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
+    if constexpr (O_AGPR) settle_o(st);
     const float ninf = -__builtin_inff();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -1103,7 +1116,14 @@ struct Fa2Fwd {
       st.lc[qb][0] = st.lc[qb][1] = st.lf[qb] = 0.f;
       st.ls[qb] = f32x4{};
 #pragma unroll
-      for (int db = 0; db < DB; ++db) st.o[qb][db] = f32x16{};
+      for (int db = 0; db < DB; ++db) {
+        st.o[qb][db] = f32x16{};
+        // The first reader of these zeros is an inline-asm output MFMA, for
+        // which the compiler inserts no wait states after its own AGPR
+        // writes: materialise them here, a whole prologue ahead, instead of
+        // letting the writes sink next to that MFMA.
+        if constexpr (O_AGPR) asm volatile("" : "+a"(st.o[qb][db]));
+      }
     }
     Scores sc[2];
     u32x4 pb[2][QB][KB][2];
@@ -1146,7 +1166,7 @@ struct Fa2Fwd {
     // an MFMA the compiler issues: an MFMA result latency after the inline-asm
     // output MFMAs it accumulates onto.
     static_assert(PIPE_G % 2 == 0, "the last tile of a group has odd parity");
-    if constexpr (O_AGPR) asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
+    if constexpr (O_AGPR) settle_o(st);
     if (count2 % PIPE_RING == 0)
       pv(cx.lds + (PIPE_RING - 1) * TILEB, cx.off, pb[1], st.o);
     else

@@ -108,6 +108,16 @@ struct Fa2Wide {
     float lu;         // bf16: the same for the unrounded ones
   };
 
+  // Wait states after the inline-asm output MFMAs before the compiler reads
+  // their accumulators: an MFMA result latency, then empty statements that
+  // claim to modify every accumulator, so no read of O is scheduled above the
+  // wait (see Fa2Fwd::settle_o).
+  static __device__ __forceinline__ void settle_o(State& st) {
+    asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
+#pragma unroll
+    for (int ob = 0; ob < OB; ++ob) asm volatile("" : "+a"(st.o[ob]));
+  }
+
   static __device__ __forceinline__ void dma16(const u32x4& rsrc, const lds_char* dst, int voffset) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
     asm volatile("s_mov_b32 m0, %0\n s_nop 0\n buffer_load_dwordx4 %1, %2, 0 offen lds"
@@ -170,7 +180,7 @@ struct Fa2Wide {
     const bool grow = mt > st.m + kMargin;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
       // O was last written by output MFMAs the compiler does not track.
-      asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
+      settle_o(st);
       const float m_new = grow ? mt : st.m;
       const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 from the unseen base
 #pragma unroll
@@ -370,7 +380,7 @@ struct Fa2Wide {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue: O / l, stores; LSE from the pair's first wave.
-    asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
+    settle_o(st);
     float lo, hi;
     halves(st.lr, lo, hi);
     const float l_tot = lo + hi;
