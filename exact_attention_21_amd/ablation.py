@@ -37,7 +37,11 @@ VARIANTS = [
     ("no_kv_swizzle", {"FA2_KV_SWIZZLE": 0}, "K and V tiles stored row-major in LDS (no chunk permutation)"),
     ("checked_only", {"FA2_UNCHECKED_RUN": 0}, "every tile's row sums checked; no fixed-base unchecked run"),
     ("no_split_kv", {"FA2_SPLIT_KV": 0}, "4 waves per workgroup with one K/V stream (no split-KV wave groups)"),
-    ("deep_ring", {"FA2_DEEP_RING": 1}, "8-slot K/V rings, one barrier per 4 tiles (instead of 4 slots, per 2)"),
+    ("deep_ring", {"FA2_KV_SLOTS": 8}, "8-slot K/V rings, one barrier per 4 tiles (instead of 4 slots, per 2)"),
+    ("two_slot_ring", {"FA2_KV_SLOTS": 2},
+     "2-slot K/V rings, one barrier per tile: the nearest form of the single K and V buffer"),
+    ("padded_rows", {"FA2_KV_PAD": 1},
+     "K/V rows padded in LDS (K +16 B, V +64 B), filled through VGPRs; no swizzle, no direct-to-LDS loads"),
     ("no_xcd_groups", {"FA2_XCD_GROUPS": 0}, "work order over all heads at once (no XCD-sized head groups)"),
     ("no_w4_bound", {"FA2_W4_TWO_PER_SIMD": 0},
      "d = 64 4-wave form without the two-waves-per-SIMD register bound"),
@@ -45,7 +49,7 @@ VARIANTS = [
 # Switches that only move data in LDS, change the barrier cadence, the order
 # of the workgroups or the register budget: the arithmetic is the same, so the
 # output must be bit-identical.
-LAYOUT_ONLY = {"no_kv_swizzle", "deep_ring", "no_xcd_groups", "no_w4_bound"}
+LAYOUT_ONLY = {"no_kv_swizzle", "deep_ring", "two_slot_ring", "padded_rows", "no_xcd_groups", "no_w4_bound"}
 
 
 def lib_path(name: str) -> str:
@@ -53,11 +57,19 @@ def lib_path(name: str) -> str:
     return LIB_PATH if name == "shipped" else variant_path(name)
 
 
+# Head dims the variant builds compile (FA2_DIMS bit mask: d = 64 and 128,
+# those of the ablation workloads), which keeps each build short.
+VARIANT_DIMS = 0x0A
+
+
 def build_all() -> None:
+    from concurrent.futures import ThreadPoolExecutor
+
     from exact_attention_21_amd._build import build_variant
-    for name, defines, _ in VARIANTS:
-        if defines is not None:
-            print(build_variant(name, defines, verbose=True), flush=True)
+    todo = [(name, {**defines, "FA2_DIMS": VARIANT_DIMS}) for name, defines, _ in VARIANTS if defines is not None]
+    with ThreadPoolExecutor(4) as ex:
+        for path in ex.map(lambda t: build_variant(t[0], t[1]), todo):
+            print(path, flush=True)
 
 
 def main() -> int:

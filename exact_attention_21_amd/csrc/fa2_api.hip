@@ -16,7 +16,20 @@
 #include "fa2_kernel.hpp"
 #include "fa2_wide.hpp"
 
+// Head dims compiled into this build: a bit mask (bit 0: d = 32, then 64, 96,
+// 128, 256, 512, 1024), all of them unless FA2_DIMS says otherwise.  Builds of
+// the library with a design switch flipped, made to measure that switch,
+// compile only the head dims they are measured on; a head dim left out is
+// rejected as unsupported.
+#ifndef FA2_DIMS
+#define FA2_DIMS 0x7f
+#endif
+
 namespace {
+
+constexpr bool built_d(int64_t d) {
+  return (FA2_DIMS >> (d == 32 ? 0 : d == 64 ? 1 : d == 96 ? 2 : d == 128 ? 3 : d == 256 ? 4 : d == 512 ? 5 : 6)) & 1;
+}
 
 // Tile configuration per head dimension: keys per K/V tile, waves per
 // workgroup, 32-row query blocks per wave, split-KV wave groups (2: two
@@ -162,6 +175,7 @@ fa2_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, 
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_UNSUPPORTED_DTYPE;
   if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256 && d != 512 && d != 1024)
     return FA2_ERR_UNSUPPORTED_HEAD_DIM;
+  if (!built_d(d)) return FA2_ERR_UNSUPPORTED_HEAD_DIM;
   if (B < 1 || H < 1 || N < 1) return FA2_ERR_BAD_SHAPE;
   const int64_t br = rows_per_wg(d);
   // One head's slice is addressed with signed 32-bit byte offsets, including
@@ -225,7 +239,9 @@ hipError_t launch_wide(const fa2::Params& p, int64_t grid, hipStream_t stream) {
 
 template <int D, bool BF16, int MASK>
 hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream, bool split) {
-  if constexpr (D >= 512) {
+  if constexpr (!built_d(D)) {
+    return hipErrorInvalidValue;  // not reached: check_shape rejects it
+  } else if constexpr (D >= 512) {
     return launch_wide<D, BF16, MASK>(p, grid, stream);
   } else if constexpr (has_split_form(D)) {
     constexpr TileCfg s = cfg_for(D, true), u = cfg_for(D, false);

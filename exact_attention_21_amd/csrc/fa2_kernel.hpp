@@ -217,7 +217,15 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 // Design switches.  The library's own build leaves each at its default, the
 // shipped design; a build that flips one measures what that choice is worth.
 //   FA2_KV_SWIZZLE     1: the K/V chunk permutations below; 0: plain row-major tiles.
-//   FA2_DEEP_RING      0: 4-slot K/V rings; 1: 8 slots where they fit the LDS.
+//   FA2_KV_SLOTS       4: 4-slot K/V rings, one barrier per 2 tiles; 8: 8 slots
+//                      where they fit the LDS, one barrier per 4 tiles; 2: 2
+//                      slots, one barrier per tile (the nearest form of a
+//                      single K and a single V buffer that this schedule,
+//                      which holds K(j+1) and V(j-1) at once, can run).
+//   FA2_KV_PAD         0: tiles filled by direct-to-LDS loads into the
+//                      swizzled layouts below; 1: tiles loaded into VGPRs and
+//                      stored to LDS rows padded by 16 bytes (K) and 64 bytes
+//                      (V), no swizzle.
 //   FA2_UNCHECKED_RUN  1: fixed-base unchecked first run (not at d = 128
 //                      under the general mask);
 //                      0: the checked pipeline only.
@@ -231,8 +239,11 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 #ifndef FA2_KV_SWIZZLE
 #define FA2_KV_SWIZZLE 1
 #endif
-#ifndef FA2_DEEP_RING
-#define FA2_DEEP_RING 0
+#ifndef FA2_KV_SLOTS
+#define FA2_KV_SLOTS 4
+#endif
+#ifndef FA2_KV_PAD
+#define FA2_KV_PAD 0
 #endif
 #ifndef FA2_UNCHECKED_RUN
 #define FA2_UNCHECKED_RUN 1
@@ -275,7 +286,7 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 //    rows (d = 96) they start at bank groups 0, 12, 8, 4: no swizzle needed.
 template <int D>
 __device__ __forceinline__ int kslot(int row, int c) {
-  if constexpr (!FA2_KV_SWIZZLE) return c;
+  if constexpr (!FA2_KV_SWIZZLE || (FA2_KV_PAD && D <= 128)) return c;
   if constexpr (D == 32) return c ^ ((row >> 2) & 3);
   if constexpr (D == 64) return c ^ ((row >> 1) & 7);
   if constexpr (D == 96) return (c + ((row >> 2) & 3)) % 12;
@@ -284,12 +295,12 @@ __device__ __forceinline__ int kslot(int row, int c) {
 // Logical chunk stored at position `slot` of row r (the inverse of kslot).
 template <int D>
 __device__ __forceinline__ int klog(int row, int slot) {
-  if constexpr (D == 96 && FA2_KV_SWIZZLE) return (slot + 12 - ((row >> 2) & 3)) % 12;
+  if constexpr (D == 96 && FA2_KV_SWIZZLE && !FA2_KV_PAD) return (slot + 12 - ((row >> 2) & 3)) % 12;
   return kslot<D>(row, slot);  // the XOR rules are involutions
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int row) {
-  if constexpr (!FA2_KV_SWIZZLE || D == 32 || D == 96) return 0;
+  if constexpr (!FA2_KV_SWIZZLE || (FA2_KV_PAD && D <= 128) || D == 32 || D == 96) return 0;
   if constexpr (D == 64) return ((row >> 1) & 1) << 2;
   return (row & 3) << 2;
 }
@@ -309,13 +320,24 @@ struct Fa2Fwd {
   static constexpr bool GENERAL = MASK == kMaskGeneral;
   static_assert(KVG == 1 || (KVG == 2 && NW == 8), "split-KV runs two groups of 4 waves");
   static constexpr int THREADS = NW * 64;
+  static constexpr int ROWB = D * 2;             // bytes per K/V row in global memory
+  static constexpr int GTILEB = BC * ROWB;       // bytes per K (or V) tile in global memory
+  // LDS row strides: rows back to back (the swizzled layouts), or padded
+  // rows (FA2_KV_PAD): K + 16 bytes, so that 16 consecutive rows start in 16
+  // different 16-byte bank groups, and V + 64 bytes, so that the 4 rows of a
+  // transposing read do.  (Padding applies up to d = 128: a padded d = 256 V
+  // ring would outgrow the 64 KiB that a ds immediate offset reaches.)
+  static constexpr bool KV_PAD = FA2_KV_PAD && D <= 128;
+  static constexpr int KROW = KV_PAD ? ROWB + 16 : ROWB;
+  static constexpr int VROW = KV_PAD ? ROWB + 64 : ROWB;
+  static constexpr int TILEK = BC * KROW;        // LDS bytes per K tile slot
+  static constexpr int TILEV = BC * VROW;        // LDS bytes per V tile slot
   // Pipelined schedule: K and V tiles each in a ring of PIPE_RING LDS slots,
   // one barrier per PIPE_RING / 2 sub-iterations.  (An 8-slot ring must fit
   // the 160 KiB LDS and keep each ring within the 64 KiB of ds immediates.)
-  static constexpr int DEEP_RING_BYTES = 8 * BC * D * 2;
   static constexpr bool DEEP_RING_FITS =
-      DEEP_RING_BYTES <= 65536 && KVG * 2 * DEEP_RING_BYTES <= 160 * 1024;
-  static constexpr int PIPE_RING = FA2_DEEP_RING && DEEP_RING_FITS ? 8 : 4;
+      8 * TILEK <= 65536 && 8 * TILEV <= 65536 && KVG * 8 * (TILEK + TILEV) <= 160 * 1024;
+  static constexpr int PIPE_RING = FA2_KV_SLOTS == 2 ? 2 : (FA2_KV_SLOTS == 8 && DEEP_RING_FITS ? 8 : 4);
   static constexpr int PIPE_G = PIPE_RING / 2;
   static constexpr int QW = 32 * QB;             // query rows per wave
   // KVG = 2 (split-KV): two groups of 4 waves own the same query rows and
@@ -330,13 +352,11 @@ struct Fa2Fwd {
   static constexpr int KB = BC / 32;             // 32-key blocks per tile
   static constexpr int DB = D / 32;              // 32-row blocks of O^T
   static constexpr int DK = D / 16;              // 16-deep k-steps of S^T = K Q^T
-  static constexpr int ROWB = D * 2;             // bytes per K/V row
-  static constexpr int TILEB = BC * ROWB;        // bytes per K (or V) tile
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int CPT = BC * CPR / STAGERS; // chunks per thread per tile (each of K, V)
   // One K/V stream in LDS: a ring of PIPE_RING tiles each of K and V.
   static constexpr int SLOTS = PIPE_RING;
-  static constexpr int STREAMB = 2 * SLOTS * TILEB;
+  static constexpr int STREAMB = SLOTS * (TILEK + TILEV);
   // Split-KV merge area: per group-1 lane, O^T (QB*DB*16 floats) then m, l
   // and the unrounded bf16 row sums.
   static constexpr int MERGE_FLOATS = QB * DB * 16 + 3 * QB;
@@ -348,7 +368,7 @@ struct Fa2Fwd {
   // compile-time offset that must fit the instruction's 16-bit immediate; the
   // start of the V ring is kept in the lanes' V offsets, so each ring (K, V)
   // only needs its own 64 KiB of immediates.
-  static constexpr int VBASE = SLOTS * TILEB;
+  static constexpr int VBASE = SLOTS * TILEK;
   static_assert(STREAMB - VBASE <= 65536 && VBASE <= 65536, "LDS image must fit the ds immediate offset");
 
   typedef __attribute__((address_space(3))) char lds_char;
@@ -357,7 +377,9 @@ struct Fa2Fwd {
   struct LdsOffsets {
     int k[DK];     // K^T operand of k-step ks for key block 0 (block kb adds kb*32 rows)
     int v[DB];     // V^T operand rows 32*db..: keys 4h+e of a 16-key group (+8 rows: second read)
-    int vst[CPT];  // store of chunk j through VGPRs, V layout (zeroing a V slot)
+    int vst[CPT];  // store of chunk j through VGPRs, V layout (zeroing a V slot; FA2_KV_PAD: staging)
+    int kst[CPT];  // the same, K layout (FA2_KV_PAD: staging)
+    int gst[CPT];  // global byte offset of chunk j in row-major order (FA2_KV_PAD)
     int gdk[CPT];  // global byte offset of the K chunk a direct-to-LDS load lands at linear slot j
     int gdv[CPT];  // the same for the V layout
     int dma;       // this wave's first linear slot (bytes) of a direct-to-LDS tile load
@@ -377,7 +399,7 @@ struct Fa2Fwd {
       for (int g = 0; g < DK; g += KG) {
         u32x4 a[KG];
 #pragma unroll
-        for (int i = 0; i < KG; ++i) a[i] = *(const __attribute__((address_space(3))) u32x4*)(sk + off.k[g + i] + kb * 32 * ROWB);
+        for (int i = 0; i < KG; ++i) a[i] = *(const __attribute__((address_space(3))) u32x4*)(sk + off.k[g + i] + kb * 32 * KROW);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -418,14 +440,14 @@ struct Fa2Fwd {
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int rows = (kb * 32 + 16 * u) * ROWB;
+        const int rows = (kb * 32 + 16 * u) * VROW;
 #pragma unroll
         for (int g = 0; g < DB; g += VG) {
           u32x4 a[VG];
 #pragma unroll
           for (int i = 0; i < VG; ++i) {
             const s16x4 va = lds_read_tr16(sv + off.v[g + i] + rows);
-            const s16x4 vb = lds_read_tr16(sv + off.v[g + i] + rows + 8 * ROWB);
+            const s16x4 vb = lds_read_tr16(sv + off.v[g + i] + rows + 8 * VROW);
             a[i][0] = __builtin_bit_cast(u32x2, va)[0];
             a[i][1] = __builtin_bit_cast(u32x2, va)[1];
             a[i][2] = __builtin_bit_cast(u32x2, vb)[0];
@@ -490,7 +512,7 @@ struct Fa2Fwd {
       const int row = lane & 31;
       const int sbase = grp * STREAMB;  // this wave's K/V stream in LDS
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks) off.k[ks] = sbase + row * ROWB + (kslot<D>(row, 2 * ks + half) << 4);
+      for (int ks = 0; ks < DK; ++ks) off.k[ks] = sbase + row * KROW + (kslot<D>(row, 2 * ks + half) << 4);
       // V^T transposed reads: lane group g = lane/16 serves A rows (dims)
       // 16*(g%2) + lane%16 for key half g/2; as a source, lane 16g + 4e + u
       // reads key row 4*(g/2) + e at dims 16*(g%2) + 4u .. +3.  Rows 32kb+16u
@@ -500,19 +522,22 @@ struct Fa2Fwd {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int dim = 32 * db + 16 * (g & 1) + 4 * (lane & 3);
-        off.v[db] = sbase + VBASE + key * ROWB + (((dim >> 3) ^ swz_v<D>(key)) << 4) + ((dim & 7) << 1);
+        off.v[db] = sbase + VBASE + key * VROW + (((dim >> 3) ^ swz_v<D>(key)) << 4) + ((dim & 7) << 1);
       }
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         const int c = stid + STAGERS * j;
         const int r = c / CPR, col = c % CPR;
-        off.vst[j] = sbase + r * ROWB + ((col ^ swz_v<D>(r)) << 4);
+        off.vst[j] = sbase + r * VROW + ((col ^ swz_v<D>(r)) << 4);
+        off.kst[j] = sbase + r * KROW + (col << 4);
         // A direct-to-LDS load writes lane L's 16 bytes at the wave's base +
         // 16 L, i.e. linear slot c (row r, position col); that position of the
         // K layout holds global chunk klog(r, col), of the V layout chunk
         // col ^ swz_v(r) (an involution).
         off.gdk[j] = (r * D + klog<D>(r, col) * 8) * 2;
         off.gdv[j] = (r * D + (col ^ swz_v<D>(r)) * 8) * 2;
+        // VGPR-staged loads (FA2_KV_PAD): lane chunk c in global order.
+        off.gst[j] = (r * D + col * 8) * 2;
       }
       off.dma = __builtin_amdgcn_readfirstlane(sbase + (stid & ~63) * 16);
     }
@@ -541,7 +566,8 @@ struct Fa2Fwd {
     const uint32_t kv_bytes = (uint32_t)klen * D * 2;
     const int late = GENERAL ? max(0, qw0 + QW - 1 - wl) / BC : -1;
     const Ctx cx{rsrc_words(p.k, slice * 2, kv_bytes), rsrc_words(p.v, slice * 2, kv_bytes), ones_operand(lane),
-                 ones_index(lane), lds, off, p.scale_log2, lane, tid, qw0, klen, wl, wr, late};
+                 ones_index(lane), lds, off, p.scale_log2, lane, tid, qw0, klen, wl, wr, late,
+                 make_rsrc((const char*)p.k + slice * 2, kv_bytes), make_rsrc((const char*)p.v + slice * 2, kv_bytes)};
     if constexpr (SPLIT) {
       // Group 0 takes key tiles [tfirst, tfirst + T0) with T0 even, group 1
       // the next T0; tiles past the end are fully masked.  Both run T0
@@ -627,6 +653,7 @@ struct Fa2Fwd {
     int n;       // keys present: N, or the sequence's key length
     int wl, wr;  // window bounds (general mask; kNoBound: none)
     int late;    // general mask: last tile in which a row of the wave can see its first key
+    __amdgpu_buffer_rsrc_t rk, rv;  // K and V buffer resources for the VGPR-staged loads (FA2_KV_PAD)
     // A wave takes part in tile j if some key of it is visible to some of its rows.
     __device__ __forceinline__ bool active(int j) const {
       if constexpr (CAUSAL) return j * BC <= qw0 + QW - 1;
@@ -663,14 +690,29 @@ struct Fa2Fwd {
   template <int BASE>
   static __device__ __forceinline__ void stage_dma_k(const Ctx& cx, int tile) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) dma16(cx.wk, cx.lds + BASE + cx.off.dma + STAGERS * 16 * i, cx.off.gdk[i] + tile * TILEB);
+    for (int i = 0; i < CPT; ++i) dma16(cx.wk, cx.lds + BASE + cx.off.dma + STAGERS * 16 * i, cx.off.gdk[i] + tile * GTILEB);
   }
   template <int BASE>
   static __device__ __forceinline__ void stage_dma_v(const Ctx& cx, int tile) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) dma16(cx.wv, cx.lds + BASE + cx.off.dma + STAGERS * 16 * i, cx.off.gdv[i] + tile * TILEB);
+    for (int i = 0; i < CPT; ++i) dma16(cx.wv, cx.lds + BASE + cx.off.dma + STAGERS * 16 * i, cx.off.gdv[i] + tile * GTILEB);
   }
   static __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+  // FA2_KV_PAD: one K or V tile into VGPRs (chunks in row-major order; rows
+  // past the keys present read as zeros) and from there into its padded LDS
+  // slot at BASE.
+  static __device__ __forceinline__ void fetch_tile(const __amdgpu_buffer_rsrc_t& rsrc, const Ctx& cx, int tile,
+                                                    u32x4 (&reg)[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) reg[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, cx.off.gst[i] + tile * GTILEB, 0, 0);
+  }
+  template <int BASE, bool ISV>
+  static __device__ __forceinline__ void commit_tile(const Ctx& cx, const u32x4 (&reg)[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      *(__attribute__((address_space(3))) u32x4*)(cx.lds + BASE + (ISV ? cx.off.vst[i] : cx.off.kst[i])) = reg[i];
+  }
 
   // ---- Pipelined schedule ------------------------------------------------
   // Iteration j issues the MFMAs of S(j+1) = K(j+1) Q^T and of
@@ -702,12 +744,12 @@ struct Fa2Fwd {
 
 
   static __device__ __forceinline__ u32x4 kfrag(const lds_char* sk, const LdsOffsets& off, int kb, int ks) {
-    return *(const __attribute__((address_space(3))) u32x4*)(sk + off.k[ks] + kb * 32 * ROWB);
+    return *(const __attribute__((address_space(3))) u32x4*)(sk + off.k[ks] + kb * 32 * KROW);
   }
   static __device__ __forceinline__ u32x4 vfrag(const lds_char* sv, const LdsOffsets& off, int kb, int u, int db) {
-    const int rows = (kb * 32 + 16 * u) * ROWB;
+    const int rows = (kb * 32 + 16 * u) * VROW;
     const s16x4 va = lds_read_tr16(sv + off.v[db] + rows);
-    const s16x4 vb = lds_read_tr16(sv + off.v[db] + rows + 8 * ROWB);
+    const s16x4 vb = lds_read_tr16(sv + off.v[db] + rows + 8 * VROW);
     u32x4 a;
     a[0] = __builtin_bit_cast(u32x2, va)[0];
     a[1] = __builtin_bit_cast(u32x2, va)[1];
@@ -902,8 +944,8 @@ struct Fa2Fwd {
   static __device__ __forceinline__ void pipe_body(const Ctx& cx, State& st, Scores (&sc)[2],
                                                    u32x4 (&pb)[2][QB][KB][2], f32x4 (&ct)[QB], float (&lt)[QB]) {
     constexpr int B = S4 % 2;
-    const lds_char* sk = cx.lds + ((S4 + 1) % PIPE_RING) * TILEB;                          // K(j+1)
-    const lds_char* sv = cx.lds + ((S4 + PIPE_RING - 1) % PIPE_RING) * TILEB;  // V(j-1) (V ring base in off.v)
+    const lds_char* sk = cx.lds + ((S4 + 1) % PIPE_RING) * TILEK;                          // K(j+1)
+    const lds_char* sv = cx.lds + ((S4 + PIPE_RING - 1) % PIPE_RING) * TILEV;  // V(j-1) (V ring base in off.v)
     constexpr int NMF = KB * DK * QB;               // MFMAs of each product (S and P V alike)
     constexpr int NSLOT = 2 * NMF;
     constexpr int NPAIR = QB * KB * 8;              // probability pairs of tile j
@@ -1045,16 +1087,36 @@ struct Fa2Fwd {
   template <int H, int I>
   static __device__ __forceinline__ void pipe_group_loads(const Ctx& cx, int first, int r) {
     if constexpr (I < PIPE_G) {
-      stage_dma_k<((H * PIPE_G + PIPE_G + 1 + I) % PIPE_RING) * TILEB>(cx, first + r + PIPE_G + 1 + I);
-      stage_dma_v<(PIPE_RING + (H * PIPE_G + PIPE_G - 1 + I) % PIPE_RING) * TILEB>(cx, first + r + PIPE_G - 1 + I);
+      stage_dma_k<((H * PIPE_G + PIPE_G + 1 + I) % PIPE_RING) * TILEK>(cx, first + r + PIPE_G + 1 + I);
+      stage_dma_v<VBASE + ((H * PIPE_G + PIPE_G - 1 + I) % PIPE_RING) * TILEV>(cx, first + r + PIPE_G - 1 + I);
       pipe_group_loads<H, I + 1>(cx, first, r);
+    }
+  }
+  // FA2_KV_PAD: sub-iteration I of the group first loads its share of the
+  // next group's tiles (K(r+G+1+I), V(r+G-1+I)) into VGPRs and stores them to
+  // their padded LDS slots after its own work.
+  template <int H, int I, bool CHECKED>
+  static __device__ __forceinline__ void pipe_group_subs_staged(const Ctx& cx, State& st, Scores (&sc)[2],
+                                                                u32x4 (&pb)[2][QB][KB][2], int first, int r) {
+    if constexpr (I < PIPE_G) {
+      u32x4 kreg[CPT], vreg[CPT];
+      fetch_tile(cx.rk, cx, first + r + PIPE_G + 1 + I, kreg);
+      fetch_tile(cx.rv, cx, first + r + PIPE_G - 1 + I, vreg);
+      pipe_sub<H * PIPE_G + I, CHECKED>(cx, st, sc, pb, first + r + I);
+      commit_tile<((H * PIPE_G + PIPE_G + 1 + I) % PIPE_RING) * TILEK, false>(cx, kreg);
+      commit_tile<VBASE + ((H * PIPE_G + PIPE_G - 1 + I) % PIPE_RING) * TILEV, true>(cx, vreg);
+      pipe_group_subs_staged<H, I + 1, CHECKED>(cx, st, sc, pb, first, r);
     }
   }
   template <int H, bool CHECKED>
   static __device__ __forceinline__ void pipe_group(const Ctx& cx, State& st, Scores (&sc)[2],
                                                     u32x4 (&pb)[2][QB][KB][2], int first, int r) {
-    pipe_group_loads<H, 0>(cx, first, r);
-    pipe_group_subs<H, 0, CHECKED>(cx, st, sc, pb, first, r);
+    if constexpr (KV_PAD) {
+      pipe_group_subs_staged<H, 0, CHECKED>(cx, st, sc, pb, first, r);
+    } else {
+      pipe_group_loads<H, 0>(cx, first, r);
+      pipe_group_subs<H, 0, CHECKED>(cx, st, sc, pb, first, r);
+    }
     dma_wait();
     __syncthreads();
   }
@@ -1063,8 +1125,18 @@ struct Fa2Fwd {
   template <int I>
   static __device__ __forceinline__ void pipe_prologue_loads(const Ctx& cx, int first) {
     if constexpr (I <= PIPE_G) {
-      stage_dma_k<I * TILEB>(cx, first + I);
-      if constexpr (I <= PIPE_G - 2) stage_dma_v<(PIPE_RING + I) * TILEB>(cx, first + I);
+      if constexpr (KV_PAD) {
+        u32x4 reg[CPT];
+        fetch_tile(cx.rk, cx, first + I, reg);
+        commit_tile<I * TILEK, false>(cx, reg);
+        if constexpr (I <= PIPE_G - 2) {
+          fetch_tile(cx.rv, cx, first + I, reg);
+          commit_tile<VBASE + I * TILEV, true>(cx, reg);
+        }
+      } else {
+        stage_dma_k<I * TILEK>(cx, first + I);
+        if constexpr (I <= PIPE_G - 2) stage_dma_v<VBASE + I * TILEV>(cx, first + I);
+      }
       pipe_prologue_loads<I + 1>(cx, first);
     }
   }
@@ -1135,7 +1207,7 @@ struct Fa2Fwd {
       for (int kb = 0; kb < KB; ++kb) pb[1][qb][kb][0] = pb[1][qb][kb][1] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < CPT; ++i) stg[i] = u32x4{0u, 0u, 0u, 0u};
-    stage_store_v<(2 * PIPE_RING - 1) * TILEB>(cx, stg);
+    stage_store_v<VBASE + (PIPE_RING - 1) * TILEV>(cx, stg);
     pipe_prologue_loads<0>(cx, first);
     dma_wait();
     __syncthreads();
@@ -1162,15 +1234,22 @@ struct Fa2Fwd {
       pipe_group<0, CHECKED>(cx, st, sc, pb, first, r);
       if (r + PIPE_G < count2) pipe_group<1, CHECKED>(cx, st, sc, pb, first, r + PIPE_G);
     }
-    // P V of the last tile (relative index count2-1: odd, V slot (count2-1) % ring),
-    // an MFMA the compiler issues: an MFMA result latency after the inline-asm
-    // output MFMAs it accumulates onto.
-    static_assert(PIPE_G % 2 == 0, "the last tile of a group has odd parity");
+    // P V of the last tile (relative index count2-1, V slot (count2-1) % ring,
+    // probabilities in set (count2-1) % 2), an MFMA the compiler issues: an
+    // MFMA result latency after the inline-asm output MFMAs it accumulates onto.
     if constexpr (O_AGPR) settle_o(st);
-    if (count2 % PIPE_RING == 0)
-      pv(cx.lds + (PIPE_RING - 1) * TILEB, cx.off, pb[1], st.o);
-    else
-      pv(cx.lds + (PIPE_G - 1) * TILEB, cx.off, pb[1], st.o);
+    if constexpr (PIPE_G % 2 == 0) {  // count2 is even: the last index is odd
+      if (count2 % PIPE_RING == 0)
+        pv(cx.lds + (PIPE_RING - 1) * TILEV, cx.off, pb[1], st.o);
+      else
+        pv(cx.lds + (PIPE_G - 1) * TILEV, cx.off, pb[1], st.o);
+    } else {  // one sub-iteration per group, two slots
+      static_assert(PIPE_RING == 2, "odd groups only with a 2-slot ring");
+      if (count2 % 2 == 0)
+        pv(cx.lds + TILEV, cx.off, pb[1], st.o);
+      else
+        pv(cx.lds, cx.off, pb[0], st.o);
+    }
     // Each lane keeps the whole sum of its query (lane%32); with LSE_FP32 the
     // unrounded sum (the lane halves' shares added) goes to lf.
 #pragma unroll
