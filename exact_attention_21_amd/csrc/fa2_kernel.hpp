@@ -361,7 +361,14 @@ struct Fa2Fwd {
   // and the unrounded bf16 row sums.
   static constexpr int MERGE_FLOATS = QB * DB * 16 + 3 * QB;
   static constexpr int MERGE_BYTES = SPLIT ? (NW / 2) * 64 * MERGE_FLOATS * 4 : 0;
-  static constexpr int LDS_BYTES = STREAMS * STREAMB > MERGE_BYTES ? STREAMS * STREAMB : MERGE_BYTES;
+  // Output staging (store_output): 32 * QB rows of O per wave; with the
+  // split-KV merge, each wave of group 0 in its own merge slot.
+  static constexpr int OUT_WAVE_BYTES = 32 * QB * D * 2;
+  static constexpr int MERGE_SLOT_BYTES = 64 * MERGE_FLOATS * 4;
+  static constexpr int OUT_BYTES = SPLIT ? QWAVES * (MERGE_SLOT_BYTES > OUT_WAVE_BYTES ? MERGE_SLOT_BYTES : OUT_WAVE_BYTES)
+                                         : NW * OUT_WAVE_BYTES;
+  static constexpr int RING_MERGE_BYTES = STREAMS * STREAMB > MERGE_BYTES ? STREAMS * STREAMB : MERGE_BYTES;
+  static constexpr int LDS_BYTES = RING_MERGE_BYTES > OUT_BYTES ? RING_MERGE_BYTES : OUT_BYTES;
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert((BC * CPR) % STAGERS == 0 && CPT >= 1, "staging split");
   // Every LDS access in the tile loop is a lane base register plus a
@@ -582,36 +589,13 @@ struct Fa2Fwd {
       }
       merge_groups(cx, st, grp);
       if (grp != 0) return;  // group 1 handed its state to group 0
+      store_output(p, st, lds, ro, rl, qw0, lane, qwave);
     } else {
       run_pipe<!OPTIMISTIC>(cx, st, tfirst, ntiles);
       if constexpr (OPTIMISTIC) {
         if (__syncthreads_or(pipe_failed(st))) run_pipe<true>(cx, st, tfirst, ntiles);
       }
-    }
-
-    // Epilogue: each lane holds its row's whole sum; divide once, store.
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qrow = qw0 + 32 * qb + (lane & 31);
-      const float l_tot = st.l[qb];
-      const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 w;
-          w[0] = pack2<BF16>(st.o[qb][db][4 * g + 0] * inv, st.o[qb][db][4 * g + 1] * inv);
-          w[1] = pack2<BF16>(st.o[qb][db][4 * g + 2] * inv, st.o[qb][db][4 * g + 3] * inv);
-          const int dim = 32 * db + 8 * g + 4 * half;
-          __builtin_amdgcn_raw_buffer_store_b64(w, ro, (qrow * D + dim) * 2, 0, 0);
-        }
-      }
-      if (half == 0) {
-        const float l_lse = LSE_FP32 ? st.lf[qb] : l_tot;
-        const float lse = (l_lse > 0.f) ? (st.m[qb] + __builtin_amdgcn_logf(l_lse)) * 0.69314718055994531f
-                                        : __builtin_inff();
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qrow * 4, 0, 0);
-      }
+      store_output(p, st, lds, ro, rl, qw0, lane, wave);
     }
   }
 
@@ -640,6 +624,71 @@ struct Fa2Fwd {
   // first tile: its fixed base is taken at the first tile in which it sees a
   // key (fix_late_bases).
   static constexpr bool OPTIMISTIC = FA2_UNCHECKED_RUN && !(D == 128 && GENERAL);
+
+  // Epilogue: O / l and LSE of one wave's rows (32 * QB), rounded and stored.
+  // A lane holds 4 consecutive dims of one row per register group, so stores
+  // straight from the accumulators would write 8 bytes to each of 32 rows per
+  // instruction; the rows go through the wave's own LDS region instead and
+  // leave as 16-byte pieces of whole rows, 64 lanes covering 1 KiB of O
+  // (measured against the direct stores: +3% to +4% at d = 128 and 256, whose
+  // workgroups of a round all finish together and store at once; +1% at
+  // d = 64).  With the split-KV merge a wave takes the merge slot it has just
+  // read (group 1 has left); otherwise every wave first passes a barrier, so
+  // that no wave still reads a K/V tile.  The 16-byte chunks of a row sit at
+  // chunk ^ (row mod 16) (power-of-two chunk counts; 12 chunks, d = 96:
+  // plain) so that the 32 rows of a half-wave's 8-byte writes spread over the
+  // banks.
+  static __device__ __forceinline__ void store_output(const Params& p, const State& st, lds_char* lds,
+                                                      __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
+                                                      int qw0, int lane, int slot) {
+    constexpr int WROWS = 32 * QB;
+    constexpr int WBYTES = OUT_WAVE_BYTES;
+    constexpr int SWZ = (CPR & (CPR - 1)) == 0 ? (CPR < 16 ? CPR - 1 : 15) : 0;
+    constexpr int MSLOT = MERGE_SLOT_BYTES;
+    static_assert(!SPLIT || MSLOT % 16 == 0, "merge slots stay 16-byte aligned");
+    int region;
+    if constexpr (SPLIT) {
+      region = slot * (MSLOT > WBYTES ? MSLOT : WBYTES);
+    } else {
+      __syncthreads();
+      region = slot * WBYTES;
+    }
+    lds_char* ob = lds + region;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = 32 * qb + (lane & 31);
+      const float l_tot = st.l[qb];
+      const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 w;
+          w[0] = pack2<BF16>(st.o[qb][db][4 * g + 0] * inv, st.o[qb][db][4 * g + 1] * inv);
+          w[1] = pack2<BF16>(st.o[qb][db][4 * g + 2] * inv, st.o[qb][db][4 * g + 3] * inv);
+          // dims 32 db + 8 g + 4 half .. +3: chunk 4 db + g, second half of it for half = 1
+          *(__attribute__((address_space(3))) u32x2*)(ob + row * ROWB + (((4 * db + g) ^ (row & SWZ)) << 4) +
+                                                       8 * half) = w;
+        }
+      }
+      if (half == 0) {
+        const float l_lse = LSE_FP32 ? st.lf[qb] : l_tot;
+        const float lse = (l_lse > 0.f) ? (st.m[qb] + __builtin_amdgcn_logf(l_lse)) * 0.69314718055994531f
+                                        : __builtin_inff();
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, (qw0 + row) * 4, 0, 0);
+      }
+    }
+    // Whole rows out: chunk c of the wave's rows is row c / CPR, chunk c % CPR;
+    // rows past N are dropped by the range-checked resource.
+#pragma unroll
+    for (int i = 0; i < WROWS * CPR / 64; ++i) {
+      const int c = i * 64 + lane;
+      const int row = c / CPR, col = c % CPR;
+      const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(ob + row * ROWB + ((col ^ (row & SWZ)) << 4));
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, ((qw0 + row) * D + col * 8) * 2, 0, 0);
+    }
+  }
 
   // Loop-invariant context.
   struct Ctx {
@@ -1141,31 +1190,23 @@ struct Fa2Fwd {
     }
   }
 
-  // Whether an unchecked run left some row of this lane with a row sum, or an
-  // output accumulator, that is not finite.
+  // Whether an unchecked run overflowed, or may have, in some row of this
+  // lane: its row sum (of the rounded probabilities) is above the limit.
   //
-  // The row sum alone is enough for fp16: a finite sum means every packed
-  // probability is at most 65504, so |O| stays below l * max|v| < 2^62.  A
-  // bf16 probability can be as large as 2^128 (a score up to 128 base-2 units
-  // above the fixed base) with l still finite, and then sum p v overflows the
-  // fp32 accumulator as soon as |v| > 2^128 / p (e.g. p = 2^121 and |v| = 300);
-  // so for bf16 every accumulator is tested as well: x * 0 is 0 for a finite x
-  // and NaN for an infinite or NaN one.  This runs once per workgroup, after
-  // the last output MFMA (compiler-issued, so it orders the reads of O).
+  // fp16: any finite sum will do.  It means every packed probability is at
+  // most 65504, so |O| stays below l * max|v| < 2^62.  bf16: a probability can
+  // be as large as 2^128 (a score up to 128 base-2 units above the fixed base)
+  // with the sum still finite, and then sum p v overflows the fp32
+  // accumulator as soon as |v| > 2^128 / p (e.g. p = 2^121 and |v| = 300).
+  // Accepting the run only while l <= 2^64 bounds every accumulator by
+  // 2^64 * max|v|, finite for any |v| < 2^64; a larger sum (a score more than
+  // 64 base-2 units above a row's first tile) sends the workgroup through the
+  // checked run, whose probabilities are at most 2^15.
+  static constexpr float kUncheckedSumLimit = BF16 ? 0x1p64f : 3.0e38f;
   static __device__ __forceinline__ bool pipe_failed(const State& st) {
     bool bad = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) bad |= !(st.l[qb] <= 3.0e38f);  // infinite or NaN
-    if constexpr (BF16) {
-      float z = 0.f;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) z = __builtin_fmaf(st.o[qb][db][r], 0.f, z);
-      bad |= !(z == 0.f);
-    }
+    for (int qb = 0; qb < QB; ++qb) bad |= !(st.l[qb] <= kUncheckedSumLimit);  // also NaN
     return bad;
   }
   // Tiles first .. first+count-1 (count >= 1) through the pipeline, in groups
