@@ -25,7 +25,11 @@
  * Numerics: scores, row statistics and the output accumulator are fp32; the
  * probabilities are rounded (to nearest even) to `dtype` before the second
  * matrix product, as are the outputs.  `scale` may be any finite float,
- * including 0 and negative values.
+ * including 0 and negative values.  The exponent base of a row is moved
+ * lazily (a probability may exceed 1 by a bounded factor before the row is
+ * rescaled), so the fp32 accumulator of O holds at most 2^64 (bf16) or
+ * N * 2^16 (fp16) times max|V|: O is finite for finite inputs, given every
+ * |V| below 2^64 for bf16 (fp16 values are below 2^16 anyway).
  *
  * Ownership: the caller allocates and owns all five buffers.  The library
  * allocates no device memory, keeps no pointer after the call returns and has
