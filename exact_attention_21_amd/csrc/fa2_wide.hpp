@@ -379,21 +379,47 @@ struct Fa2Wide {
     // workgroup's LDS is released.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // Epilogue: O / l, stores; LSE from the pair's first wave.
+    // Epilogue: O / l, stores; LSE from the pair's first wave.  As in the
+    // main kernel, the rows go out through LDS (the ring is free once every
+    // wave has passed the barrier below) as 16-byte pieces of whole runs of
+    // the row instead of 8-byte pieces of 32 rows: each wave stages half of
+    // its output blocks at a time in a 16 KiB region of its own (32 rows x
+    // OB/2 blocks x 64 bytes, chunks at chunk ^ (row mod 16)).  Measured
+    // against the direct stores: +1% to +4% at d = 512 and 1024.
     settle_o(st);
     float lo, hi;
     halves(st.lr, lo, hi);
     const float l_tot = lo + hi;
     const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+    __syncthreads();
+    constexpr int HB = OB / 2;            // output blocks per half
+    constexpr int RB = HB * 64;           // staged bytes per row
+    static_assert(NW * 32 * RB <= RING * SLOTB, "output staging fits the ring");
+    lds_char* ob_lds = lds + wave * 32 * RB;
+    const int srow = lane & 31;
 #pragma unroll
-    for (int ob = 0; ob < OB; ++ob) {
-      const int dim0 = (ob / VB) * CW + 32 * (pw * VB + ob % VB);
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = pack2<BF16>(st.o[ob][4 * g + 0] * inv, st.o[ob][4 * g + 1] * inv);
-        w[1] = pack2<BF16>(st.o[ob][4 * g + 2] * inv, st.o[ob][4 * g + 3] * inv);
-        __builtin_amdgcn_raw_buffer_store_b64(w, ro, (qrow * D + dim0 + 8 * g + 4 * half) * 2, 0, 0);
+      for (int i = 0; i < HB; ++i) {
+        const int ob = h * HB + i;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 w;
+          w[0] = pack2<BF16>(st.o[ob][4 * g + 0] * inv, st.o[ob][4 * g + 1] * inv);
+          w[1] = pack2<BF16>(st.o[ob][4 * g + 2] * inv, st.o[ob][4 * g + 3] * inv);
+          // dims 8 g + 4 half .. +3 of block ob: chunk 4 i + g, second half of it for half = 1
+          *(__attribute__((address_space(3))) u32x2*)(ob_lds + srow * RB + (((4 * i + g) ^ (srow & 15)) << 4) +
+                                                       8 * half) = w;
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < 32 * HB * 4 / 64; ++it) {
+        const int c = it * 64 + lane;
+        const int row = c / (HB * 4), col = c % (HB * 4);
+        const int ob = h * HB + col / 4;
+        const int dim = (ob / VB) * CW + 32 * (pw * VB + ob % VB) + 8 * (col % 4);
+        const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(ob_lds + row * RB + ((col ^ (row & 15)) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, ((qw0 + row) * D + dim) * 2, 0, 0);
       }
     }
     float l_lse = l_tot;
