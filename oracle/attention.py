@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the FlashAttention-2 forward pass (test infrastructure).
+"""fp64 CPU oracle for the FlashAttention-2 forward pass and its gradients
+(test infrastructure).
 
 This module is test infrastructure.  Only ``tests/``, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py`` may import it.  It shares no code,
@@ -17,7 +18,10 @@ Sources (page title, then the part of the page followed):
   §15.4.3: masking happens before the softmax; the note after the §15.3
   skeleton: with sliding-window or padding masks a row can meet only hidden keys
   in its first tiles, which is what the -inf guards (exponent base 0 while the
-  row max is -inf, O = 0 and LSE = +inf when l = 0) are there for.
+  row max is -inf, O = 0 and LSE = +inf when l = 0) are there for; the
+  chapter's closing summary: the backward recomputes S and P from Q, K and
+  the stored statistic instead of reading them (attention_bwd_ref gives the
+  gradients that computation reaches).
 
 Precision: every step is fp64.  Inputs are the already-rounded fp16/bf16 values,
 upcast exactly by the caller.  ``scale`` is rounded to fp32 first, because that
@@ -27,7 +31,10 @@ Every function here is pinned by tests that do not re-use its own formulas
 (tests/test_oracle.py): a pure-Python brute force on tiny shapes, closed forms
 derived by hand (tests/golden/closed_forms.json), invariants (key shift,
 key/value permutation), special cases (one key, identical keys, scale 0) and a
-library routine (torch scaled_dot_product_attention in fp64 on the CPU).
+library routine (torch scaled_dot_product_attention in fp64 on the CPU).  The
+backward is pinned in tests/test_oracle_bwd.py by finite differences of the
+forward oracle, a hand-derived two-key closed form, special cases,
+invariants and torch autograd in fp64.
 """
 from __future__ import annotations
 
@@ -236,3 +243,60 @@ def attention_ref_masked(q, k, v, scale: float, window_left: int, window_right: 
                 out[b, h, r0:r0 + idx.size, :] = np.where(seen[:, None], (p @ v[b, h]) / safe_l[:, None], 0.0)
                 lse[b, h, r0:r0 + idx.size] = np.where(seen, m + np.log(safe_l), np.inf)
     return out, lse
+
+
+def _row_delta(do, o):
+    """Delta_i = sum_d dO_id O_id: the row term the softmax backward subtracts."""
+    return (do * o).sum(axis=1, keepdims=True)
+
+
+def _score_grad(p, dp, delta):
+    """dS = P * (dP - Delta): the softmax backward, row by row."""
+    return p * (dp - delta)
+
+
+def attention_bwd_ref(q, k, v, do, scale: float, causal: bool):
+    """Gradients of sum(dO * O) with O = attention_ref(q, k, v), in fp64.
+
+    The backward of the definition, written out (chain rule through the
+    softmax; "第 15 章 FA2 前向：Tiling 与 Online Softmax", closing summary:
+    the backward recomputes S and P from the stored statistic and loops over
+    key tiles outside, query tiles inside; the arithmetic here is the
+    definition those steps reach):
+
+      S = scale * Q K^T (hidden keys -inf),  P = softmax_rows(S) = exp(S - LSE)
+      dV = P^T dO
+      dP = dO V^T
+      Delta_i = sum_j P_ij dP_ij = sum_d dO_id O_id
+      dS = P * (dP - Delta)          (elementwise; Delta broadcast over keys)
+      dQ = scale * dS K,   dK = scale * dS^T Q
+
+    Returns (dQ, dK, dV), fp64 [B, H, N, d].  ``scale`` is rounded to fp32
+    first, as in the forward.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    if q.ndim != 4 or any(x.shape != q.shape for x in (k, v, do)):
+        raise ValueError("q, k, v, do must share one [B, H, N, d] shape")
+    b_, h_, n, d = q.shape
+    c = float(np.float32(scale))
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(q)
+    dv = np.zeros_like(q)
+    for b in range(b_):
+        for h in range(h_):
+            s = (q[b, h] @ k[b, h].T) * c
+            if causal:
+                s = np.where(np.arange(n)[None, :] <= np.arange(n)[:, None], s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            p = e / e.sum(axis=1, keepdims=True)
+            o = p @ v[b, h]
+            dv[b, h] = p.T @ do[b, h]
+            dp = do[b, h] @ v[b, h].T
+            ds = _score_grad(p, dp, _row_delta(do[b, h], o))
+            dq[b, h] = c * (ds @ k[b, h])
+            dk[b, h] = c * (ds.T @ q[b, h])
+    return dq, dk, dv
