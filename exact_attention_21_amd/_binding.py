@@ -25,7 +25,7 @@ FA2_ERR_OVERLAP = 7
 FA2_ERR_HIP = 8
 
 # Every symbol include/fa2.h declares.
-EXPORTED = ("fa2_fwd", "fa2_fwd_masked", "fa2_status_string", "fa2_launch_info")
+EXPORTED = ("fa2_fwd", "fa2_fwd_masked", "fa2_bwd", "fa2_status_string", "fa2_launch_info")
 
 _lock = threading.Lock()
 _lib = None
@@ -47,6 +47,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.fa2_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
                                    i64, i64, vp, ctypes.c_int, vp]
     lib.fa2_fwd_masked.restype = ctypes.c_int
+    lib.fa2_bwd.argtypes = [vp] * 10 + [i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa2_bwd.restype = ctypes.c_int
     lib.fa2_status_string.argtypes = [ctypes.c_int]
     lib.fa2_status_string.restype = ctypes.c_char_p
     lib.fa2_launch_info.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
@@ -81,6 +83,13 @@ def fa2_fwd_masked(Q: int, K: int, V: int, O: int, LSE: int, B: int, H: int, N: 
     """Same arguments and status as the C function; pointers are integers (key_lens may be None)."""
     return library().fa2_fwd_masked(Q, K, V, O, LSE, B, H, N, d, scale, int(window_left), int(window_right),
                                     key_lens, int(dtype), stream)
+
+
+def fa2_bwd(Q: int, K: int, V: int, O: int, dO: int, LSE: int, dQ: int, dK: int, dV: int, workspace: int,
+            B: int, H: int, N: int, d: int, scale: float, is_causal: int, dtype: int, stream: int) -> int:
+    """Same arguments and status as the C function; pointers are integers."""
+    return library().fa2_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, B, H, N, d, scale, int(is_causal),
+                             int(dtype), stream)
 
 
 def fa2_status_string(status: int) -> str:

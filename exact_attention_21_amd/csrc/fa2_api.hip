@@ -13,6 +13,7 @@
 #include <mutex>
 #include <unordered_map>
 
+#include "fa2_bwd.hpp"
 #include "fa2_kernel.hpp"
 #include "fa2_wide.hpp"
 
@@ -323,6 +324,61 @@ fa2_status_t checked_launch(const void* Q, const void* K, const void* V, void* O
   return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
 }
 
+// ---- backward ----------------------------------------------------------
+// Waves per workgroup of the two backward kernels (32 rows each).
+constexpr int kBwdWaves = 4;
+
+template <int D, bool BF16, bool CAUSAL>
+hipError_t launch_bwd(const fa2::BwdParams& base, hipStream_t stream) {
+  using KQ = fa2::Fa2BwdQ<D, kBwdWaves, BF16, CAUSAL>;
+  using KKV = fa2::Fa2BwdKV<D, kBwdWaves, BF16, CAUSAL>;
+  auto kq = fa2::fa2_bwd_q_kernel<D, kBwdWaves, BF16, CAUSAL>;
+  auto kkv = fa2::fa2_bwd_kv_kernel<D, kBwdWaves, BF16, CAUSAL>;
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute((const void*)kq, hipFuncAttributeMaxDynamicSharedMemorySize, KQ::LDS_BYTES);
+    if (attr_err == hipSuccess)
+      attr_err = hipFuncSetAttribute((const void*)kkv, hipFuncAttributeMaxDynamicSharedMemorySize, KKV::LDS_BYTES);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  // dQ and Delta first: the dK/dV kernel reads Delta.
+  fa2::BwdParams p = base;
+  p.n_tiles = (p.n + KQ::BQ - 1) / KQ::BQ;
+  hipLaunchKernelGGL(kq, dim3((unsigned)((int64_t)p.n_tiles * p.bh)), dim3(KQ::THREADS), KQ::LDS_BYTES, stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  p.n_tiles = (p.n + KKV::BK - 1) / KKV::BK;
+  hipLaunchKernelGGL(kkv, dim3((unsigned)((int64_t)p.n_tiles * p.bh)), dim3(KKV::THREADS), KKV::LDS_BYTES, stream,
+                     p);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool CAUSAL>
+hipError_t launch_bwd_d(int64_t d, const fa2::BwdParams& p, hipStream_t stream) {
+  return d == 64 ? launch_bwd<64, BF16, CAUSAL>(p, stream) : launch_bwd<128, BF16, CAUSAL>(p, stream);
+}
+
+// Rows per workgroup of either backward kernel (the grid-size limit).
+constexpr int64_t kBwdRows = 32 * kBwdWaves;
+static_assert(fa2::Fa2BwdQ<64, kBwdWaves, false, false>::BQ == kBwdRows &&
+                  fa2::Fa2BwdKV<64, kBwdWaves, false, false>::BK == kBwdRows,
+              "backward tiles");
+static_assert(kBwdRows <= kPadRows && fa2::Fa2BwdQ<64, kBwdWaves, false, false>::BC <= kPadRows &&
+                  fa2::Fa2BwdKV<64, kBwdWaves, false, false>::BQ <= kPadRows,
+              "backward rows past N stay within the padded slice");
+
+fa2_status_t bwd_check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+  if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_UNSUPPORTED_DTYPE;
+  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_HEAD_DIM;
+  if (B < 1 || H < 1 || N < 1) return FA2_ERR_BAD_SHAPE;
+  if ((N + kPadRows) * d * 2 >= (int64_t(1) << 31)) return FA2_ERR_BAD_SHAPE;
+  if (B > (int64_t(1) << 31) / H) return FA2_ERR_BAD_SHAPE;
+  const int64_t tiles = (N + kBwdRows - 1) / kBwdRows;
+  if (tiles > ((int64_t(1) << 31) - 1) / (B * H)) return FA2_ERR_BAD_SHAPE;
+  return FA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -379,6 +435,54 @@ fa2_status_t fa2_fwd_masked(const void* Q, const void* K, const void* V, void* O
   if (no_left && window_right == 0) mask = fa2::kMaskCausal;
   return checked_launch(Q, K, V, O, LSE, B, H, N, d, scale, mask, window_left, window_right, key_lens, dtype,
                         stream);
+}
+
+fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                     void* dQ, void* dK, void* dV, float* workspace, int64_t B, int64_t H, int64_t N, int64_t d,
+                     float scale, int is_causal, int dtype, void* stream) {
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV || !workspace) return FA2_ERR_NULL_POINTER;
+  const fa2_status_t st = bwd_check_shape(B, H, N, d, dtype);
+  if (st != FA2_OK) return st;
+  if (!std::isfinite(scale)) return FA2_ERR_BAD_SCALE;
+  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)dO | (uintptr_t)dQ | (uintptr_t)dK |
+       (uintptr_t)dV) & 15u)
+    return FA2_ERR_MISALIGNED;
+  if (((uintptr_t)LSE | (uintptr_t)workspace) & 3u) return FA2_ERR_MISALIGNED;
+  const size_t tb = (size_t)(B * H * N * d) * 2;
+  const size_t rb = (size_t)(B * H * N) * 4;
+  const void* ins[6] = {Q, K, V, O, dO, LSE};
+  const size_t in_bytes[6] = {tb, tb, tb, tb, tb, rb};
+  const void* outs[4] = {dQ, dK, dV, workspace};
+  const size_t out_bytes[4] = {tb, tb, tb, rb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA2_ERR_OVERLAP;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA2_ERR_OVERLAP;
+  }
+  fa2::BwdParams p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.dout = dO;
+  p.lse = LSE;
+  p.delta = workspace;
+  p.dq = dQ;
+  p.dk = dK;
+  p.dv = dV;
+  p.n = (int)N;
+  p.bh = (int)(B * H);
+  p.n_tiles = 0;  // set per kernel
+  p.scale = scale;
+  p.c2 = scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err;
+  if (dtype == FA2_DTYPE_BF16)
+    err = is_causal ? launch_bwd_d<true, true>(d, p, s) : launch_bwd_d<true, false>(d, p, s);
+  else
+    err = is_causal ? launch_bwd_d<false, true>(d, p, s) : launch_bwd_d<false, false>(d, p, s);
+  return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
 }
 
 }  // extern "C"

@@ -1,0 +1,501 @@
+// FlashAttention-2 backward kernels for gfx950 (CDNA4), wave64 MFMA.
+//
+// What they compute (per batch b, head h), given the forward's O and LSE and
+// the output gradient dO, with S = scale * Q K^T (causal: key j hidden from
+// query i when j > i) and P = exp(S - LSE) (the forward's probabilities,
+// recomputed):
+//   dV = P^T dO
+//   dP = dO V^T,   Delta_i = sum_d dO[i,d] O[i,d],   dS = P * (dP - Delta)
+//   dQ = scale * dS K,   dK = scale * dS^T Q
+// Method: "第 15 章 FA2 前向：Tiling 与 Online Softmax" (yangyitao.com), the
+// chapter's closing paragraph on the backward: S and P are recomputed from Q,
+// K and the stored LSE instead of being read, and the loop runs over key
+// tiles outside and query tiles inside; the arithmetic is the chain rule
+// through the softmax of the forward's definition ("FlashAttention-2 MMA
+// 代码学习" (chuoer47.github.io), step 0).
+//
+// gfx950 design (where it departs from the pages' outline):
+//   * The pages accumulate dQ with atomic adds from every key tile.  Here two
+//     kernels share the work without atomics, and the results do not depend
+//     on the order in which workgroups run:
+//       - Fa2BwdQ (query rows stationary, key tiles streamed): Delta of its
+//         rows (written to a workspace), then S^T, dP^T, dS^T and
+//         dQ^T += K^T dS^T.  Launched first.
+//       - Fa2BwdKV (key rows stationary, query tiles streamed, the pages'
+//         loop order): S, dP, dS, dV^T += dO^T P and dK^T += Q^T dS.
+//     S and dP are computed in both, 7 matrix products in all instead of 5.
+//   * Every product is v_mfma_f32_32x32x16_{f16,bf16} with fp32 accumulation.
+//     The operand that stays in registers (Q^T and dO^T in Fa2BwdQ, K^T and
+//     V^T in Fa2BwdKV) is the B operand of the score products, so the score
+//     accumulators hold one row (or key) per lane and 16 keys (or queries)
+//     in registers; registers 8u..8u+7 of such an accumulator are, packed to
+//     16 bits, the B operand of the gradient product for k-step u, exactly as
+//     the forward feeds P to its output product.  The A operands of the
+//     gradient products (K^T, dO^T, Q^T) are read from LDS transposed, with
+//     ds_read_b64_tr_b16.
+//   * Streamed tiles go from global memory straight into a 2-slot LDS ring
+//     (buffer_load ... lds), one barrier per tile.  A streamed tile is read
+//     both as plain rows and transposed; its 16-byte chunks are permuted
+//     per row (bwd_swz) so that both reads are free of LDS bank conflicts.
+//   * Rows past N load as zeros from range-checked buffer resources and
+//     contribute exactly zero; out-of-range stores are dropped by the same
+//     check.
+//
+// Precision: S, dP, Delta and the gradient accumulators are fp32; P and dS
+// are rounded (to nearest even) to the input dtype before the products that
+// take them, as the forward rounds P; the gradients are rounded to the input
+// dtype once, at the end.
+#pragma once
+
+#include "fa2_kernel.hpp"
+
+namespace fa2 {
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;  // natural-log LSE of the forward, [B*H, N]
+  float* delta;      // workspace [B*H, N]: written by Fa2BwdQ, read by Fa2BwdKV
+  void* dq;
+  void* dk;
+  void* dv;
+  int n;        // sequence length N
+  int bh;       // B * H
+  int n_tiles;  // stationary tiles per (batch*head) slice of the kernel launched
+  float scale;  // softmax scale (any finite value)
+  float c2;     // scale * log2(e): scores to the base-2 exponent domain
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Position of 16-byte chunk c of row r of a streamed tile: c ^ bwd_swz(r).
+// A tile is read two ways:
+//  * plain: 16 lanes read 16 consecutive rows at one chunk, so the 16 chunks
+//    must fall in distinct 16-byte bank groups of the 256-byte LDS line;
+//  * transposed (ds_read_b64_tr_b16): 32 lanes read 4 consecutive rows 4a+e
+//    (e = 0..3) at one aligned group of 4 chunks, so those 16 chunks must too.
+// d = 64 (8 chunks, two rows per line, the line half given by r%2): bits 0-1
+// of the XOR walk the four aligned 4-row groups of 16 rows and bit 2 follows
+// r/2 % 2, which puts rows 4a and 4a+2 (same line half) in different 4-chunk
+// halves.  d = 128 (16 chunks, one row per line): bits 2-3 follow r%4 (the
+// four rows of a transposed read in four different 4-chunk groups) and bits
+// 0-1 follow r/4 % 4, so 16 consecutive rows take 16 distinct values.  Both
+// depend on r only through r%16.
+template <int D>
+__device__ __forceinline__ int bwd_swz(int row) {
+  static_assert(D == 64 || D == 128, "backward head dims");
+  if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  return ((row & 3) << 2) | ((row >> 2) & 3);
+}
+
+template <int D, bool BF16>
+struct BwdBase {
+  static constexpr int ROWB = D * 2;  // bytes per row
+  static constexpr int CPR = D / 8;   // 16-byte chunks per row
+  static constexpr int DK = D / 16;   // 16-deep k-steps over the head dim
+  static constexpr int DB = D / 32;   // 32-dim blocks of a gradient accumulator
+  typedef __attribute__((address_space(3))) char lds_char;
+
+  static __device__ __forceinline__ u32x4 lds16(const lds_char* p) {
+    return *(const __attribute__((address_space(3))) u32x4*)p;
+  }
+  static __device__ __forceinline__ f32x4 lds_f4(const lds_char* p) {
+    return *(const __attribute__((address_space(3))) f32x4*)p;
+  }
+  static __device__ __forceinline__ s16x4 tr16(const lds_char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  }
+
+  // Plain read: lane L reads row L%32 at chunk 2ks + L/32 (dims 16ks + 8(L/32)
+  // .. +7): the A operand [32 rows x 16 dims] of a score product.  Rows of
+  // later 32-row blocks are added as immediates (multiples of 16 rows keep
+  // the swizzle).
+  static __device__ __forceinline__ int plain_off(int lane, int ks) {
+    const int row = lane & 31;
+    return row * ROWB + (((2 * ks + (lane >> 5)) ^ bwd_swz<D>(row)) << 4);
+  }
+  // Transposed read of dims 32db.. of 16 rows: lane group g = L/16 serves A
+  // rows (dims) 16(g%2) + L%16; as a source, lane 16g + 4e + u reads row
+  // 4(g/2) + e (+8 for the second read) at dims 32db + 16(g%2) + 4u .. +3.
+  // The two reads give the A operand [32 dims x 16 rows] with its k index
+  // ordered rows {4h + e, 8 + 4h + e} for lane half h, the order of
+  // registers 8u..8u+7 of a score accumulator.
+  static __device__ __forceinline__ int tr_off(int lane, int db, int second) {
+    const int g = lane >> 4;
+    const int row = 4 * (g >> 1) + ((lane >> 2) & 3) + 8 * second;
+    const int c = 4 * db + 2 * (g & 1) + ((lane & 3) >> 1);
+    return row * ROWB + ((c ^ bwd_swz<D>(row)) << 4) + 8 * (lane & 1);
+  }
+  static __device__ __forceinline__ u32x4 tr_frag(const lds_char* base, int off0, int off1) {
+    const s16x4 a = tr16(base + off0);
+    const s16x4 b = tr16(base + off1);
+    u32x4 r;
+    r[0] = __builtin_bit_cast(u32x2, a)[0];
+    r[1] = __builtin_bit_cast(u32x2, a)[1];
+    r[2] = __builtin_bit_cast(u32x2, b)[0];
+    r[3] = __builtin_bit_cast(u32x2, b)[1];
+    return r;
+  }
+
+  // Global -> LDS copies that bypass the VGPRs: lane L of the wave writes its
+  // 16 (or 4) bytes at the LDS address `dst` + 16 L (4 L).  Written as inline
+  // asm so that the compiler does not drain the memory counter before every
+  // LDS read; dma_wait before each barrier is the only wait.
+  static __device__ __forceinline__ void dma16(const u32x4& rsrc, const lds_char* dst, int voffset) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %0\n s_nop 0\n buffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(m0), "v"(voffset), "s"(rsrc) : "memory", "m0");
+  }
+  static __device__ __forceinline__ void dma4(const u32x4& rsrc, const lds_char* dst, int voffset) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %0\n s_nop 0\n buffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(m0), "v"(voffset), "s"(rsrc) : "memory", "m0");
+  }
+  static __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+  // Staging of a ROWS-row tile by T threads: thread t copies linear LDS slots
+  // t + T j; slot s is row s / CPR at position s % CPR, which holds chunk
+  // (s % CPR) ^ bwd_swz(row) of that row (the XOR is an involution).
+  template <int ROWS, int T>
+  struct Stager {
+    static constexpr int CPT = ROWS * CPR / T;
+    static_assert(CPT >= 1 && (ROWS * CPR) % T == 0, "staging split");
+    int goff[CPT];  // global byte offset within the tile
+    int lds0;       // this wave's first slot (bytes)
+    __device__ __forceinline__ Stager(int tid) {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int s = tid + T * j;
+        const int row = s / CPR;
+        const int c = (s % CPR) ^ bwd_swz<D>(row);
+        goff[j] = (row * D + c * 8) * 2;
+      }
+      lds0 = (tid & ~63) * 16;
+    }
+    // Tile of rows r0.. into LDS at dst.
+    __device__ __forceinline__ void stage(const u32x4& rsrc, const lds_char* dst, int r0) const {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) dma16(rsrc, dst + lds0 + T * 16 * j, goff[j] + r0 * ROWB);
+    }
+  };
+
+  // Registers 8u..8u+7 of a score accumulator, rounded and packed: the B
+  // operand of a gradient product for k-step u.
+  static __device__ __forceinline__ void pack_operand(const float (&x)[16], u32x4 (&b)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) b[u][m] = pack2<BF16>(x[8 * u + 2 * m], x[8 * u + 2 * m + 1]);
+    }
+  }
+
+  // A gradient accumulator [32 dims x 32 rows] times `mul`, rounded and
+  // stored: lane L holds row `row` (its column) and, in register group g,
+  // dims 32db + 8g + 4(L/32) .. +3, stored as 8 bytes.
+  static __device__ __forceinline__ void store_grad(__amdgpu_buffer_rsrc_t r, const f32x16 (&acc)[DB], int row,
+                                                    int lane, float mul) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack2<BF16>(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul);
+        w[1] = pack2<BF16>(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, (row * D + 32 * db + 8 * g + 4 * h) * 2, 0, 0);
+      }
+    }
+  }
+};
+
+// ---- dQ (and Delta): query rows stationary, key tiles streamed ----------
+template <int D, int NW, bool BF16, bool CAUSAL>
+struct Fa2BwdQ : BwdBase<D, BF16> {
+  using Base = BwdBase<D, BF16>;
+  using Base::CPR;
+  using Base::DB;
+  using Base::DK;
+  using Base::ROWB;
+  using typename Base::lds_char;
+  static constexpr int THREADS = NW * 64;
+  static constexpr int BQ = NW * 32;  // query rows per workgroup (32 per wave)
+  static constexpr int BC = 64;       // keys per streamed tile
+  static constexpr int KB = BC / 32;
+  static constexpr int TILEB = BC * ROWB;
+  static constexpr int SLOTB = 2 * TILEB;  // one K tile and one V tile
+  static constexpr int LDS_BYTES = 2 * SLOTB;
+  using St = typename Base::template Stager<BC, THREADS>;
+
+  static __device__ __forceinline__ void run(const BwdParams& p, lds_char* lds) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int h = lane >> 5;
+    const int step = blockIdx.x / p.bh;
+    const int bh = blockIdx.x - step * p.bh;
+    // Causal: the last query tiles (the most keys) first.
+    const int qtile = CAUSAL ? p.n_tiles - 1 - step : step;
+    const int n = p.n;
+    const int q0 = qtile * BQ;
+    const int qw0 = q0 + 32 * wave;
+    const int myq = qw0 + (lane & 31);
+
+    const size_t slice = (size_t)bh * (size_t)n * D;
+    const uint32_t bytes = (uint32_t)n * D * 2;
+    const auto rq = make_rsrc((const char*)p.q + slice * 2, bytes);
+    const auto rdo = make_rsrc((const char*)p.dout + slice * 2, bytes);
+    const auto ro = make_rsrc((const char*)p.o + slice * 2, bytes);
+    const auto rdq = make_rsrc((char*)p.dq + slice * 2, bytes);
+    const auto rl = make_rsrc(p.lse + (size_t)bh * n, (uint32_t)n * 4);
+    const auto rd = make_rsrc(p.delta + (size_t)bh * n, (uint32_t)n * 4);
+
+    // Q^T and dO^T operands (lane: row myq, dims 16ks + 8h .. +7), and Delta
+    // of the row from dO and O as stored.
+    u32x4 qf[DK], df[DK];
+    float dsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+      const int off = (myq * D + 16 * ks + 8 * h) * 2;
+      qf[ks] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+      df[ks] = __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0);
+      const u32x4 of = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
+      if constexpr (BF16) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, df[ks]), b = __builtin_bit_cast(bf16x8, of);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dsum = __builtin_fmaf((float)a[i], (float)b[i], dsum);
+      } else {
+        const f16x8 a = __builtin_bit_cast(f16x8, df[ks]), b = __builtin_bit_cast(f16x8, of);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dsum = __builtin_fmaf((float)a[i], (float)b[i], dsum);
+      }
+    }
+    float lo, hi;
+    halves(dsum, lo, hi);
+    const float delta = lo + hi;
+    if (h == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), rd, myq * 4, 0, 0);
+    const float l2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, myq * 4, 0, 0)) * kLog2e;
+
+    // Lane-constant LDS offsets.
+    int poff[DK], toff[DB][2];
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) poff[ks] = Base::plain_off(lane, ks);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      toff[db][0] = Base::tr_off(lane, db, 0);
+      toff[db][1] = Base::tr_off(lane, db, 1);
+    }
+    const St st(tid);
+    const uint32_t kv_bytes = bytes;
+    const u32x4 wk = rsrc_words(p.k, slice * 2, kv_bytes);
+    const u32x4 wv = rsrc_words(p.v, slice * 2, kv_bytes);
+
+    f32x16 dq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+
+    const int kend = CAUSAL ? min(n, q0 + BQ) : n;
+    const int ntiles = (kend + BC - 1) / BC;
+    st.stage(wk, lds, 0);
+    st.stage(wv, lds + TILEB, 0);
+    for (int t = 0; t < ntiles; ++t) {
+      Base::dma_wait();
+      __syncthreads();
+      const lds_char* sk = lds + (t & 1) * SLOTB;
+      const lds_char* sv = sk + TILEB;
+      if (t + 1 < ntiles) {
+        const lds_char* nk = lds + ((t + 1) & 1) * SLOTB;
+        st.stage(wk, nk, (t + 1) * BC);
+        st.stage(wv, nk + TILEB, (t + 1) * BC);
+      }
+      const int k0 = t * BC;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int kr0 = k0 + 32 * kb;
+        if (CAUSAL && kr0 > qw0 + 31) continue;  // every key after every row of the wave
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) s = mfma32<BF16>(Base::lds16(sk + poff[ks] + kb * 32 * ROWB), qf[ks], s);
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) dp = mfma32<BF16>(Base::lds16(sv + poff[ks] + kb * 32 * ROWB), df[ks], dp);
+        // Lane: row myq; register r: key kr0 + 8(r/4) + 4h + r%4.
+        const bool masked = (kr0 + 32 > n) || (CAUSAL && kr0 + 31 > qw0);
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c2, -l2));
+          if (masked) {
+            const int key = kr0 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (key >= n || (CAUSAL && key > myq)) pr = 0.f;
+          }
+          ds[r] = pr * (dp[r] - delta);
+        }
+        u32x4 b[2];
+        Base::pack_operand(ds, b);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int rows = (kb * 32 + 16 * u) * ROWB;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            dq[db] = mfma32<BF16>(Base::tr_frag(sk, toff[db][0] + rows, toff[db][1] + rows), b[u], dq[db]);
+        }
+      }
+    }
+    Base::store_grad(rdq, dq, myq, lane, p.scale);
+  }
+};
+
+// ---- dK and dV: key rows stationary, query tiles streamed -----------------
+template <int D, int NW, bool BF16, bool CAUSAL>
+struct Fa2BwdKV : BwdBase<D, BF16> {
+  using Base = BwdBase<D, BF16>;
+  using Base::CPR;
+  using Base::DB;
+  using Base::DK;
+  using Base::ROWB;
+  using typename Base::lds_char;
+  static constexpr int THREADS = NW * 64;
+  static constexpr int BK = NW * 32;  // key rows per workgroup (32 per wave)
+  static constexpr int BQ = 64;       // query rows per streamed tile
+  static constexpr int QBLK = BQ / 32;
+  static constexpr int TILEB = BQ * ROWB;
+  // Slot: Q tile, dO tile, then LSE and Delta of its rows (BQ floats each).
+  static constexpr int SLOTB = 2 * TILEB + 2 * BQ * 4;
+  static constexpr int LDS_BYTES = 2 * SLOTB;
+  static_assert(BQ == 64, "LSE and Delta of a tile are one 64-lane dword copy each");
+  using St = typename Base::template Stager<BQ, THREADS>;
+
+  static __device__ __forceinline__ void run(const BwdParams& p, lds_char* lds) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int h = lane >> 5;
+    // Causal: the first key tiles (the most queries) first.
+    const int ktile = blockIdx.x / p.bh;
+    const int bh = blockIdx.x - ktile * p.bh;
+    const int n = p.n;
+    const int k0 = ktile * BK;
+    const int kw0 = k0 + 32 * wave;
+    const int mykey = kw0 + (lane & 31);
+
+    const size_t slice = (size_t)bh * (size_t)n * D;
+    const uint32_t bytes = (uint32_t)n * D * 2;
+    const auto rk = make_rsrc((const char*)p.k + slice * 2, bytes);
+    const auto rv = make_rsrc((const char*)p.v + slice * 2, bytes);
+    const auto rdk = make_rsrc((char*)p.dk + slice * 2, bytes);
+    const auto rdv = make_rsrc((char*)p.dv + slice * 2, bytes);
+
+    // K^T and V^T operands (lane: key mykey, dims 16ks + 8h .. +7).
+    u32x4 kf[DK], vf[DK];
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+      const int off = (mykey * D + 16 * ks + 8 * h) * 2;
+      kf[ks] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+      vf[ks] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    }
+
+    int poff[DK], toff[DB][2];
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) poff[ks] = Base::plain_off(lane, ks);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      toff[db][0] = Base::tr_off(lane, db, 0);
+      toff[db][1] = Base::tr_off(lane, db, 1);
+    }
+    const St st(tid);
+    const u32x4 wq = rsrc_words(p.q, slice * 2, bytes);
+    const u32x4 wdo = rsrc_words(p.dout, slice * 2, bytes);
+    const u32x4 wl = rsrc_words(p.lse, (size_t)bh * n * 4, (uint32_t)n * 4);
+    const u32x4 wd = rsrc_words(p.delta, (size_t)bh * n * 4, (uint32_t)n * 4);
+
+    f32x16 dv[DB], dk[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dv[db] = f32x16{};
+      dk[db] = f32x16{};
+    }
+
+    // Query tiles that see some key of the workgroup (rows past N load as
+    // zeros: Q, dO, LSE and Delta all 0, so P = 1 meets dO = 0 and
+    // dP - Delta = 0, and the row adds exactly nothing).
+    const int tfirst = CAUSAL ? k0 / BQ : 0;
+    const int tend = (n + BQ - 1) / BQ;
+    auto stage = [&](int t, const lds_char* dst) {
+      st.stage(wq, dst, t * BQ);
+      st.stage(wdo, dst + TILEB, t * BQ);
+      if (wave == 0) {
+        Base::dma4(wl, dst + 2 * TILEB, (t * BQ + lane) * 4);
+        Base::dma4(wd, dst + 2 * TILEB + BQ * 4, (t * BQ + lane) * 4);
+      }
+    };
+    stage(tfirst, lds);
+    for (int t = tfirst; t < tend; ++t) {
+      Base::dma_wait();
+      __syncthreads();
+      const lds_char* sq = lds + ((t - tfirst) & 1) * SLOTB;
+      const lds_char* sdo = sq + TILEB;
+      const lds_char* sst = sq + 2 * TILEB;
+      if (t + 1 < tend) stage(t + 1, lds + ((t + 1 - tfirst) & 1) * SLOTB);
+#pragma unroll
+      for (int qb = 0; qb < QBLK; ++qb) {
+        const int qr0 = t * BQ + 32 * qb;
+        if (CAUSAL && kw0 > qr0 + 31) continue;  // every key of the wave after every row of the block
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) s = mfma32<BF16>(Base::lds16(sq + poff[ks] + qb * 32 * ROWB), kf[ks], s);
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) dp = mfma32<BF16>(Base::lds16(sdo + poff[ks] + qb * 32 * ROWB), vf[ks], dp);
+        // Lane: key mykey; register r: query row qr0 + 8(r/4) + 4h + r%4,
+        // whose LSE and Delta sit at tile row 32qb + 8(r/4) + 4h + r%4.
+        const bool masked = CAUSAL && kw0 + 31 > qr0;
+        float pr[16], ds[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int trow = 32 * qb + 8 * g + 4 * h;
+          const f32x4 lse = Base::lds_f4(sst + trow * 4);
+          const f32x4 del = Base::lds_f4(sst + BQ * 4 + trow * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c2, -lse[e] * kLog2e));
+            if (masked && mykey > qr0 + 8 * g + 4 * h + e) x = 0.f;
+            pr[r] = x;
+            ds[r] = x * (dp[r] - del[e]);
+          }
+        }
+        u32x4 pb[2], sb[2];
+        Base::pack_operand(pr, pb);
+        Base::pack_operand(ds, sb);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int rows = (qb * 32 + 16 * u) * ROWB;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dv[db] = mfma32<BF16>(Base::tr_frag(sdo, toff[db][0] + rows, toff[db][1] + rows), pb[u], dv[db]);
+            dk[db] = mfma32<BF16>(Base::tr_frag(sq, toff[db][0] + rows, toff[db][1] + rows), sb[u], dk[db]);
+          }
+        }
+      }
+    }
+    Base::store_grad(rdv, dv, mykey, lane, 1.0f);
+    Base::store_grad(rdk, dk, mykey, lane, p.scale);
+  }
+};
+
+template <int D, int NW, bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64) fa2_bwd_q_kernel(const BwdParams p) {
+  extern __shared__ __attribute__((aligned(16))) char lds_generic[];
+  Fa2BwdQ<D, NW, BF16, CAUSAL>::run(
+      p, (__attribute__((address_space(3))) char*)(__attribute__((address_space(3))) void*)lds_generic);
+}
+
+template <int D, int NW, bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64) fa2_bwd_kv_kernel(const BwdParams p) {
+  extern __shared__ __attribute__((aligned(16))) char lds_generic[];
+  Fa2BwdKV<D, NW, BF16, CAUSAL>::run(
+      p, (__attribute__((address_space(3))) char*)(__attribute__((address_space(3))) void*)lds_generic);
+}
+
+}  // namespace fa2

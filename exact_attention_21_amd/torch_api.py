@@ -1,7 +1,7 @@
-"""PyTorch entry point: allocate O and LSE with torch and call the C ABI.
+"""PyTorch entry points: allocate outputs with torch and call the C ABI.
 
 torch supplies device memory and the current stream; the computation runs in
-the HIP kernel behind ``fa2_fwd``.
+the HIP kernels behind ``fa2_fwd``, ``fa2_fwd_masked`` and ``fa2_bwd``.
 """
 from __future__ import annotations
 
@@ -9,7 +9,7 @@ import math
 
 import torch
 
-from ._binding import FA2_DTYPE_BF16, FA2_DTYPE_FP16, FA2_OK, Fa2Error, fa2_fwd, fa2_fwd_masked
+from ._binding import FA2_DTYPE_BF16, FA2_DTYPE_FP16, FA2_OK, Fa2Error, fa2_bwd, fa2_fwd, fa2_fwd_masked
 
 _DTYPES = {torch.float16: FA2_DTYPE_FP16, torch.bfloat16: FA2_DTYPE_BF16}
 
@@ -72,3 +72,43 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | No
     if st != FA2_OK:
         raise Fa2Error(st, "fa2_fwd_masked" if masked else "fa2_fwd")
     return out, lse
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+             do: torch.Tensor, scale: float | None = None, causal: bool = False,
+             workspace: torch.Tensor | None = None):
+    """Gradients (dQ, dK, dV) of the attention of ``forward`` given dO.
+
+    q, k, v, o, do: [B, H, N, d] fp16/bf16 tensors of one dtype on one GPU
+    (d = 64 or 128); o and lse are forward's outputs for the same q, k, v,
+    scale and causal.  ``workspace`` (float32, B*H*N elements) may be given to
+    reuse it.  The two kernels are enqueued on torch's current stream.
+    """
+    ts = (q, k, v, o, do)
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise ValueError("q, k, v, o, do must share one [B, H, N, d] shape")
+    if q.dtype not in _DTYPES or any(t.dtype != q.dtype for t in ts):
+        raise TypeError("q, k, v, o, do must all be float16 or all bfloat16")
+    if not all(t.is_cuda and t.device == q.device for t in ts + (lse,)):
+        raise ValueError("all tensors must be on one GPU")
+    if not all(t.is_contiguous() for t in ts + (lse,)):
+        raise ValueError("all tensors must be contiguous")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if workspace.numel() < B * H * N or workspace.dtype != torch.float32 or not workspace.is_contiguous() \
+            or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous float32 tensor of B*H*N elements on q's device")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                     B, H, N, d, float(scale), int(bool(causal)), _DTYPES[q.dtype], stream)
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_bwd")
+    return dq, dk, dv

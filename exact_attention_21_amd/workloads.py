@@ -80,6 +80,12 @@ class Workload:
             return f / 2.0 if self.causal else f
         return 4.0 * self.H * self.d * float(self.visible_keys().sum())
 
+    def backward_flops(self) -> float:
+        """The metric's FLOP count of the backward pass: five products of
+        2 N^2 d per (batch, head) (S, dP, dV, dK, dQ), 2.5 times the forward's,
+        halved under the causal mask."""
+        return 2.5 * self.flops()
+
     def describe(self) -> dict:
         out = {"B": self.B, "H": self.H, "N": self.N, "d": self.d, "dtype": self.dtype,
                "causal": self.causal, "scale": self.softmax_scale()}
@@ -155,3 +161,13 @@ def make_inputs(w: Workload, seed: int = 0, N: int | None = None, B: int | None 
     k = round_to_storage(_draw(rng, shape, w.k_dist), w.dtype)
     v = round_to_storage(_draw(rng, shape, w.v_dist), w.dtype)
     return q, k, v
+
+
+def make_grad_output(w: Workload, seed: int = 0, N: int | None = None, B: int | None = None,
+                     H: int | None = None, sigma: float = 1.0):
+    """Draw the output gradient dO for a workload's backward pass: N(0, sigma^2)
+    of shape [B, H, N, d] from its own generator, ``default_rng([seed, 1])``,
+    rounded to the storage dtype (so Q, K, V of ``make_inputs`` are unchanged)."""
+    shape = (B or w.B, H or w.H, N or w.N, w.d)
+    rng = np.random.default_rng([seed, 1])
+    return round_to_storage(rng.standard_normal(shape) * sigma, w.dtype)

@@ -131,6 +131,47 @@ fa2_status_t fa2_fwd_masked(const void* Q, const void* K, const void* V, void* O
                             int64_t window_left, int64_t window_right, const int32_t* key_lens,
                             int dtype, void* stream);
 
+/*
+ * fa2_bwd - gradients of the attention of fa2_fwd (no window, no key
+ * lengths): given dO = dL/dO for some loss L, writes dQ, dK and dV.  With S
+ * and P = exp(S - LSE) as above (the forward's probabilities, recomputed
+ * from Q, K and the forward's LSE):
+ *
+ *   dV    = P^T dO
+ *   dP    = dO V^T,   Delta_i = sum_d dO[i,d] O[i,d],   dS = P * (dP - Delta)
+ *   dQ    = scale * dS K,   dK = scale * dS^T Q
+ *
+ *   The backward the pages outline: "第 15 章 FA2 前向：Tiling 与 Online
+ *   Softmax" (yangyitao.com), the chapter's closing paragraph (S and P
+ *   recomputed from the stored statistic, keys in the outer loop); the
+ *   arithmetic is the chain rule through the softmax of the definition above.
+ *
+ *   Q, K, V, O, dO  device pointers to [B, H, N, d] `dtype` tensors (read
+ *             only); O and LSE are the outputs of fa2_fwd for the same Q, K,
+ *             V, scale and is_causal (any O and LSE are accepted: they enter
+ *             the formulas above as given).
+ *   LSE       device pointer to the [B, H, N] float32 LSE of fa2_fwd.
+ *   dQ, dK, dV  device pointers to [B, H, N, d] `dtype` tensors (written,
+ *             every element).
+ *   workspace device pointer to B * H * N float32 values of scratch (Delta),
+ *             owned by the caller; its contents on entry do not matter and
+ *             it holds Delta when the call's work has run.
+ *   B, H, N, scale, is_causal, dtype, stream: as for fa2_fwd, with d = 64
+ *             or 128 only, and ceil(N / 128) * H * B < 2^31.
+ *
+ * Numerics: S, dP, Delta and the accumulators are fp32; P and dS are rounded
+ * to `dtype` (to nearest even) before the products that take them, and the
+ * gradients once at the end.  The call enqueues two kernels on `stream`
+ * (first dQ and Delta, then dK and dV), allocates nothing and does not
+ * synchronise.  Errors: as for fa2_fwd; FA2_ERR_OVERLAP when dQ, dK, dV or
+ * the workspace overlaps an input or one another; FA2_ERR_UNSUPPORTED_HEAD_DIM
+ * for d other than 64 and 128.
+ */
+fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
+                     int64_t B, int64_t H, int64_t N, int64_t d, float scale, int is_causal,
+                     int dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa2_status_string(int status);
 

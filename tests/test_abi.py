@@ -185,3 +185,52 @@ def test_masked_shares_fwd_checks():
     assert call_masked(dtype=5) == bd.FA2_ERR_UNSUPPORTED_DTYPE
     assert call_masked(scale=math.nan) == bd.FA2_ERR_BAD_SCALE
 
+
+
+# ---- fa2_bwd: the same checks, before any HIP call --------------------------
+BQ_, BK_, BV_, BO_, BDO_, BL_, BDQ_, BDK_, BDV_, BW_ = (0x10000000 * (i + 1) for i in range(10))
+
+
+def call_bwd(**kw):
+    args = dict(Q=BQ_, K=BK_, V=BV_, O=BO_, dO=BDO_, LSE=BL_, dQ=BDQ_, dK=BDK_, dV=BDV_, workspace=BW_,
+                B=1, H=2, N=100, d=64, scale=0.125, is_causal=0, dtype=fa.FA2_DTYPE_FP16, stream=0)
+    args.update(kw)
+    return fa.fa2_bwd(**args)
+
+
+@pytest.mark.parametrize("name", ["Q", "K", "V", "O", "dO", "LSE", "dQ", "dK", "dV", "workspace"])
+def test_bwd_null_pointer(name):
+    assert call_bwd(**{name: 0}) == bd.FA2_ERR_NULL_POINTER
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=-3), dict(N=1 << 24, d=64),
+                                dict(B=1 << 20, H=1 << 20)])
+def test_bwd_bad_shape(kw):
+    assert call_bwd(**kw) == bd.FA2_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("d", [0, 16, 32, 96, 256, 512, 1024])
+def test_bwd_unsupported_head_dim(d):
+    assert call_bwd(d=d) == bd.FA2_ERR_UNSUPPORTED_HEAD_DIM
+
+
+@pytest.mark.parametrize("dtype", [-1, 2])
+def test_bwd_unsupported_dtype(dtype):
+    assert call_bwd(dtype=dtype) == bd.FA2_ERR_UNSUPPORTED_DTYPE
+
+
+@pytest.mark.parametrize("scale", [math.inf, math.nan])
+def test_bwd_bad_scale(scale):
+    assert call_bwd(scale=scale) == bd.FA2_ERR_BAD_SCALE
+
+
+@pytest.mark.parametrize("kw", [dict(Q=BQ_ + 2), dict(dO=BDO_ + 8), dict(dV=BDV_ + 4), dict(LSE=BL_ + 2),
+                                dict(workspace=BW_ + 1)])
+def test_bwd_misaligned(kw):
+    assert call_bwd(**kw) == bd.FA2_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("kw", [dict(dQ=BQ_), dict(dK=BO_ + 16), dict(dV=BDK_ + 32), dict(workspace=BL_ + 4),
+                                dict(workspace=BDQ_ + 64), dict(dQ=BL_ - 16)])
+def test_bwd_overlap(kw):
+    assert call_bwd(**kw) == bd.FA2_ERR_OVERLAP

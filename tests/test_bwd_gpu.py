@@ -1,0 +1,125 @@
+"""GPU parity of fa2_bwd against the fp64 oracle's gradients
+(attention_bwd_ref), element by element, within the rounding bound of
+tests/bwd_helpers.py.
+
+O and LSE passed to the kernels come from the oracle's forward (rounded as a
+caller's would be), except in the chained test, which feeds the GPU
+forward's own O and LSE.  The full-size shapes are checked on sampled heads
+(every element of those heads); heads are independent."""
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_21_amd import backward, forward
+from exact_attention_21_amd import workloads as wl
+from tests import bwd_helpers as bh
+from tests.gpu_helpers import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(case_args, device, heads=None, seed=3, chained=False, stream=None):
+    B, H, N, d, dtype, causal, scale, sigma = case_args
+    w, q, k, v, do = bh.make_case(B, H, N, d, dtype, seed, causal=causal, scale=scale, sigma=sigma)
+    sc = w.softmax_scale()
+    print(f"case {w.name} causal={causal} scale={sc} sigma={sigma} chained={chained}", flush=True)
+    q64, k64, v64, do64 = (wl.to_float64(x, dtype) for x in (q, k, v, do))
+    tq, tk, tv, tdo = (to_device(x, dtype, device) for x in (q, k, v, do))
+    if chained:
+        o_t, lse_t = forward(tq, tk, tv, scale=sc, causal=causal)
+    else:
+        o_in, lse_in = bh.forward_inputs(q64, k64, v64, sc, causal, dtype)
+        o_t = to_device(o_in, dtype, device)
+        lse_t = torch.from_numpy(lse_in).to(device)
+    if stream is None:
+        dq, dk, dv = backward(tq, tk, tv, o_t, lse_t, tdo, scale=sc, causal=causal)
+    else:
+        with torch.cuda.stream(stream):
+            dq, dk, dv = backward(tq, tk, tv, o_t, lse_t, tdo, scale=sc, causal=causal)
+    torch.cuda.synchronize(device)
+    o_in64 = bh.to_np(o_t)
+    lse_in64 = lse_t.cpu().numpy().astype(np.float64)
+    refs, bounds = bh.grad_bounds(q64, k64, v64, do64, o_in64, lse_in64, sc, causal, dtype, heads=heads)
+    got = {}
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        g = bh.to_np(t)
+        got[name] = np.stack([g[b, h] for b, h in heads]) if heads is not None else g.reshape(refs[name].shape)
+    bh.assert_grads_within(got, refs, bounds, w.name)
+    return (tq, tk, tv, o_t, lse_t, tdo, dq, dk, dv)
+
+
+ONE = (1.0, 1.0, 1.0, 1.0)
+SMALL = [
+    (1, 2, 300, 64, wl.FP16, False, None, ONE),
+    (1, 2, 300, 64, wl.FP16, True, None, ONE),
+    (2, 1, 257, 128, wl.BF16, False, None, ONE),
+    (2, 1, 257, 128, wl.BF16, True, None, ONE),
+    (1, 1, 1, 64, wl.FP16, True, None, ONE),
+    (1, 1, 1, 128, wl.BF16, False, None, ONE),
+    (1, 1, 33, 128, wl.FP16, False, None, ONE),
+    (1, 3, 129, 64, wl.BF16, True, None, ONE),
+    (1, 2, 64, 64, wl.FP16, False, None, ONE),
+    (1, 1, 128, 128, wl.BF16, True, None, ONE),
+    (1, 2, 256, 128, wl.FP16, True, -0.2, ONE),
+    (1, 1, 200, 64, wl.BF16, False, 0.0, ONE),
+    (1, 1, 500, 64, wl.FP16, True, None, (3.0, 3.0, 1.0, 2.0)),
+    (1, 1, 380, 128, wl.BF16, False, None, (3.0, 3.0, 1.0, 0.5)),
+    (2, 2, 191, 64, wl.BF16, False, 0.5, ONE),
+    (1, 2, 700, 128, wl.FP16, True, None, ONE),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"b{c[0]}h{c[1]}n{c[2]}d{c[3]}{c[4]}"
+                         f"{'_causal' if c[5] else ''}_s{c[6]}_sig{c[7][0]:g}")
+def test_bwd_small(gpu_device, case):
+    _run(case, gpu_device)
+
+
+@pytest.mark.parametrize("case", [(1, 2, 2048, 64, wl.FP16, True, None, ONE),
+                                  (1, 2, 1024, 128, wl.BF16, False, None, ONE),
+                                  (1, 1, 1500, 128, wl.FP16, False, None, ONE)],
+                         ids=["n2048d64_fp16_causal", "n1024d128_bf16", "n1500d128_fp16"])
+def test_bwd_medium(gpu_device, case):
+    _run(case, gpu_device)
+
+
+# The bench's backward workloads at full size, every element of sampled heads.
+@pytest.mark.parametrize("w,heads", [(wl.HEADLINE, [(0, 0), (0, 5)]),
+                                     (wl.CAUSAL_TRAIN, [(0, 3), (1, 14)])],
+                         ids=["headline_b1h8n8192d64_fp16", "causal_b2h16n4096d128_bf16"])
+def test_bwd_full_size_sampled_heads(gpu_device, w, heads):
+    _run((w.B, w.H, w.N, w.d, w.dtype, w.causal, None, ONE), gpu_device, heads=heads, seed=0)
+
+
+@pytest.mark.parametrize("case", [(1, 2, 520, 64, wl.FP16, True, None, ONE),
+                                  (2, 1, 300, 128, wl.BF16, False, None, ONE)],
+                         ids=["d64_fp16_causal", "d128_bf16"])
+def test_bwd_chained_after_gpu_forward(gpu_device, case):
+    _run(case, gpu_device, chained=True)
+
+
+def test_bwd_workspace_holds_delta_and_results_repeat_bit_for_bit(gpu_device):
+    from exact_attention_21_amd import fa2_bwd, FA2_OK
+    B, H, N, d, dtype = 1, 2, 333, 128, wl.FP16
+    tq, tk, tv, o_t, lse_t, tdo, dq, dk, dv = _run((B, H, N, d, dtype, True, None, ONE), gpu_device)
+    ws = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=gpu_device)
+    outs = [torch.empty_like(tq) for _ in range(3)]
+    st = fa2_bwd(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o_t.data_ptr(), tdo.data_ptr(), lse_t.data_ptr(),
+                 outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), ws.data_ptr(), B, H, N, d,
+                 1.0 / np.sqrt(d), 1, 0, torch.cuda.current_stream(gpu_device).cuda_stream)
+    assert st == FA2_OK
+    torch.cuda.synchronize(gpu_device)
+    # No atomics: a second call gives the same bits.
+    for a, b in zip(outs, (dq, dk, dv)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    do64, o64 = bh.to_np(tdo), bh.to_np(o_t)
+    delta = np.sum(do64 * o64, axis=3)
+    tol = d * 2.0 ** -24 * np.sum(np.abs(do64 * o64), axis=3)
+    got = ws.cpu().numpy().astype(np.float64)
+    print(f"  Delta: max err {float(np.max(np.abs(got - delta))):.3e}", flush=True)
+    assert np.all(np.abs(got - delta) <= tol)
+
+
+def test_bwd_on_a_side_stream(gpu_device):
+    s = torch.cuda.Stream(device=gpu_device)
+    _run((1, 2, 400, 64, wl.BF16, True, None, ONE), gpu_device, stream=s)
