@@ -9,6 +9,8 @@ average kernel time used for the roofline figure.
 
 Prints one JSON line.  ``--workload NAME`` times one of the other seeded
 workloads instead (for the design notes; the default line is the headline one).
+``--pass bwd`` times the backward pass (fa2_bwd: dQ, dK, dV from the
+forward's O and LSE and a seeded N(0,1) dO) on d = 64 or 128 workloads.
 """
 from __future__ import annotations
 
@@ -23,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOPS at 1 GPU (4BHN²d, causal halved) + % of MFMA peak"
+METRIC_BWD = "attention bwd TFLOPS at 1 GPU (10BHN²d, causal halved) + % of MFMA peak"
 # MI355X dense fp16/bf16 MFMA peak: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz.
 MFMA_PEAK_TFLOPS = 2516.6
 # Best hand-written kernel on the leetCUDA notes page (RTX 4090, same shape):
@@ -30,19 +33,21 @@ MFMA_PEAK_TFLOPS = 2516.6
 PAGE_BEST_TFLOPS = 4 * 8 * 8192 ** 2 * 64 / 0.740e-3 / 1e12
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_21_amd", "csrc", f)
                   for f in ("fa2_kernel.hpp", "fa2_wide.hpp", "fa2_api.hip")]
+BWD_SOURCES = [os.path.join(ROOT, "exact_attention_21_amd", "csrc", f)
+               for f in ("fa2_bwd.hpp", "fa2_kernel.hpp", "fa2_api.hip")]
 
 
-def kernel_hash() -> str:
+def kernel_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload_name: str):
+def read_traffic(workload_name: str, prefix: str = "fa2_fwd_kernel", sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"fa2_fwd_kernel_{workload_name}.md")
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{workload_name}.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -50,7 +55,7 @@ def read_traffic(workload_name: str):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
-    if vals.get("kernel_sources_sha256_16") != kernel_hash():
+    if vals.get("kernel_sources_sha256_16") != kernel_hash(sources):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -107,6 +112,31 @@ def cpu_baseline(w, q, k, v, target_s: float = 10.0):
                       f"host has {len(os.sched_getaffinity(0))} usable cores)"}
 
 
+def cpu_baseline_bwd(w, q, k, v, do, target_s: float = 10.0):
+    """Time the fp64 backward oracle on a bounded sample of the workload: the
+    first (batch, head) pair, whole, repeated until about target_s of CPU
+    time has been spent; the mean pass is reported."""
+    from threadpoolctl import threadpool_info
+
+    from exact_attention_21_amd import workloads as wl
+    from oracle import attention_bwd_ref
+
+    qf, kf, vf, dof = (wl.to_float64(x[:1, :1], w.dtype) for x in (q, k, v, do))
+    passes, total = 0, 0.0
+    while total < target_s or passes == 0:
+        t0 = time.perf_counter()
+        attention_bwd_ref(qf, kf, vf, dof, w.softmax_scale(), w.causal)
+        total += time.perf_counter() - t0
+        passes += 1
+    dt = total / passes
+    flops = w.backward_flops() / (w.B * w.H)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"(batch 0, head 0) of {w.B * w.H} heads, all {w.N} rows, {passes} passes "
+                      f"({flops / 1e9:.1f} GFLOP under the metric's count, {dt:.2f} s per pass; "
+                      f"host has {len(os.sched_getaffinity(0))} usable cores)"}
+
+
 def settle_clock(step, stream, block: int = 25, min_ms: float = 1000.0, max_ms: float = 3000.0):
     """Run the hot path untimed until its per-launch time is steady.
 
@@ -141,6 +171,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="headline_b1h8n8192d64_fp16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -149,7 +180,7 @@ def main() -> int:
 
     import torch
 
-    from exact_attention_21_amd import forward, library
+    from exact_attention_21_amd import backward, forward, library
     from exact_attention_21_amd import workloads as wl
 
     library()  # fail loudly if the HIP library is not built
@@ -177,8 +208,22 @@ def main() -> int:
     if w.key_lens is not None:
         mask_kw["key_lens"] = torch.tensor(w.key_lens, dtype=torch.int32, device=dev)
 
-    def step():
-        forward(tq, tk, tv, scale=scale, causal=w.causal, out=out, lse=lse, **mask_kw)
+    bwd = args.pass_ == "bwd"
+    if bwd:
+        if w.masked or w.d not in (64, 128):
+            print(f"--pass bwd supports unmasked d = 64 and 128 workloads, not {w.name}", file=sys.stderr)
+            return 2
+        do = wl.make_grad_output(w, seed=0)
+        tdo = to_dev(do)
+        forward(tq, tk, tv, scale=scale, causal=w.causal, out=out, lse=lse)
+        grads = (torch.empty_like(tq), torch.empty_like(tq), torch.empty_like(tq))
+        ws = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def step():
+            backward(tq, tk, tv, out, lse, tdo, scale=scale, causal=w.causal, workspace=ws, out=grads)
+    else:
+        def step():
+            forward(tq, tk, tv, scale=scale, causal=w.causal, out=out, lse=lse, **mask_kw)
 
     settle = settle_clock(step, stream)
     for _ in range(args.warmup):
@@ -195,12 +240,14 @@ def main() -> int:
     wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
 
-    flops = w.flops()
+    flops = w.backward_flops() if bwd else w.flops()
     value = flops * args.steps / wall / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    traffic = read_traffic(w.name)
+    traffic = read_traffic(w.name, "fa2_bwd_kernels", BWD_SOURCES) if bwd else read_traffic(w.name)
+    kernel = ("fa2_bwd_q_kernel + fa2_bwd_kv_kernel" if bwd
+              else "fa2_wide_kernel" if w.d >= 512 else "fa2_fwd_kernel")
     line = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if bwd else METRIC,
         "value": round(value, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -209,24 +256,28 @@ def main() -> int:
         "ms_per_step": round(wall * 1e3 / args.steps, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / PAGE_BEST_TFLOPS, 3) if w.name == wl.HEADLINE.name else None,
+        "vs_baseline": round(value / PAGE_BEST_TFLOPS, 3) if w.name == wl.HEADLINE.name and not bwd else None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) Q, K, V; no dataset)",
+        "data": "synthetic (seeded N(0,1) Q, K, V" + (", dO" if bwd else "") + "; no dataset)",
         "config": {"workload": w.name, **w.describe()},
         "pct_of_mfma_peak": round(100.0 * value / MFMA_PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5),
-                     "kernel": "fa2_wide_kernel" if w.d >= 512 else "fa2_fwd_kernel",
+                     "kernel": kernel,
                      "flops_per_launch": flops},
         "clock_settle": {"launches": settle[0], "ms": round(settle[1], 1),
                          "note": "untimed launches before the warmup, until the per-launch time is steady"},
-        "baseline_note": "vs_baseline divides by 185.7 TFLOPS: the leetCUDA notes page's best "
-                         "kernel (0.740 ms on an RTX 4090, same shape) under this metric's FLOP "
-                         "count; other hardware, context only",
+        "baseline_note": ("the pages print no backward figure" if bwd else
+                          "vs_baseline divides by 185.7 TFLOPS: the leetCUDA notes page's best "
+                          "kernel (0.740 ms on an RTX 4090, same shape) under this metric's FLOP "
+                          "count; other hardware, context only"),
     }
+    if bwd:
+        line["roofline"]["note"] = ("achieved over both kernels' time; the metric counts 5 products of "
+                                    "2N^2d, the two kernels compute 7 (S and dP in each)")
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v)
+        line["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do) if bwd else cpu_baseline(w, q, k, v)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -76,13 +76,14 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | No
 
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
              do: torch.Tensor, scale: float | None = None, causal: bool = False,
-             workspace: torch.Tensor | None = None):
+             workspace: torch.Tensor | None = None, out: tuple | None = None):
     """Gradients (dQ, dK, dV) of the attention of ``forward`` given dO.
 
     q, k, v, o, do: [B, H, N, d] fp16/bf16 tensors of one dtype on one GPU
     (d = 64 or 128); o and lse are forward's outputs for the same q, k, v,
-    scale and causal.  ``workspace`` (float32, B*H*N elements) may be given to
-    reuse it.  The two kernels are enqueued on torch's current stream.
+    scale and causal.  ``workspace`` (float32, B*H*N elements) and ``out``
+    (a (dq, dk, dv) tuple of tensors like q) may be given to reuse buffers.
+    The two kernels are enqueued on torch's current stream.
     """
     ts = (q, k, v, o, do)
     if q.dim() != 4 or any(t.shape != q.shape for t in ts):
@@ -103,7 +104,12 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if workspace.numel() < B * H * N or workspace.dtype != torch.float32 or not workspace.is_contiguous() \
             or workspace.device != q.device:
         raise ValueError("workspace must be a contiguous float32 tensor of B*H*N elements on q's device")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = out
+    if any(t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device
+           for t in out):
+        raise ValueError("out must be three contiguous tensors like q")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
