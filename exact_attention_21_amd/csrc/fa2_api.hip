@@ -379,6 +379,96 @@ fa2_status_t bwd_check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dty
   return FA2_OK;
 }
 
+// Delta scratch of fa2_bwd_noalloc: one array per device, in the library's
+// code object, for callers that cannot allocate.  Host code never uses the
+// array's own name as a device address: the address is looked up once per
+// device (scratch_workspace) and that pointer is what the kernels get.
+constexpr int64_t kScratchFloats = int64_t(1) << 21;  // 8 MiB: B * H * N <= 2^21
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+// The device address of `scratch` on the current device (looked up on the
+// first call on each device), or null with *err set.
+float* scratch_workspace(int64_t floats, fa2_status_t* err) {
+  if (floats > kScratchFloats) {
+    *err = FA2_ERR_TOO_LARGE;
+    return nullptr;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    *err = FA2_ERR_HIP;
+    return nullptr;
+  }
+  static std::mutex mu;
+  static std::unordered_map<int, float*> ptrs;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = ptrs.find(dev);
+  if (it != ptrs.end()) return it->second;
+  float* ptr = nullptr;
+  if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+    *err = FA2_ERR_HIP;
+    return nullptr;
+  }
+  ptrs[dev] = ptr;
+  return ptr;
+}
+
+// Checks and launch of both backward entry points.  `get_scratch` (the
+// allocation-free entry point) supplies the workspace after every argument
+// check has passed; otherwise `workspace` is the caller's.
+fa2_status_t bwd_checked_launch(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                                const float* LSE, void* dQ, void* dK, void* dV, float* workspace, int64_t B,
+                                int64_t H, int64_t N, int64_t d, float scale, int is_causal, int dtype, void* stream,
+                                float* (*get_scratch)(int64_t, fa2_status_t*)) {
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA2_ERR_NULL_POINTER;
+  const fa2_status_t st = bwd_check_shape(B, H, N, d, dtype);
+  if (st != FA2_OK) return st;
+  if (!std::isfinite(scale)) return FA2_ERR_BAD_SCALE;
+  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)dO | (uintptr_t)dQ | (uintptr_t)dK |
+       (uintptr_t)dV) & 15u)
+    return FA2_ERR_MISALIGNED;
+  if (((uintptr_t)LSE | (uintptr_t)workspace) & 3u) return FA2_ERR_MISALIGNED;
+  const size_t tb = (size_t)(B * H * N * d) * 2;
+  const size_t rb = (size_t)(B * H * N) * 4;
+  const void* ins[6] = {Q, K, V, O, dO, LSE};
+  const size_t in_bytes[6] = {tb, tb, tb, tb, tb, rb};
+  const void* outs[4] = {dQ, dK, dV, workspace};
+  const size_t out_bytes[4] = {tb, tb, tb, workspace ? rb : 0};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA2_ERR_OVERLAP;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA2_ERR_OVERLAP;
+  }
+  if (get_scratch) {
+    fa2_status_t err = FA2_OK;
+    workspace = get_scratch(B * H * N, &err);
+    if (!workspace) return err;
+  }
+  fa2::BwdParams p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.dout = dO;
+  p.lse = LSE;
+  p.delta = workspace;
+  p.dq = dQ;
+  p.dk = dK;
+  p.dv = dV;
+  p.n = (int)N;
+  p.bh = (int)(B * H);
+  p.n_tiles = 0;  // set per kernel
+  p.scale = scale;
+  p.c2 = scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err;
+  if (dtype == FA2_DTYPE_BF16)
+    err = is_causal ? launch_bwd_d<true, true>(d, p, s) : launch_bwd_d<true, false>(d, p, s);
+  else
+    err = is_causal ? launch_bwd_d<false, true>(d, p, s) : launch_bwd_d<false, false>(d, p, s);
+  return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,9 +481,11 @@ const char* fa2_status_string(int status) {
     case FA2_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension (supported: 32, 64, 96, 128, 256, 512, 1024)";
     case FA2_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype (supported: fp16, bf16)";
     case FA2_ERR_BAD_SCALE: return "scale is not a finite number";
-    case FA2_ERR_MISALIGNED: return "Q, K, V, O must be 16-byte aligned and LSE 4-byte aligned";
-    case FA2_ERR_OVERLAP: return "O or LSE overlaps an input or each other";
+    case FA2_ERR_MISALIGNED:
+      return "a [B, H, N, d] tensor is not 16-byte aligned, or LSE, key_lens or the workspace not 4-byte aligned";
+    case FA2_ERR_OVERLAP: return "an output overlaps an input or another output";
     case FA2_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case FA2_ERR_TOO_LARGE: return "B * H * N exceeds what the allocation-free entry point's scratch holds";
     default: return "unknown status";
   }
 }
@@ -440,49 +532,16 @@ fa2_status_t fa2_fwd_masked(const void* Q, const void* K, const void* V, void* O
 fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
                      void* dQ, void* dK, void* dV, float* workspace, int64_t B, int64_t H, int64_t N, int64_t d,
                      float scale, int is_causal, int dtype, void* stream) {
-  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV || !workspace) return FA2_ERR_NULL_POINTER;
-  const fa2_status_t st = bwd_check_shape(B, H, N, d, dtype);
-  if (st != FA2_OK) return st;
-  if (!std::isfinite(scale)) return FA2_ERR_BAD_SCALE;
-  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)dO | (uintptr_t)dQ | (uintptr_t)dK |
-       (uintptr_t)dV) & 15u)
-    return FA2_ERR_MISALIGNED;
-  if (((uintptr_t)LSE | (uintptr_t)workspace) & 3u) return FA2_ERR_MISALIGNED;
-  const size_t tb = (size_t)(B * H * N * d) * 2;
-  const size_t rb = (size_t)(B * H * N) * 4;
-  const void* ins[6] = {Q, K, V, O, dO, LSE};
-  const size_t in_bytes[6] = {tb, tb, tb, tb, tb, rb};
-  const void* outs[4] = {dQ, dK, dV, workspace};
-  const size_t out_bytes[4] = {tb, tb, tb, rb};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
-      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA2_ERR_OVERLAP;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA2_ERR_OVERLAP;
-  }
-  fa2::BwdParams p;
-  p.q = Q;
-  p.k = K;
-  p.v = V;
-  p.o = O;
-  p.dout = dO;
-  p.lse = LSE;
-  p.delta = workspace;
-  p.dq = dQ;
-  p.dk = dK;
-  p.dv = dV;
-  p.n = (int)N;
-  p.bh = (int)(B * H);
-  p.n_tiles = 0;  // set per kernel
-  p.scale = scale;
-  p.c2 = scale * 1.4426950408889634f;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t err;
-  if (dtype == FA2_DTYPE_BF16)
-    err = is_causal ? launch_bwd_d<true, true>(d, p, s) : launch_bwd_d<true, false>(d, p, s);
-  else
-    err = is_causal ? launch_bwd_d<false, true>(d, p, s) : launch_bwd_d<false, false>(d, p, s);
-  return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
+  if (!workspace) return FA2_ERR_NULL_POINTER;
+  return bwd_checked_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, B, H, N, d, scale, is_causal, dtype, stream,
+                            nullptr);
+}
+
+fa2_status_t fa2_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                             const float* LSE, void* dQ, void* dK, void* dV, int64_t B, int64_t H, int64_t N,
+                             int64_t d, float scale, int is_causal, int dtype, void* stream) {
+  return bwd_checked_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, nullptr, B, H, N, d, scale, is_causal, dtype, stream,
+                            &scratch_workspace);
 }
 
 }  // extern "C"

@@ -32,10 +32,10 @@
  * |V| below 2^64 for bf16 (fp16 values are below 2^16 anyway).
  *
  * Ownership: the caller allocates and owns all five buffers.  The library
- * allocates no device memory, keeps no pointer after the call returns and has
- * no mutable global state.  Q, K, V are read only; O and LSE are fully
- * overwritten (every element, rows 0..N-1).  O and LSE must not overlap Q, K, V
- * or each other.
+ * allocates no device memory and keeps no pointer after the call returns.  Its
+ * only mutable global state is the scratch array of fa2_bwd_noalloc (below).
+ * Q, K, V are read only; O and LSE are fully overwritten (every element, rows
+ * 0..N-1).  O and LSE must not overlap Q, K, V or each other.
  *
  * Execution: the call validates its arguments on the host, then enqueues one
  * kernel on `stream` (a hipStream_t; NULL means the null stream) and returns
@@ -67,9 +67,11 @@ typedef enum {
   FA2_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d is not 32, 64, 96, 128, 256, 512 or 1024            */
   FA2_ERR_UNSUPPORTED_DTYPE = 4,    /* dtype is not FA2_DTYPE_FP16 or FA2_DTYPE_BF16         */
   FA2_ERR_BAD_SCALE = 5,            /* scale is NaN or infinite                              */
-  FA2_ERR_MISALIGNED = 6,           /* Q, K, V, O not 16-byte aligned, LSE or key_lens not 4 */
-  FA2_ERR_OVERLAP = 7,              /* O or LSE overlaps Q, K, V, key_lens or each other     */
-  FA2_ERR_HIP = 8                   /* the HIP runtime reported an error at launch           */
+  FA2_ERR_MISALIGNED = 6,           /* a [B,H,N,d] tensor not 16-byte aligned, LSE, key_lens
+                                       or the workspace not 4-byte aligned                  */
+  FA2_ERR_OVERLAP = 7,              /* an output overlaps an input or another output        */
+  FA2_ERR_HIP = 8,                  /* the HIP runtime reported an error at launch           */
+  FA2_ERR_TOO_LARGE = 9             /* fa2_bwd_noalloc: B * H * N above its scratch (2^21)   */
 } fa2_status_t;
 
 /*
@@ -171,6 +173,25 @@ fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O,
                      const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale, int is_causal,
                      int dtype, void* stream);
+
+/*
+ * fa2_bwd_noalloc - fa2_bwd without the workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc).  Delta goes to a scratch array inside the
+ * library (one per GPU, 2^21 floats, held until the process ends); the call
+ * allocates nothing.  B * H * N above 2^21 returns FA2_ERR_TOO_LARGE (before
+ * anything is enqueued).  Every call on one GPU shares that GPU's array: calls
+ * whose work overlaps in time on one GPU (on different streams, or from
+ * different host threads without ordering) race on it and give undefined
+ * results; calls ordered on one stream do not.  Delta is fully rewritten by
+ * each call before it is read, so nothing needs clearing.  Results are
+ * bit-identical to fa2_bwd's (same kernels).  All other arguments, checks and
+ * status codes are those of fa2_bwd.
+ */
+fa2_status_t fa2_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                             const float* LSE, void* dQ, void* dK, void* dV,
+                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, int is_causal,
+                             int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa2_status_string(int status);

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(0, 9):
+    for st in range(0, 10):
         s = fa.fa2_status_string(st)
         assert isinstance(s, str) and s and s != "unknown status"
     assert fa.fa2_status_string(99) == "unknown status"
@@ -234,3 +234,14 @@ def test_bwd_misaligned(kw):
                                 dict(workspace=BDQ_ + 64), dict(dQ=BL_ - 16)])
 def test_bwd_overlap(kw):
     assert call_bwd(**kw) == bd.FA2_ERR_OVERLAP
+
+
+def test_bwd_noalloc_checks_and_scratch_limit():
+    # 4 GiB apart: tensors of 2^21 rows of 64 dims do not overlap.
+    p = [(i + 1) << 32 for i in range(9)]
+    base = dict(Q=p[0], K=p[1], V=p[2], O=p[3], dO=p[4], LSE=p[5], dQ=p[6], dK=p[7], dV=p[8],
+                B=1, H=64, N=(1 << 21) // 64 + 1, d=64, scale=0.125, is_causal=0, dtype=0, stream=0)
+    assert fa.fa2_bwd_noalloc(**base) == bd.FA2_ERR_TOO_LARGE
+    assert fa.fa2_bwd_noalloc(**{**base, "dQ": 0}) == bd.FA2_ERR_NULL_POINTER
+    assert fa.fa2_bwd_noalloc(**{**base, "d": 96}) == bd.FA2_ERR_UNSUPPORTED_HEAD_DIM
+    assert fa.fa2_bwd_noalloc(**{**base, "dK": p[0]}) == bd.FA2_ERR_OVERLAP
