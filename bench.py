@@ -217,7 +217,7 @@ def main() -> int:
         tdo = to_dev(do)
         forward(tq, tk, tv, scale=scale, causal=w.causal, out=out, lse=lse)
         grads = (torch.empty_like(tq), torch.empty_like(tq), torch.empty_like(tq))
-        ws = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        ws = torch.empty((2, w.B, w.H, w.N), dtype=torch.float32, device=dev)
 
         def step():
             backward(tq, tk, tv, out, lse, tdo, scale=scale, causal=w.causal, workspace=ws, out=grads)

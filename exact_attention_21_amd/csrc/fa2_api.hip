@@ -379,11 +379,11 @@ fa2_status_t bwd_check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dty
   return FA2_OK;
 }
 
-// Delta scratch of fa2_bwd_noalloc: one array per device, in the library's
-// code object, for callers that cannot allocate.  Host code never uses the
+// Workspace of fa2_bwd_noalloc: one array per device, in the library's code
+// object, for callers that cannot allocate.  Host code never uses the
 // array's own name as a device address: the address is looked up once per
 // device (scratch_workspace) and that pointer is what the kernels get.
-constexpr int64_t kScratchFloats = int64_t(1) << 21;  // 8 MiB: B * H * N <= 2^21
+constexpr int64_t kScratchFloats = int64_t(1) << 22;  // 16 MiB: B * H * N <= 2^21
 static __device__ __align__(256) float scratch[kScratchFloats];
 
 // The device address of `scratch` on the current device (looked up on the
@@ -432,7 +432,7 @@ fa2_status_t bwd_checked_launch(const void* Q, const void* K, const void* V, con
   const void* ins[6] = {Q, K, V, O, dO, LSE};
   const size_t in_bytes[6] = {tb, tb, tb, tb, tb, rb};
   const void* outs[4] = {dQ, dK, dV, workspace};
-  const size_t out_bytes[4] = {tb, tb, tb, workspace ? rb : 0};
+  const size_t out_bytes[4] = {tb, tb, tb, workspace ? 2 * rb : 0};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA2_ERR_OVERLAP;
@@ -441,7 +441,7 @@ fa2_status_t bwd_checked_launch(const void* Q, const void* K, const void* V, con
   }
   if (get_scratch) {
     fa2_status_t err = FA2_OK;
-    workspace = get_scratch(B * H * N, &err);
+    workspace = get_scratch(2 * B * H * N, &err);
     if (!workspace) return err;
   }
   fa2::BwdParams p;

@@ -18,9 +18,9 @@
 //   * The pages accumulate dQ with atomic adds from every key tile.  Here two
 //     kernels share the work without atomics, and the results do not depend
 //     on the order in which workgroups run:
-//       - Fa2BwdQ (query rows stationary, key tiles streamed): Delta of its
-//         rows (written to a workspace), then S^T, dP^T, dS^T and
-//         dQ^T += K^T dS^T.  Launched first.
+//       - Fa2BwdQ (query rows stationary, key tiles streamed): Delta and the
+//         base-2 LSE of its rows (written to a workspace, negated), then
+//         S^T, dP^T, dS^T and dQ^T += K^T dS^T.  Launched first.
 //       - Fa2BwdKV (key rows stationary, query tiles streamed, the pages'
 //         loop order): S, dP, dS, dV^T += dO^T P and dK^T += Q^T dS.
 //     S and dP are computed in both, 7 matrix products in all instead of 5.
@@ -37,6 +37,8 @@
 //     (buffer_load ... lds), one barrier per tile.  A streamed tile is read
 //     both as plain rows and transposed; its 16-byte chunks are permuted
 //     per row (bwd_swz) so that both reads are free of LDS bank conflicts.
+//   * The dP accumulators start at -Delta instead of 0, so the product gives
+//     dP - Delta and dS = P (dP - Delta) is one multiply per element.
 //   * Rows past N load as zeros from range-checked buffer resources and
 //     contribute exactly zero; out-of-range stores are dropped by the same
 //     check.
@@ -58,7 +60,7 @@ struct BwdParams {
   const void* o;
   const void* dout;
   const float* lse;  // natural-log LSE of the forward, [B*H, N]
-  float* delta;      // workspace [B*H, N]: written by Fa2BwdQ, read by Fa2BwdKV
+  float* delta;      // workspace [2, B*H, N]: -Delta, then -LSE * log2(e) (Fa2BwdQ writes, Fa2BwdKV reads)
   void* dq;
   void* dk;
   void* dv;
@@ -222,12 +224,22 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
   using typename Base::lds_char;
   static constexpr int THREADS = NW * 64;
   static constexpr int BQ = NW * 32;  // query rows per workgroup (32 per wave)
-  static constexpr int BC = 64;       // keys per streamed tile
+  // Keys per streamed tile: 128 at d = 64, 64 at d = 128 (two tiles in LDS,
+  // 64 KiB, so that two workgroups share a CU).
+  static constexpr int BC = D == 64 ? 128 : 64;
   static constexpr int KB = BC / 32;
   static constexpr int TILEB = BC * ROWB;
   static constexpr int SLOTB = 2 * TILEB;  // one K tile and one V tile
   static constexpr int LDS_BYTES = 2 * SLOTB;
   using St = typename Base::template Stager<BC, THREADS>;
+  // Software pipeline over the KB 32-key blocks of a tile: step j issues the
+  // MFMAs of S(j+1) and dP(j+1) (NSD, S and dP alternating) and of
+  // dQ += K^T dS(j-1) (NQ), one at a time, each followed by its share of the
+  // VALU work of block j (8 pairs of probabilities: exponential, dS, packing).
+  static constexpr int NSD = 2 * DK;
+  static constexpr int NQ = 2 * DB;
+  static constexpr int NPOS = NSD + NQ;
+  static constexpr int PF = 3;  // positions between a fragment's LDS read and its MFMA
 
   static __device__ __forceinline__ void run(const BwdParams& p, lds_char* lds) {
     const int tid = threadIdx.x;
@@ -250,7 +262,9 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
     const auto ro = make_rsrc((const char*)p.o + slice * 2, bytes);
     const auto rdq = make_rsrc((char*)p.dq + slice * 2, bytes);
     const auto rl = make_rsrc(p.lse + (size_t)bh * n, (uint32_t)n * 4);
-    const auto rd = make_rsrc(p.delta + (size_t)bh * n, (uint32_t)n * 4);
+    // Workspace: -Delta of every row, then -LSE * log2(e) of every row.
+    const auto rnd = make_rsrc(p.delta + (size_t)bh * n, (uint32_t)n * 4);
+    const auto rnl = make_rsrc(p.delta + ((size_t)p.bh + bh) * n, (uint32_t)n * 4);
 
     // Q^T and dO^T operands (lane: row myq, dims 16ks + 8h .. +7), and Delta
     // of the row from dO and O as stored.
@@ -274,9 +288,16 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
     }
     float lo, hi;
     halves(dsum, lo, hi);
-    const float delta = lo + hi;
-    if (h == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), rd, myq * 4, 0, 0);
-    const float l2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, myq * 4, 0, 0)) * kLog2e;
+    const float ndelta = -(lo + hi);
+    const float nl2 = -__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, myq * 4, 0, 0)) * kLog2e;
+    if (h == 0) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ndelta), rnd, myq * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nl2), rnl, myq * 4, 0, 0);
+    }
+    // dP^T accumulators start at -Delta, so the product gives dP - Delta.
+    f32x16 dp0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dp0[r] = ndelta;
 
     // Lane-constant LDS offsets.
     int poff[DK], toff[DB][2];
@@ -288,19 +309,20 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
       toff[db][1] = Base::tr_off(lane, db, 1);
     }
     const St st(tid);
-    const uint32_t kv_bytes = bytes;
-    const u32x4 wk = rsrc_words(p.k, slice * 2, kv_bytes);
-    const u32x4 wv = rsrc_words(p.v, slice * 2, kv_bytes);
+    const u32x4 wk = rsrc_words(p.k, slice * 2, bytes);
+    const u32x4 wv = rsrc_words(p.v, slice * 2, bytes);
 
     f32x16 dq[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
 
+    // Key tiles [0, ntiles); those from `plain` on hold a key past N or past
+    // some row of the workgroup (causal) and take the per-element mask.
     const int kend = CAUSAL ? min(n, q0 + BQ) : n;
     const int ntiles = (kend + BC - 1) / BC;
-    st.stage(wk, lds, 0);
-    st.stage(wv, lds + TILEB, 0);
-    for (int t = 0; t < ntiles; ++t) {
+    const int plain = min(ntiles, CAUSAL ? min(n, q0 + 1) / BC : n / BC);
+    auto tile = [&](int t, auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
       Base::dma_wait();
       __syncthreads();
       const lds_char* sk = lds + (t & 1) * SLOTB;
@@ -311,38 +333,81 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
         st.stage(wv, nk + TILEB, (t + 1) * BC);
       }
       const int k0 = t * BC;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int kr0 = k0 + 32 * kb;
-        if (CAUSAL && kr0 > qw0 + 31) continue;  // every key after every row of the wave
-        f32x16 s = {}, dp = {};
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) s = mfma32<BF16>(Base::lds16(sk + poff[ks] + kb * 32 * ROWB), qf[ks], s);
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) dp = mfma32<BF16>(Base::lds16(sv + poff[ks] + kb * 32 * ROWB), df[ks], dp);
-        // Lane: row myq; register r: key kr0 + 8(r/4) + 4h + r%4.
-        const bool masked = (kr0 + 32 > n) || (CAUSAL && kr0 + 31 > qw0);
-        float ds[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c2, -l2));
-          if (masked) {
-            const int key = kr0 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key >= n || (CAUSAL && key > myq)) pr = 0.f;
-          }
-          ds[r] = pr * (dp[r] - delta);
+      f32x16 sc[2], dp[2];  // S^T and dP^T - Delta of blocks of either parity
+      u32x4 b[2][2];        // packed dS^T of blocks of either parity
+      // A operand of MFMA `pos` of the step that works on block j: S(j+1)
+      // and dP(j+1) (K and V rows), then dQ(j-1) (K^T, transposed read).
+      auto frag = [&](int j, int pos) -> u32x4 {
+        if (pos < NSD) {
+          const int kb = j + 1, ks = pos / 2;
+          return Base::lds16((pos % 2 ? sv : sk) + poff[ks] + kb * 32 * ROWB);
         }
-        u32x4 b[2];
-        Base::pack_operand(ds, b);
+        const int kb = j - 1, u = (pos - NSD) / DB, db = (pos - NSD) % DB;
+        const int rows = (kb * 32 + 16 * u) * ROWB;
+        return Base::tr_frag(sk, toff[db][0] + rows, toff[db][1] + rows);
+      };
+      auto active = [&](int j, int pos) { return pos < NSD ? j + 1 < KB : j >= 1; };
+      auto issue = [&](int j, int pos, const u32x4& a) {
+        if (pos < NSD) {
+          const int kb = j + 1, ks = pos / 2;
+          if (pos % 2 == 0)
+            sc[kb % 2] = mfma32<BF16>(a, qf[ks], ks == 0 ? f32x16{} : sc[kb % 2]);
+          else
+            dp[kb % 2] = mfma32<BF16>(a, df[ks], ks == 0 ? dp0 : dp[kb % 2]);
+        } else {
+          const int kb = j - 1, u = (pos - NSD) / DB, db = (pos - NSD) % DB;
+          dq[db] = mfma32<BF16>(a, b[kb % 2][u], dq[db]);
+        }
+      };
+      // VALU work of pair c of block j: registers 2c, 2c+1 (keys
+      // kr0 + 8(r/4) + 4h + r%4 of row myq).
+      auto pair = [&](int j, int c) {
+        float x[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int rows = (kb * 32 + 16 * u) * ROWB;
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * c + e;
+          x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j % 2][r], p.c2, nl2));
+          if constexpr (MASKED) {
+            const int key = k0 + 32 * j + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (key >= n || (CAUSAL && key > myq)) x[e] = 0.f;
+          }
+          x[e] *= dp[j % 2][r];
+        }
+        b[j % 2][c / 4][c % 4] = pack2<BF16>(x[0], x[1]);
+      };
+      // Prologue: S(0) and dP(0).
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
-            dq[db] = mfma32<BF16>(Base::tr_frag(sk, toff[db][0] + rows, toff[db][1] + rows), b[u], dq[db]);
+      for (int pos = 0; pos < NSD; ++pos) {
+        const u32x4 a = frag(-1, pos);
+        issue(-1, pos, a);
+      }
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        u32x4 fr[NPOS];
+#pragma unroll
+        for (int pos = 0; pos < PF && pos < NPOS; ++pos)
+          if (active(j, pos)) fr[pos] = frag(j, pos);
+#pragma unroll
+        for (int pos = 0; pos < NPOS; ++pos) {
+          if (pos + PF < NPOS && active(j, pos + PF)) fr[pos + PF] = frag(j, pos + PF);
+          if (active(j, pos)) issue(j, pos, fr[pos]);
+#pragma unroll
+          for (int c = pos * 8 / NPOS; c < (pos + 1) * 8 / NPOS; ++c) pair(j, c);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-    }
+      // Epilogue: dQ(KB-1).
+#pragma unroll
+      for (int pos = NSD; pos < NPOS; ++pos) {
+        const u32x4 a = frag(KB, pos);
+        issue(KB, pos, a);
+      }
+    };
+    st.stage(wk, lds, 0);
+    st.stage(wv, lds + TILEB, 0);
+    int t = 0;
+    for (; t < plain; ++t) tile(t, std::false_type{});
+    for (; t < ntiles; ++t) tile(t, std::true_type{});
     Base::store_grad(rdq, dq, myq, lane, p.scale);
   }
 };
@@ -358,14 +423,51 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
   using typename Base::lds_char;
   static constexpr int THREADS = NW * 64;
   static constexpr int BK = NW * 32;  // key rows per workgroup (32 per wave)
-  static constexpr int BQ = 64;       // query rows per streamed tile
+  static constexpr int BQ = 128;      // query rows per streamed tile
   static constexpr int QBLK = BQ / 32;
   static constexpr int TILEB = BQ * ROWB;
-  // Slot: Q tile, dO tile, then LSE and Delta of its rows (BQ floats each).
+  // Slot: Q tile, dO tile, then -LSE * log2(e) and -Delta of its rows (BQ
+  // floats each).
   static constexpr int SLOTB = 2 * TILEB + 2 * BQ * 4;
   static constexpr int LDS_BYTES = 2 * SLOTB;
-  static_assert(BQ == 64, "LSE and Delta of a tile are one 64-lane dword copy each");
+  static_assert(BQ == 128 && NW >= 2, "the row statistics of a tile are two 64-lane dword copies each");
   using St = typename Base::template Stager<BQ, THREADS>;
+  // dV and dK accumulators in AGPRs at d = 128 (one wave per SIMD: the arch
+  // VGPRs hold the rest), through the inline-asm MFMA of the forward's output
+  // product and under the same rules: its A and B operands are never written
+  // by VALU just before it (the B operands are packed a step earlier), the
+  // two MFMAs of one accumulator in a step are 2 DB - 1 MFMAs apart, and the
+  // epilogue reads the accumulators only after settle_acc.
+  static constexpr bool ACC_AGPR = D >= 128;
+  // Software pipeline over the QBLK 32-row blocks of a tile: step j issues
+  // the MFMAs of dV(j-1) and dK(j-1) (NG, u = 0 first), then of S(j+1) and
+  // dP(j+1) (NSD, alternating), one at a time, each followed by its share of
+  // the VALU work of block j (8 pairs: exponential, mask, dS, packing of P
+  // and dS).
+  static constexpr int NG = 4 * DB;
+  static constexpr int NSD = 2 * DK;
+  static constexpr int NPOS = NG + NSD;
+  static constexpr int PF = 3;  // positions between a fragment's LDS read and its MFMA
+
+  static __device__ __forceinline__ void acc_mfma(f32x16& c, const u32x4& a, const u32x4& b) {
+    if constexpr (ACC_AGPR)
+      mfma32_acc_agpr<BF16>(c, a, b);
+    else
+      c = mfma32<BF16>(a, b, c);
+  }
+  // Wait states between the last inline-asm MFMA of an accumulator and a
+  // compiler-issued read of it (a 32x32 MFMA's result is readable 18 passes
+  // after issue); the pins keep the reads behind the wait.
+  static __device__ __forceinline__ void settle_acc(f32x16 (&x)[DB], f32x16 (&y)[DB]) {
+    if constexpr (ACC_AGPR) {
+      asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        asm volatile("" : "+a"(x[db]));
+        asm volatile("" : "+a"(y[db]));
+      }
+    }
+  }
 
   static __device__ __forceinline__ void run(const BwdParams& p, lds_char* lds) {
     const int tid = threadIdx.x;
@@ -407,85 +509,155 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
     const St st(tid);
     const u32x4 wq = rsrc_words(p.q, slice * 2, bytes);
     const u32x4 wdo = rsrc_words(p.dout, slice * 2, bytes);
-    const u32x4 wl = rsrc_words(p.lse, (size_t)bh * n * 4, (uint32_t)n * 4);
+    // The row statistics the dQ kernel left in the workspace.
     const u32x4 wd = rsrc_words(p.delta, (size_t)bh * n * 4, (uint32_t)n * 4);
+    const u32x4 wl = rsrc_words(p.delta, ((size_t)p.bh + bh) * n * 4, (uint32_t)n * 4);
 
     f32x16 dv[DB], dk[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       dv[db] = f32x16{};
       dk[db] = f32x16{};
+      if constexpr (ACC_AGPR) {
+        asm volatile("" : "+a"(dv[db]));
+        asm volatile("" : "+a"(dk[db]));
+      }
     }
 
-    // Query tiles that see some key of the workgroup (rows past N load as
-    // zeros: Q, dO, LSE and Delta all 0, so P = 1 meets dO = 0 and
-    // dP - Delta = 0, and the row adds exactly nothing).
+    // Query tiles that see some key of the workgroup: [tfirst, tend); those
+    // before `mask_end` hold a row before some key (causal) and take the
+    // per-element mask.  Rows past N load as zeros: Q, dO and both
+    // statistics 0, so P = 1 meets dO = 0 and dP - Delta = 0, and the row
+    // adds exactly nothing.
     const int tfirst = CAUSAL ? k0 / BQ : 0;
     const int tend = (n + BQ - 1) / BQ;
+    const int mask_end = CAUSAL ? min(tend, (k0 + BK - 1 + BQ - 1) / BQ) : tfirst;
     auto stage = [&](int t, const lds_char* dst) {
       st.stage(wq, dst, t * BQ);
       st.stage(wdo, dst + TILEB, t * BQ);
-      if (wave == 0) {
-        Base::dma4(wl, dst + 2 * TILEB, (t * BQ + lane) * 4);
-        Base::dma4(wd, dst + 2 * TILEB + BQ * 4, (t * BQ + lane) * 4);
+      // Wave 0: -LSE * log2(e) of the tile's rows; wave 1: -Delta.
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (wave == 0) Base::dma4(wl, dst + 2 * TILEB + half * 256, (t * BQ + 64 * half + lane) * 4);
+        if (wave == 1) Base::dma4(wd, dst + 2 * TILEB + BQ * 4 + half * 256, (t * BQ + 64 * half + lane) * 4);
       }
     };
-    stage(tfirst, lds);
-    for (int t = tfirst; t < tend; ++t) {
+    auto tile = [&](int t, auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
       Base::dma_wait();
       __syncthreads();
       const lds_char* sq = lds + ((t - tfirst) & 1) * SLOTB;
       const lds_char* sdo = sq + TILEB;
       const lds_char* sst = sq + 2 * TILEB;
       if (t + 1 < tend) stage(t + 1, lds + ((t + 1 - tfirst) & 1) * SLOTB);
-#pragma unroll
-      for (int qb = 0; qb < QBLK; ++qb) {
-        const int qr0 = t * BQ + 32 * qb;
-        if (CAUSAL && kw0 > qr0 + 31) continue;  // every key of the wave after every row of the block
-        f32x16 s = {}, dp = {};
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) s = mfma32<BF16>(Base::lds16(sq + poff[ks] + qb * 32 * ROWB), kf[ks], s);
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) dp = mfma32<BF16>(Base::lds16(sdo + poff[ks] + qb * 32 * ROWB), vf[ks], dp);
-        // Lane: key mykey; register r: query row qr0 + 8(r/4) + 4h + r%4,
-        // whose LSE and Delta sit at tile row 32qb + 8(r/4) + 4h + r%4.
-        const bool masked = CAUSAL && kw0 + 31 > qr0;
-        float pr[16], ds[16];
+      const int q0 = t * BQ;
+      f32x16 sc[2], dp[2];      // S and dP - Delta of blocks of either parity
+      f32x16 nl2[2];            // -LSE * log2(e) of the rows, accumulator order
+      u32x4 pb[2][2], sb[2][2]; // packed P and dS of blocks of either parity
+      // Row statistics of block qb in accumulator order: register r holds
+      // tile row 32qb + 8(r/4) + 4h + r%4, four 16-byte reads.
+      auto stats = [&](int qb, int which) -> f32x16 {
+        f32x16 out;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int trow = 32 * qb + 8 * g + 4 * h;
-          const f32x4 lse = Base::lds_f4(sst + trow * 4);
-          const f32x4 del = Base::lds_f4(sst + BQ * 4 + trow * 4);
+          const f32x4 x = Base::lds_f4(sst + which * BQ * 4 + (32 * qb + 8 * g + 4 * h) * 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c2, -lse[e] * kLog2e));
-            if (masked && mykey > qr0 + 8 * g + 4 * h + e) x = 0.f;
-            pr[r] = x;
-            ds[r] = x * (dp[r] - del[e]);
-          }
+          for (int e = 0; e < 4; ++e) out[4 * g + e] = x[e];
         }
-        u32x4 pb[2], sb[2];
-        Base::pack_operand(pr, pb);
-        Base::pack_operand(ds, sb);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        return out;
+      };
+      f32x16 ndel;  // -Delta of the block whose dP is being accumulated
+      // A operand of MFMA `pos` of the step that works on block j.
+      auto frag = [&](int j, int pos) -> u32x4 {
+        if (pos < NG) {
+          const int qb = j - 1, u = pos / (2 * DB), db = (pos % (2 * DB)) / 2;
           const int rows = (qb * 32 + 16 * u) * ROWB;
+          return Base::tr_frag(pos % 2 ? sq : sdo, toff[db][0] + rows, toff[db][1] + rows);
+        }
+        const int qb = j + 1, ks = (pos - NG) / 2;
+        return Base::lds16(((pos - NG) % 2 ? sdo : sq) + poff[ks] + qb * 32 * ROWB);
+      };
+      auto active = [&](int j, int pos) { return pos < NG ? j >= 1 : j + 1 < QBLK; };
+      auto issue = [&](int j, int pos, const u32x4& a) {
+        if (pos < NG) {
+          const int qb = j - 1, u = pos / (2 * DB), db = (pos % (2 * DB)) / 2;
+          if (pos % 2 == 0)
+            acc_mfma(dv[db], a, pb[qb % 2][u]);
+          else
+            acc_mfma(dk[db], a, sb[qb % 2][u]);
+        } else {
+          const int qb = j + 1, ks = (pos - NG) / 2;
+          if ((pos - NG) % 2 == 0)
+            sc[qb % 2] = mfma32<BF16>(a, kf[ks], ks == 0 ? f32x16{} : sc[qb % 2]);
+          else
+            dp[qb % 2] = mfma32<BF16>(a, vf[ks], ks == 0 ? ndel : dp[qb % 2]);
+        }
+      };
+      // VALU work of pair c of block j: registers 2c, 2c+1 (rows
+      // q0 + 32j + 8(r/4) + 4h + r%4 against key mykey).
+      auto pair = [&](int j, int c) {
+        float x[2], y[2];
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            dv[db] = mfma32<BF16>(Base::tr_frag(sdo, toff[db][0] + rows, toff[db][1] + rows), pb[u], dv[db]);
-            dk[db] = mfma32<BF16>(Base::tr_frag(sq, toff[db][0] + rows, toff[db][1] + rows), sb[u], dk[db]);
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * c + e;
+          x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j % 2][r], p.c2, nl2[j % 2][r]));
+          if constexpr (MASKED) {
+            if (mykey > q0 + 32 * j + 8 * (r >> 2) + 4 * h + (r & 3)) x[e] = 0.f;
           }
+          y[e] = x[e] * dp[j % 2][r];
+        }
+        pb[j % 2][c / 4][c % 4] = pack2<BF16>(x[0], x[1]);
+        sb[j % 2][c / 4][c % 4] = pack2<BF16>(y[0], y[1]);
+      };
+      // Prologue: the statistics of block 0, S(0) and dP(0).
+      nl2[0] = stats(0, 0);
+      ndel = stats(0, 1);
+#pragma unroll
+      for (int pos = NG; pos < NPOS; ++pos) {
+        const u32x4 a = frag(-1, pos);
+        issue(-1, pos, a);
+      }
+#pragma unroll
+      for (int j = 0; j < QBLK; ++j) {
+        if (j + 1 < QBLK) {
+          nl2[(j + 1) % 2] = stats(j + 1, 0);
+          ndel = stats(j + 1, 1);
+        }
+        u32x4 fr[NPOS];
+#pragma unroll
+        for (int pos = 0; pos < PF && pos < NPOS; ++pos)
+          if (active(j, pos)) fr[pos] = frag(j, pos);
+#pragma unroll
+        for (int pos = 0; pos < NPOS; ++pos) {
+          if (pos + PF < NPOS && active(j, pos + PF)) fr[pos + PF] = frag(j, pos + PF);
+          if (active(j, pos)) issue(j, pos, fr[pos]);
+#pragma unroll
+          for (int c = pos * 8 / NPOS; c < (pos + 1) * 8 / NPOS; ++c) pair(j, c);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-    }
+      // Epilogue: dV(QBLK-1) and dK(QBLK-1).
+#pragma unroll
+      for (int pos = 0; pos < NG; ++pos) {
+        const u32x4 a = frag(QBLK, pos);
+        issue(QBLK, pos, a);
+      }
+    };
+    stage(tfirst, lds);
+    int t = tfirst;
+    for (; t < mask_end; ++t) tile(t, std::true_type{});
+    for (; t < tend; ++t) tile(t, std::false_type{});
+    settle_acc(dv, dk);
     Base::store_grad(rdv, dv, mykey, lane, 1.0f);
     Base::store_grad(rdk, dk, mykey, lane, p.scale);
   }
 };
 
+// Two waves per SIMD (256 registers each), so that one wave's VALU work
+// issues beside the other's MFMAs.
 template <int D, int NW, bool BF16, bool CAUSAL>
-__global__ void __launch_bounds__(NW * 64) fa2_bwd_q_kernel(const BwdParams p) {
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+    fa2_bwd_q_kernel(const BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) char lds_generic[];
   Fa2BwdQ<D, NW, BF16, CAUSAL>::run(
       p, (__attribute__((address_space(3))) char*)(__attribute__((address_space(3))) void*)lds_generic);

@@ -81,7 +81,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
 
     q, k, v, o, do: [B, H, N, d] fp16/bf16 tensors of one dtype on one GPU
     (d = 64 or 128); o and lse are forward's outputs for the same q, k, v,
-    scale and causal.  ``workspace`` (float32, B*H*N elements) and ``out``
+    scale and causal.  ``workspace`` (float32, 2*B*H*N elements) and ``out``
     (a (dq, dk, dv) tuple of tensors like q) may be given to reuse buffers.
     The two kernels are enqueued on torch's current stream.
     """
@@ -100,10 +100,10 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        workspace = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if workspace.numel() < B * H * N or workspace.dtype != torch.float32 or not workspace.is_contiguous() \
+        workspace = torch.empty((2, B, H, N), dtype=torch.float32, device=q.device)
+    if workspace.numel() < 2 * B * H * N or workspace.dtype != torch.float32 or not workspace.is_contiguous() \
             or workspace.device != q.device:
-        raise ValueError("workspace must be a contiguous float32 tensor of B*H*N elements on q's device")
+        raise ValueError("workspace must be a contiguous float32 tensor of 2*B*H*N elements on q's device")
     if out is None:
         out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = out

@@ -155,16 +155,17 @@ fa2_status_t fa2_fwd_masked(const void* Q, const void* K, const void* V, void* O
  *   LSE       device pointer to the [B, H, N] float32 LSE of fa2_fwd.
  *   dQ, dK, dV  device pointers to [B, H, N, d] `dtype` tensors (written,
  *             every element).
- *   workspace device pointer to B * H * N float32 values of scratch (Delta),
- *             owned by the caller; its contents on entry do not matter and
- *             it holds Delta when the call's work has run.
+ *   workspace device pointer to 2 * B * H * N float32 values of scratch,
+ *             owned by the caller; its contents on entry do not matter.  When
+ *             the call's work has run it holds -Delta of every row ([B, H, N])
+ *             followed by -LSE * log2(e) of every row ([B, H, N]).
  *   B, H, N, scale, is_causal, dtype, stream: as for fa2_fwd, with d = 64
  *             or 128 only, and ceil(N / 128) * H * B < 2^31.
  *
  * Numerics: S, dP, Delta and the accumulators are fp32; P and dS are rounded
  * to `dtype` (to nearest even) before the products that take them, and the
  * gradients once at the end.  The call enqueues two kernels on `stream`
- * (first dQ and Delta, then dK and dV), allocates nothing and does not
+ * (first dQ and the row statistics, then dK and dV), allocates nothing and does not
  * synchronise.  Errors: as for fa2_fwd; FA2_ERR_OVERLAP when dQ, dK, dV or
  * the workspace overlaps an input or one another; FA2_ERR_UNSUPPORTED_HEAD_DIM
  * for d other than 64 and 128.
@@ -177,13 +178,13 @@ fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O,
 /*
  * fa2_bwd_noalloc - fa2_bwd without the workspace argument, for callers that
  * cannot allocate device memory (code under HIP graph capture, serving loops,
- * harnesses that forbid hipMalloc).  Delta goes to a scratch array inside the
- * library (one per GPU, 2^21 floats, held until the process ends); the call
- * allocates nothing.  B * H * N above 2^21 returns FA2_ERR_TOO_LARGE (before
+ * harnesses that forbid hipMalloc).  The workspace is a scratch array inside
+ * the library (one per GPU, 2^22 floats, held until the process ends); the
+ * call allocates nothing.  B * H * N above 2^21 returns FA2_ERR_TOO_LARGE (before
  * anything is enqueued).  Every call on one GPU shares that GPU's array: calls
  * whose work overlaps in time on one GPU (on different streams, or from
  * different host threads without ordering) race on it and give undefined
- * results; calls ordered on one stream do not.  Delta is fully rewritten by
+ * results; calls ordered on one stream do not.  The workspace is fully rewritten by
  * each call before it is read, so nothing needs clearing.  Results are
  * bit-identical to fa2_bwd's (same kernels).  All other arguments, checks and
  * status codes are those of fa2_bwd.

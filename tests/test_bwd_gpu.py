@@ -98,11 +98,11 @@ def test_bwd_chained_after_gpu_forward(gpu_device, case):
     _run(case, gpu_device, chained=True)
 
 
-def test_bwd_workspace_holds_delta_and_results_repeat_bit_for_bit(gpu_device):
+def test_bwd_workspace_holds_row_statistics_and_results_repeat_bit_for_bit(gpu_device):
     from exact_attention_21_amd import fa2_bwd, FA2_OK
     B, H, N, d, dtype = 1, 2, 333, 128, wl.FP16
     tq, tk, tv, o_t, lse_t, tdo, dq, dk, dv = _run((B, H, N, d, dtype, True, None, ONE), gpu_device)
-    ws = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=gpu_device)
+    ws = torch.full((2, B, H, N), float("nan"), dtype=torch.float32, device=gpu_device)
     outs = [torch.empty_like(tq) for _ in range(3)]
     st = fa2_bwd(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o_t.data_ptr(), tdo.data_ptr(), lse_t.data_ptr(),
                  outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), ws.data_ptr(), B, H, N, d,
@@ -112,12 +112,15 @@ def test_bwd_workspace_holds_delta_and_results_repeat_bit_for_bit(gpu_device):
     # No atomics: a second call gives the same bits.
     for a, b in zip(outs, (dq, dk, dv)):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # The workspace: -Delta, then -LSE * log2(e), of every row.
     do64, o64 = bh.to_np(tdo), bh.to_np(o_t)
     delta = np.sum(do64 * o64, axis=3)
     tol = d * 2.0 ** -24 * np.sum(np.abs(do64 * o64), axis=3)
     got = ws.cpu().numpy().astype(np.float64)
-    print(f"  Delta: max err {float(np.max(np.abs(got - delta))):.3e}", flush=True)
-    assert np.all(np.abs(got - delta) <= tol)
+    print(f"  Delta: max err {float(np.max(np.abs(-got[0] - delta))):.3e}", flush=True)
+    assert np.all(np.abs(-got[0] - delta) <= tol)
+    l2 = lse_t.cpu().numpy().astype(np.float64) * np.log2(np.e)
+    assert np.all(np.abs(-got[1] - l2) <= 2.0 ** -22 * np.abs(l2))
 
 
 def test_bwd_on_a_side_stream(gpu_device):

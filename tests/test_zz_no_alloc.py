@@ -45,7 +45,7 @@ def test_noalloc_matches_fa2_bwd_on_two_calls(gpu_device):
                                                      (1, 2, 300, 64, wl.FP16, False)]):
         print(f"call {i}: B={B} H={H} N={N} d={d} {dtype} causal={causal}", flush=True)
         w, host, ts, lse = _inputs(B, H, N, d, dtype, causal, gpu_device, seed=11 + i)
-        ws = torch.empty((B, H, N), dtype=torch.float32, device=gpu_device)
+        ws = torch.empty((2, B, H, N), dtype=torch.float32, device=gpu_device)
         ref = _grads(ts, lse, w, gpu_device, ws)
         got = _grads(ts, lse, w, gpu_device, None)
         for name, a, b in zip(("dq", "dk", "dv"), got, ref):
