@@ -200,21 +200,37 @@ int resident_per_cu(const void* kern, int threads, int lds) {
   return n;
 }
 
+// Per-device set-up of one kernel: its dynamic LDS limit raised to `lds`
+// bytes and its resident workgroups per CU, done once for each device the
+// kernel is launched on (each template instantiation has its own cache).
+struct KernelSetup {
+  hipError_t err;
+  int per_cu;
+};
+template <typename Tag>
+KernelSetup kernel_setup(const void* kern, int threads, int lds) {
+  static std::mutex mu;
+  static std::unordered_map<int, KernelSetup> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  KernelSetup k{hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds), 1};
+  if (k.err == hipSuccess) k.per_cu = resident_per_cu(kern, threads, lds);
+  cache[dev] = k;
+  return k;
+}
+
 template <int D, int BC, int NW, int QB, int KVG, bool BF16, int MASK>
 hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
   constexpr int lds = fa2::Fa2Fwd<D, BC, NW, QB, KVG, BF16, MASK>::LDS_BYTES;
   static_assert(lds == lds_bytes_for(D, KVG == 2 || !has_split_form(D)), "LDS size");
   auto kern = fa2::fa2_fwd_kernel<D, BC, NW, QB, KVG, BF16, MASK>;
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  static int per_cu = 1;
-  std::call_once(once, [&] {
-    attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (attr_err == hipSuccess) per_cu = resident_per_cu((const void*)kern, NW * 64, lds);
-  });
-  if (attr_err != hipSuccess) return attr_err;
+  const KernelSetup k = kernel_setup<fa2::Fa2Fwd<D, BC, NW, QB, KVG, BF16, MASK>>((const void*)kern, NW * 64, lds);
+  if (k.err != hipSuccess) return k.err;
   fa2::Params q = p;
-  q.group = slice_group(p, per_cu, MASK);
+  q.group = slice_group(p, k.per_cu, MASK);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), lds, stream, q);
   return hipGetLastError();
 }
@@ -224,16 +240,10 @@ hipError_t launch_wide(const fa2::Params& p, int64_t grid, hipStream_t stream) {
   using W = fa2::Fa2Wide<D, BF16, MASK>;
   static_assert(W::LDS_BYTES == lds_bytes_for(D) && W::BR == rows_per_wg(D), "chunked kernel shape");
   auto kern = fa2::fa2_wide_kernel<D, BF16, MASK>;
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  static int per_cu = 1;
-  std::call_once(once, [&] {
-    attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, W::LDS_BYTES);
-    if (attr_err == hipSuccess) per_cu = resident_per_cu((const void*)kern, W::THREADS, W::LDS_BYTES);
-  });
-  if (attr_err != hipSuccess) return attr_err;
+  const KernelSetup k = kernel_setup<W>((const void*)kern, W::THREADS, W::LDS_BYTES);
+  if (k.err != hipSuccess) return k.err;
   fa2::Params q = p;
-  q.group = slice_group(p, per_cu, MASK);
+  q.group = slice_group(p, k.per_cu, MASK);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(W::THREADS), W::LDS_BYTES, stream, q);
   return hipGetLastError();
 }
@@ -334,14 +344,10 @@ hipError_t launch_bwd(const fa2::BwdParams& base, hipStream_t stream) {
   using KKV = fa2::Fa2BwdKV<D, kBwdWaves, BF16, CAUSAL>;
   auto kq = fa2::fa2_bwd_q_kernel<D, kBwdWaves, BF16, CAUSAL>;
   auto kkv = fa2::fa2_bwd_kv_kernel<D, kBwdWaves, BF16, CAUSAL>;
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [&] {
-    attr_err = hipFuncSetAttribute((const void*)kq, hipFuncAttributeMaxDynamicSharedMemorySize, KQ::LDS_BYTES);
-    if (attr_err == hipSuccess)
-      attr_err = hipFuncSetAttribute((const void*)kkv, hipFuncAttributeMaxDynamicSharedMemorySize, KKV::LDS_BYTES);
-  });
-  if (attr_err != hipSuccess) return attr_err;
+  const KernelSetup sq = kernel_setup<KQ>((const void*)kq, KQ::THREADS, KQ::LDS_BYTES);
+  if (sq.err != hipSuccess) return sq.err;
+  const KernelSetup skv = kernel_setup<KKV>((const void*)kkv, KKV::THREADS, KKV::LDS_BYTES);
+  if (skv.err != hipSuccess) return skv.err;
   // dQ and Delta first: the dK/dV kernel reads Delta.
   fa2::BwdParams p = base;
   p.n_tiles = (p.n + KQ::BQ - 1) / KQ::BQ;

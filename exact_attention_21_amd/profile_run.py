@@ -1,5 +1,6 @@
 """Driver for hardware-counter runs: a few fa2_fwd launches on one seeded
-workload, then one plain device-to-device copy of known size.
+workload (``--pass bwd``: one fa2_fwd launch, then a few fa2_bwd calls), then
+one plain device-to-device copy of known size.
 
 The copy gives the factor that turns the FETCH_SIZE / WRITE_SIZE counters into
 bytes (it moves exactly ``copy_mb`` MiB each way).  Usage (from any directory):
@@ -21,11 +22,12 @@ def main() -> int:
     ap.add_argument("--workload", default="headline_b1h8n8192d64_fp16")
     ap.add_argument("--launches", type=int, default=3)
     ap.add_argument("--copy-mb", type=int, default=256)
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd")
     args = ap.parse_args()
 
     import torch
 
-    from exact_attention_21_amd import forward, library
+    from exact_attention_21_amd import backward, forward, library
     from exact_attention_21_amd import workloads as wl
 
     library()
@@ -46,8 +48,16 @@ def main() -> int:
         mask_kw["window"] = w.window
     if w.key_lens is not None:
         mask_kw["key_lens"] = torch.tensor(w.key_lens, dtype=torch.int32, device=dev)
-    for _ in range(args.launches):
-        forward(tq, tk, tv, scale=w.softmax_scale(), causal=w.causal, out=out, lse=lse, **mask_kw)
+    if args.pass_ == "bwd":
+        forward(tq, tk, tv, scale=w.softmax_scale(), causal=w.causal, out=out, lse=lse)
+        tdo = to_dev(wl.make_grad_output(w, seed=0))
+        grads = (torch.empty_like(tq), torch.empty_like(tq), torch.empty_like(tq))
+        ws = torch.empty((2, w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        for _ in range(args.launches):
+            backward(tq, tk, tv, out, lse, tdo, scale=w.softmax_scale(), causal=w.causal, workspace=ws, out=grads)
+    else:
+        for _ in range(args.launches):
+            forward(tq, tk, tv, scale=w.softmax_scale(), causal=w.causal, out=out, lse=lse, **mask_kw)
     torch.cuda.synchronize(dev)
     n = args.copy_mb * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -55,7 +65,7 @@ def main() -> int:
     torch.cuda.synchronize(dev)
     dst.copy_(src)
     torch.cuda.synchronize(dev)
-    print(f"profile_run: {args.launches} launches of {w.name}, copy of {args.copy_mb} MiB", flush=True)
+    print(f"profile_run: {args.launches} {args.pass_} launches of {w.name}, copy of {args.copy_mb} MiB", flush=True)
     return 0
 
 
