@@ -43,49 +43,53 @@ struct TileCfg {
 };
 
 // Two waves per SIMD let one wave's softmax issue beside the other's MFMAs.
-// d = 32 and 64 have two forms with the same rows per workgroup: 8 waves in
-// two split-KV groups (one workgroup per CU, two waves per SIMD), or 4 waves
-// on one K/V stream, of which two workgroups share a CU and hide each other's
-// prologue and epilogue (choose_split picks by grid size).  d = 128 runs 8
-// waves of 32 rows on one K/V stream (64 rows per wave, 4 waves, measured 8%
-// slower).  d = 32 and 96 use 64-key tiles: with 32 keys their tiles have
-// fewer 16-byte chunks than the threads that load them (d = 32) or a
-// fractional number per thread (d = 96).  d = 96 runs without split-KV so
-// that its ring (96 KiB) fits the LDS.
-constexpr bool has_split_form(int64_t d) { return d == 32 || d == 64; }
+// d = 32, 64 and 128 have two forms.  The 8-wave form runs one workgroup per
+// CU (two waves per SIMD): at d = 32 and 64 in two split-KV groups of 4
+// waves, at d = 128 as 8 waves of 32 rows on one K/V stream (64 rows per
+// wave, 4 waves, measured 8% slower).  The 4-wave form runs two workgroups
+// per CU on one K/V stream each, which hide each other's prologue and
+// epilogue (choose_eight picks by grid size).  At d = 32 and 64 both forms
+// cover the same rows; the 4-wave form of d = 128 covers 128 rows instead of
+// 256.  d = 32 and 96 use 64-key tiles: with 32 keys their tiles have fewer
+// 16-byte chunks than the threads that load them (d = 32) or a fractional
+// number per thread (d = 96).  d = 96 runs without split-KV so that its ring
+// (96 KiB) fits the LDS.
+constexpr bool has_two_forms(int64_t d) { return d == 32 || d == 64 || d == 128; }
 
-constexpr TileCfg cfg_for(int64_t d, bool split = true) {
-  return d == 32    ? (split ? TileCfg{64, 8, 1, 2} : TileCfg{64, 4, 1, 1})
-         : d == 64  ? (split ? TileCfg{32, 8, 2, 2} : TileCfg{32, 4, 2, 1})
+constexpr TileCfg cfg_for(int64_t d, bool eight = true) {
+  return d == 32    ? (eight ? TileCfg{64, 8, 1, 2} : TileCfg{64, 4, 1, 1})
+         : d == 64  ? (eight ? TileCfg{32, 8, 2, 2} : TileCfg{32, 4, 2, 1})
          : d == 96  ? TileCfg{64, 4, 1, 1}
-         : d == 128 ? TileCfg{32, 8, 1, 1}
+         : d == 128 ? (eight ? TileCfg{32, 8, 1, 1} : TileCfg{32, 4, 1, 1})
                     : TileCfg{32, 4, 1, 1};
 }
 
-template <int D, bool SPLIT = true>
-using KernelFor = fa2::Fa2Fwd<D, cfg_for(D, SPLIT).bc, cfg_for(D, SPLIT).nw, cfg_for(D, SPLIT).qb,
-                              cfg_for(D, SPLIT).kvg, false, false>;
+template <int D, bool EIGHT = true>
+using KernelFor = fa2::Fa2Fwd<D, cfg_for(D, EIGHT).bc, cfg_for(D, EIGHT).nw, cfg_for(D, EIGHT).qb,
+                              cfg_for(D, EIGHT).kvg, false, false>;
 static_assert(KernelFor<32, false>::BR == KernelFor<32>::BR && KernelFor<64, false>::BR == KernelFor<64>::BR,
-              "both forms of d = 32 and 64 cover the same rows, so the grid does not depend on the choice");
+              "both forms of d = 32 and 64 cover the same rows");
 // Head dims 512 and 1024 run the chunked kernel (fa2_wide.hpp).
 template <int D>
 using WideFor = fa2::Fa2Wide<D, false, fa2::kMaskNone>;
 
-constexpr int rows_per_wg(int64_t d) {
+// Query rows per workgroup; `eight` selects the form where there are two.
+constexpr int rows_per_wg(int64_t d, bool eight = true) {
   return d == 32 ? KernelFor<32>::BR : d == 64 ? KernelFor<64>::BR : d == 96 ? KernelFor<96>::BR
-         : d == 128 ? KernelFor<128>::BR : d == 256 ? KernelFor<256>::BR
+         : d == 128 ? (eight ? KernelFor<128>::BR : KernelFor<128, false>::BR) : d == 256 ? KernelFor<256>::BR
          : d == 512 ? WideFor<512>::BR : WideFor<1024>::BR;
 }
 
-constexpr int lds_bytes_for(int64_t d, bool split = true) {
-  return d == 32 ? (split ? KernelFor<32>::LDS_BYTES : KernelFor<32, false>::LDS_BYTES)
-         : d == 64 ? (split ? KernelFor<64>::LDS_BYTES : KernelFor<64, false>::LDS_BYTES)
-         : d == 96 ? KernelFor<96>::LDS_BYTES : d == 128 ? KernelFor<128>::LDS_BYTES
+constexpr int lds_bytes_for(int64_t d, bool eight = true) {
+  return d == 32 ? (eight ? KernelFor<32>::LDS_BYTES : KernelFor<32, false>::LDS_BYTES)
+         : d == 64 ? (eight ? KernelFor<64>::LDS_BYTES : KernelFor<64, false>::LDS_BYTES)
+         : d == 96 ? KernelFor<96>::LDS_BYTES
+         : d == 128 ? (eight ? KernelFor<128>::LDS_BYTES : KernelFor<128, false>::LDS_BYTES)
          : d == 256 ? KernelFor<256>::LDS_BYTES : d == 512 ? WideFor<512>::LDS_BYTES : WideFor<1024>::LDS_BYTES;
 }
 
-constexpr int threads_for(int64_t d, bool split = true) {
-  return d == 512 ? WideFor<512>::THREADS : d == 1024 ? WideFor<1024>::THREADS : cfg_for(d, split).nw * 64;
+constexpr int threads_for(int64_t d, bool eight = true) {
+  return d == 512 ? WideFor<512>::THREADS : d == 1024 ? WideFor<1024>::THREADS : cfg_for(d, eight).nw * 64;
 }
 
 // Compute units of the current device (256, MI355X's count, when no device
@@ -104,20 +108,30 @@ int device_cus() {
   return n;
 }
 
-// Split-KV form for d = 32 and 64 (see cfg_for) unless the grid gives every
-// CU enough workgroups of the 4-wave form (two of which share a CU).
+// The 8-wave form (see cfg_for) unless the grid gives every CU enough
+// workgroups of the 4-wave form.  `grid` is the grid of the 8-wave form.
 // Measured, same-process A/B of the two forms:
-//   no mask: split-KV +1% to +2% at one workgroup per CU, even at two, the
-//     4-wave form +2% to +4% beyond and +35% at N = 512 (d = 64);
+//   d = 32 and 64, no mask: split-KV +1% to +2% at one workgroup per CU,
+//     even at two, the 4-wave form +2% to +4% beyond and +35% at N = 512
+//     (d = 64);
 //   causal, fp16 d = 64: split-KV +11% at two per CU (the query tiles differ
 //     in length, and two per CU balance only over several rounds), the 4-wave
 //     form +3% to +13% from three;
 //   bf16 d = 64 under any mask: the 4-wave form +11% to +32% at every grid
 //     tried (one to five per CU): the split-KV form's 8 waves spill there;
 //   windows (fp16 d = 64) and d = 32 under a mask: the 4-wave form +4% to
-//     +23% at two per CU, even at three.
-bool choose_split(int64_t d, int64_t grid, int mask, int dtype) {
-  if (!has_split_form(d) || !FA2_SPLIT_KV) return false;
+//     +23% at two per CU, even at three;
+//   d = 128 (8-wave grid in workgroups per CU): no mask, the 4-wave form +27%
+//     at 0.5, -6% at 1 (three shapes) and -5% at 2; causal, +16% to +38% at
+//     0.5 and 1 (four shapes), -1% at 1.5, -6% at 2.  The general mask keeps
+//     the 8-wave form (not measured).
+bool choose_eight(int64_t d, int64_t grid, int mask, int dtype) {
+  if (!has_two_forms(d)) return true;
+  if (d == 128) {
+    if (mask == fa2::kMaskGeneral) return true;
+    return mask == fa2::kMaskCausal ? grid > device_cus() : grid >= device_cus();
+  }
+  if (!FA2_SPLIT_KV) return false;
   if (mask != fa2::kMaskNone && d == 64 && dtype == FA2_DTYPE_BF16) return false;
   const int64_t per_cu = (mask == fa2::kMaskCausal && d == 64) ? 3 : 2;
   return grid < per_cu * device_cus();
@@ -225,7 +239,7 @@ KernelSetup kernel_setup(const void* kern, int threads, int lds) {
 template <int D, int BC, int NW, int QB, int KVG, bool BF16, int MASK>
 hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
   constexpr int lds = fa2::Fa2Fwd<D, BC, NW, QB, KVG, BF16, MASK>::LDS_BYTES;
-  static_assert(lds == lds_bytes_for(D, KVG == 2 || !has_split_form(D)), "LDS size");
+  static_assert(lds == lds_bytes_for(D, NW == 8 || !has_two_forms(D)), "LDS size");
   auto kern = fa2::fa2_fwd_kernel<D, BC, NW, QB, KVG, BF16, MASK>;
   const KernelSetup k = kernel_setup<fa2::Fa2Fwd<D, BC, NW, QB, KVG, BF16, MASK>>((const void*)kern, NW * 64, lds);
   if (k.err != hipSuccess) return k.err;
@@ -249,14 +263,14 @@ hipError_t launch_wide(const fa2::Params& p, int64_t grid, hipStream_t stream) {
 }
 
 template <int D, bool BF16, int MASK>
-hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream, bool split) {
+hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream, bool eight) {
   if constexpr (!built_d(D)) {
     return hipErrorInvalidValue;  // not reached: check_shape rejects it
   } else if constexpr (D >= 512) {
     return launch_wide<D, BF16, MASK>(p, grid, stream);
-  } else if constexpr (has_split_form(D)) {
+  } else if constexpr (has_two_forms(D)) {
     constexpr TileCfg s = cfg_for(D, true), u = cfg_for(D, false);
-    return split ? launch<D, s.bc, s.nw, s.qb, s.kvg, BF16, MASK>(p, grid, stream)
+    return eight ? launch<D, s.bc, s.nw, s.qb, s.kvg, BF16, MASK>(p, grid, stream)
                  : launch<D, u.bc, u.nw, u.qb, u.kvg, BF16, MASK>(p, grid, stream);
   } else {
     constexpr TileCfg c = cfg_for(D);
@@ -265,24 +279,24 @@ hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream, bool
 }
 
 template <bool BF16, int MASK>
-hipError_t launch_dt(int64_t d, const fa2::Params& p, int64_t grid, hipStream_t stream, bool split) {
+hipError_t launch_dt(int64_t d, const fa2::Params& p, int64_t grid, hipStream_t stream, bool eight) {
   switch (d) {
-    case 32: return launch_d<32, BF16, MASK>(p, grid, stream, split);
-    case 64: return launch_d<64, BF16, MASK>(p, grid, stream, split);
-    case 96: return launch_d<96, BF16, MASK>(p, grid, stream, split);
-    case 128: return launch_d<128, BF16, MASK>(p, grid, stream, split);
-    case 256: return launch_d<256, BF16, MASK>(p, grid, stream, split);
-    case 512: return launch_d<512, BF16, MASK>(p, grid, stream, split);
-    default: return launch_d<1024, BF16, MASK>(p, grid, stream, split);
+    case 32: return launch_d<32, BF16, MASK>(p, grid, stream, eight);
+    case 64: return launch_d<64, BF16, MASK>(p, grid, stream, eight);
+    case 96: return launch_d<96, BF16, MASK>(p, grid, stream, eight);
+    case 128: return launch_d<128, BF16, MASK>(p, grid, stream, eight);
+    case 256: return launch_d<256, BF16, MASK>(p, grid, stream, eight);
+    case 512: return launch_d<512, BF16, MASK>(p, grid, stream, eight);
+    default: return launch_d<1024, BF16, MASK>(p, grid, stream, eight);
   }
 }
 
 template <bool BF16>
-hipError_t launch_mask(int mask, int64_t d, const fa2::Params& p, int64_t grid, hipStream_t stream, bool split) {
+hipError_t launch_mask(int mask, int64_t d, const fa2::Params& p, int64_t grid, hipStream_t stream, bool eight) {
   switch (mask) {
-    case fa2::kMaskNone: return launch_dt<BF16, fa2::kMaskNone>(d, p, grid, stream, split);
-    case fa2::kMaskCausal: return launch_dt<BF16, fa2::kMaskCausal>(d, p, grid, stream, split);
-    default: return launch_dt<BF16, fa2::kMaskGeneral>(d, p, grid, stream, split);
+    case fa2::kMaskNone: return launch_dt<BF16, fa2::kMaskNone>(d, p, grid, stream, eight);
+    case fa2::kMaskCausal: return launch_dt<BF16, fa2::kMaskCausal>(d, p, grid, stream, eight);
+    default: return launch_dt<BF16, fa2::kMaskGeneral>(d, p, grid, stream, eight);
   }
 }
 
@@ -308,7 +322,11 @@ fa2_status_t checked_launch(const void* Q, const void* K, const void* V, void* O
       overlaps(LSE, lse_bytes, key_lens, len_bytes))
     return FA2_ERR_OVERLAP;
 
-  const int br = rows_per_wg(d);
+  // The form, chosen on the 8-wave form's grid; the 4-wave form of d = 128
+  // covers fewer rows per workgroup, so its grid is recomputed.
+  const bool eight = choose_eight(d, grid, mask, dtype);
+  const int br = rows_per_wg(d, eight);
+  grid = (N + br - 1) / br * (B * H);
   fa2::Params p;
   p.q = Q;
   p.k = K;
@@ -328,9 +346,8 @@ fa2_status_t checked_launch(const void* Q, const void* K, const void* V, void* O
   p.group = p.bh;  // set per kernel at launch (slice_group)
 
   hipStream_t s = (hipStream_t)stream;
-  const bool split = choose_split(d, grid, mask, dtype);
-  const hipError_t err = dtype == FA2_DTYPE_BF16 ? launch_mask<true>(mask, d, p, grid, s, split)
-                                                 : launch_mask<false>(mask, d, p, grid, s, split);
+  const hipError_t err = dtype == FA2_DTYPE_BF16 ? launch_mask<true>(mask, d, p, grid, s, eight)
+                                                 : launch_mask<false>(mask, d, p, grid, s, eight);
   return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
 }
 
@@ -502,13 +519,14 @@ fa2_status_t fa2_launch_info(int64_t B, int64_t H, int64_t N, int64_t d, int is_
   int64_t grid = 0;
   const fa2_status_t st = check_shape(B, H, N, d, dtype, &grid);
   if (st != FA2_OK) return st;
-  const bool split = choose_split(d, grid, is_causal ? fa2::kMaskCausal : fa2::kMaskNone, dtype);
-  const TileCfg c = cfg_for(d, split);
+  const bool eight = choose_eight(d, grid, is_causal ? fa2::kMaskCausal : fa2::kMaskNone, dtype);
+  const TileCfg c = cfg_for(d, eight);
+  grid = (N + ::rows_per_wg(d, eight) - 1) / ::rows_per_wg(d, eight) * (B * H);
   if (workgroups) *workgroups = grid;
-  if (threads) *threads = threads_for(d, split);
-  if (rows_per_wg) *rows_per_wg = ::rows_per_wg(d);
+  if (threads) *threads = threads_for(d, eight);
+  if (rows_per_wg) *rows_per_wg = ::rows_per_wg(d, eight);
   if (keys_per_tile) *keys_per_tile = c.bc;
-  if (lds_bytes) *lds_bytes = lds_bytes_for(d, split);
+  if (lds_bytes) *lds_bytes = lds_bytes_for(d, eight);
   return FA2_OK;
 }
 

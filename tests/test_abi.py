@@ -106,9 +106,10 @@ def test_launch_info_headline_shape():
 
 
 # (B, H, N, d, causal, dtype) -> threads per workgroup the launch picks for
-# d = 32 and 64 (512: 8-wave split-KV form, 256: 4-wave form).  Without a GPU
+# d = 32, 64 and 128 (512: 8-wave form, 256: 4-wave form).  Without a GPU
 # the library assumes 256 compute units, so the grid sizes below are 1, 2 and
-# 3 workgroups per CU (256 query rows per workgroup at d = 64, 128 at d = 32).
+# 3 workgroups per CU (256 query rows per workgroup at d = 64, 128 at d = 32)
+# and, for d = 128, 0.5 to 4 workgroups of the 8-wave form per CU (256 rows).
 FORM_CHOICES = [
     ((1, 8, 8192, 64, 0, 0), 512),  # no mask, one per CU: split-KV
     ((2, 8, 8192, 64, 0, 0), 256),  # no mask, two per CU: 4-wave
@@ -119,13 +120,22 @@ FORM_CHOICES = [
     ((1, 2, 300, 64, 1, 1), 256),
     ((1, 8, 4096, 32, 1, 0), 512),  # d = 32 causal, one per CU: split-KV
     ((2, 8, 4096, 32, 1, 0), 256),  # two per CU: 4-wave
-    ((4, 8, 8192, 128, 1, 1), 512),  # d = 128: one form (8 waves)
+    ((4, 8, 8192, 128, 1, 1), 512),  # d = 128, four 8-wave workgroups per CU: 8 waves
+    ((1, 8, 8192, 128, 0, 0), 512),  # no mask, one per CU: 8 waves
+    ((1, 16, 4096, 128, 1, 1), 256),  # causal, one per CU: 4 waves
+    ((1, 32, 1024, 128, 0, 0), 256),  # no mask, half a round: 4 waves
+    ((2, 16, 4096, 128, 1, 0), 512),  # causal, two per CU: 8 waves
 ]
 
 
 @pytest.mark.parametrize("args,threads", FORM_CHOICES, ids=[str(a) for a, _ in FORM_CHOICES])
 def test_launch_form_choice_without_gpu(args, threads):
-    assert fa.fa2_launch_info(*args)["threads"] == threads
+    info = fa.fa2_launch_info(*args)
+    assert info["threads"] == threads
+    B, H, N = args[:3]
+    assert info["workgroups"] == B * H * math.ceil(N / info["rows_per_wg"])
+    if args[3] == 128:  # the 4-wave form of d = 128 covers 128 rows
+        assert info["rows_per_wg"] == (256 if threads == 512 else 128)
 
 
 @pytest.mark.parametrize("d", [32, 64, 96, 128, 256, 512, 1024])

@@ -232,3 +232,28 @@ def test_four_wave_form_on_large_grids(gpu_device, d, dtype, causal):
     o_ref, lse_ref = attention_ref(*(wl.to_float64(x, dtype) for x in (q, k, v)), w.softmax_scale(), causal,
                                    rows=rows)
     assert_close(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, dtype, f"4-wave form d{d} {dtype} causal={causal}")
+
+
+D128_FORMS = [(c, dt) for c in (False, True) for dt in (wl.FP16, wl.BF16)]
+
+
+@pytest.mark.parametrize("causal,dtype", D128_FORMS,
+                         ids=[f"{dt}-{'causal' if c else 'full'}" for c, dt in D128_FORMS])
+def test_d128_both_forms(gpu_device, causal, dtype):
+    """d = 128 runs 4 waves of 32 rows (128 rows, two workgroups per CU) on
+    grids of at most one 8-wave workgroup per CU, and 8 waves (256 rows)
+    beyond: parity of both forms, every element on the small grid, sampled
+    rows on the large one."""
+    import exact_attention_21_amd as fa
+    dt = 1 if dtype == wl.BF16 else 0
+    for B, H, N, threads in ((1, 4, 700, 256), (4, 32, 2000, 512)):
+        info = fa.fa2_launch_info(B, H, N, 128, int(causal), dt)
+        assert info["threads"] == threads, (B, H, N, info)
+        w = wl.Workload("f128", B, H, N, 128, dtype, causal)
+        q, k, v = wl.make_inputs(w, seed=23)
+        o, lse = run_gpu(q, k, v, dtype, w.softmax_scale(), causal, gpu_device)
+        rows = np.arange(N) if threads == 256 else sampled_rows(N, seed=5, edge=32, inner=32)
+        o_ref, lse_ref = attention_ref(*(wl.to_float64(x, dtype) for x in (q, k, v)), w.softmax_scale(), causal,
+                                       rows=rows)
+        assert_close(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, dtype,
+                     f"d128 {threads // 64}-wave form {dtype} causal={causal}")
