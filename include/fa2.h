@@ -164,7 +164,10 @@ fa2_status_t fa2_fwd_masked(const void* Q, const void* K, const void* V, void* O
  *
  * Numerics: S, dP, Delta and the accumulators are fp32; P and dS are rounded
  * to `dtype` (to nearest even) before the products that take them, and the
- * gradients once at the end.  The call enqueues two kernels on `stream`
+ * gradients once at the end.  P <= 1 needs no guard; with fp16 the rounded
+ * dS = P (dP - Delta) must stay below 65504 in magnitude (dP is a dot
+ * product of dO and V rows), else dQ and dK of that row and key are not
+ * finite.  The call enqueues two kernels on `stream`
  * (first dQ and the row statistics, then dK and dV), allocates nothing and does not
  * synchronise.  Errors: as for fa2_fwd; FA2_ERR_OVERLAP when dQ, dK, dV or
  * the workspace overlaps an input or one another; FA2_ERR_UNSUPPORTED_HEAD_DIM

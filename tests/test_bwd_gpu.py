@@ -126,3 +126,27 @@ def test_bwd_workspace_holds_row_statistics_and_results_repeat_bit_for_bit(gpu_d
 def test_bwd_on_a_side_stream(gpu_device):
     s = torch.cuda.Stream(device=gpu_device)
     _run((1, 2, 400, 64, wl.BF16, True, None, ONE), gpu_device, stream=s)
+
+
+def _draw_bwd_case(i):
+    rng = np.random.default_rng(5000 + i)
+    d = int(rng.choice((64, 128)))
+    B, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    N = int(rng.integers(1, 700))
+    dtype = wl.FP16 if rng.random() < 0.5 else wl.BF16
+    scale = float(rng.choice([1.0, -1.0]) * rng.uniform(0.3, 1.5) / np.sqrt(d))
+    causal = bool(rng.random() < 0.5)
+    return (B, H, N, d, dtype, causal, scale, ONE)
+
+
+RANDOM_CASES = [_draw_bwd_case(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES,
+                         ids=[f"{i}-b{c[0]}h{c[1]}n{c[2]}d{c[3]}{c[4]}{'c' if c[5] else ''}"
+                              for i, c in enumerate(RANDOM_CASES)])
+def test_bwd_random_shapes(gpu_device, case):
+    """Seeded random batch, heads, length (ragged tails of every kind), head
+    dim, dtype, scale of either sign and mask: every element of dQ, dK, dV
+    within the rounding bound."""
+    _run(case, gpu_device, seed=case[2] + case[3])
