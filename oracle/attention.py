@@ -300,3 +300,43 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool):
             dq[b, h] = c * (ds @ k[b, h])
             dk[b, h] = c * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def attention_bwd_ref_masked(q, k, v, do, scale: float, window_left: int, window_right: int, key_lens=None):
+    """attention_bwd_ref for attention_ref_masked's visibility: the same chain
+    rule with P the softmax over each row's visible keys (``_visible_range``;
+    key lengths clamped to [0, N]).  A row with no visible key has P = 0 and
+    O = 0, so its dQ is 0 and it adds nothing to dK or dV; keys at or past a
+    sequence's length get dK = dV = 0.  Returns (dQ, dK, dV), fp64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    if q.ndim != 4 or any(x.shape != q.shape for x in (k, v, do)):
+        raise ValueError("q, k, v, do must share one [B, H, N, d] shape")
+    b_, h_, n, d = q.shape
+    c = float(np.float32(scale))
+    lens = [n] * b_ if key_lens is None else [min(max(int(x), 0), n) for x in key_lens]
+    if len(lens) != b_:
+        raise ValueError("key_lens must hold one length per batch")
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(q)
+    dv = np.zeros_like(q)
+    j = np.arange(n)[None, :]
+    for b in range(b_):
+        bounds = np.array([_visible_range(i, window_left, window_right, lens[b]) for i in range(n)],
+                          dtype=np.int64).reshape(n, 2)
+        visible = (j >= bounds[:, :1]) & (j < bounds[:, 1:])
+        seen = visible.any(axis=1)
+        for h in range(h_):
+            s = np.where(visible, (q[b, h] @ k[b, h].T) * c, -np.inf)
+            m = np.where(seen, s.max(axis=1), 0.0)
+            e = np.where(visible, np.exp(s - m[:, None]), 0.0)
+            p = e / np.where(seen, e.sum(axis=1), 1.0)[:, None]
+            o = p @ v[b, h]
+            dv[b, h] = p.T @ do[b, h]
+            dp = do[b, h] @ v[b, h].T
+            ds = _score_grad(p, dp, _row_delta(do[b, h], o))
+            dq[b, h] = c * (ds @ k[b, h])
+            dk[b, h] = c * (ds.T @ q[b, h])
+    return dq, dk, dv

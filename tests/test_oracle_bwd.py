@@ -17,6 +17,15 @@ things other than its own formulas.
 * planted mistakes in the oracle (the row term Delta dropped, dS transposed,
   the causal mask missing, the scores transposed, a perturbed exponential,
   the scale dropped) are each caught by at least one of the pins above.
+
+The masked backward (attention_bwd_ref_masked: sliding window and key
+lengths) is pinned by finite differences through the (separately pinned)
+masked forward oracle, including rows that see no key; torch autograd with a
+boolean mask built here from the definition (and dQ = 0 on hidden rows);
+reduction to attention_bwd_ref for no window, the causal window and a window
+wider than N; and padding that changes nothing (K, V rows past a length
+replaced, dK = dV = 0 there).  Planted mistakes: the left bound off by one,
+the key lengths ignored.
 """
 import math
 
@@ -201,3 +210,135 @@ def test_backward_pins_catch_planted_mistakes(monkeypatch, mutant):
 @pytest.mark.parametrize("mutant", sorted(CALL_MUTANTS))
 def test_backward_pins_catch_planted_call_mistakes(mutant):
     assert _caught(CALL_MUTANTS[mutant]) >= 1, f"planted mistake {mutant} went unnoticed"
+
+
+# ---- sliding window and key lengths ------------------------------------------
+from oracle import attention_bwd_ref_masked, attention_ref_masked  # noqa: E402
+
+# (shape, window_left, window_right, key_lens): windows on both sides, one
+# side, none; key lengths with a padded tail, a fully padded sequence, and
+# windows that leave rows with no visible key.
+MASK_CASES = [
+    ((1, 2, 6, 3), 2, 1, None),
+    ((2, 1, 7, 2), -1, 0, [5, 7]),
+    ((2, 1, 6, 4), 1, -1, [3, 0]),
+    ((1, 1, 8, 2), 0, 0, None),
+    ((2, 2, 5, 3), 1, 0, [2, 4]),  # rows 3, 4 of batch 0 see no key
+]
+
+
+def _mask_matrix(n, left, right, key_len):
+    """Test-side visibility, written from the definition: key j is visible to
+    query i iff j < key_len, j >= i - left (left >= 0) and j <= i + right
+    (right >= 0)."""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    vis = j < key_len
+    if left >= 0:
+        vis = vis & (j >= i - left)
+    if right >= 0:
+        vis = vis & (j <= i + right)
+    return vis
+
+
+def check_masked_finite_differences(fn, tol=1e-7):
+    for n_case, (shape, left, right, lens) in enumerate(MASK_CASES):
+        q, k, v, do = _inputs(shape, 200 + n_case)
+        scale = 0.6
+
+        def f(qq, kk, vv):
+            return float(np.sum(do * attention_ref_masked(qq, kk, vv, scale, left, right, lens)[0]))
+
+        got = fn(q, k, v, do, scale, left, right, lens)
+        for which in range(3):
+            args = [q.copy(), k.copy(), v.copy()]
+            g = np.zeros_like(args[which])
+            for idx in np.ndindex(g.shape):
+                base = args[which][idx]
+                args[which][idx] = base + 1e-5
+                fp = f(*args)
+                args[which][idx] = base - 1e-5
+                fm = f(*args)
+                args[which][idx] = base
+                g[idx] = (fp - fm) / 2e-5
+            assert np.max(np.abs(got[which] - g)) <= tol, (shape, left, right, lens, which)
+
+
+def check_masked_against_torch(fn, tol=1e-12):
+    """torch autograd through scaled_dot_product_attention with a boolean
+    mask, on rows that see at least one key (torch gives NaN on the others);
+    the oracle's hidden rows must have dQ = 0."""
+    for n_case, (shape, left, right, lens) in enumerate(MASK_CASES):
+        q, k, v, do = _inputs(shape, 300 + n_case)
+        B, H, N, d = shape
+        scale = 0.6
+        got = fn(q, k, v, do, scale, left, right, lens)
+        for b in range(B):
+            vis = _mask_matrix(N, left, right, N if lens is None else lens[b])
+            seen = vis.any(axis=1)
+            assert np.all(got[0][b][:, ~seen] == 0.0), "hidden rows must have dQ = 0"
+            if not seen.any():
+                assert np.all(got[1][b] == 0.0) and np.all(got[2][b] == 0.0)
+                continue
+            rows = np.nonzero(seen)[0]
+            t = [torch.tensor(x[b:b + 1], requires_grad=True) for x in (q, k, v)]
+            qs = t[0][:, :, rows]
+            o = torch.nn.functional.scaled_dot_product_attention(
+                qs, t[1], t[2], attn_mask=torch.tensor(vis[rows]), scale=float(np.float32(scale)))
+            o.backward(torch.tensor(do[b:b + 1, :, rows]))
+            assert np.max(np.abs(got[0][b][:, rows] - t[0].grad.numpy()[0][:, rows])) <= tol
+            assert np.max(np.abs(got[1][b] - t[1].grad.numpy()[0])) <= tol
+            assert np.max(np.abs(got[2][b] - t[2].grad.numpy()[0])) <= tol
+
+
+def check_masked_reduces_to_unmasked(fn, tol=1e-13):
+    q, k, v, do = _inputs((2, 2, 9, 4), 400)
+    for (left, right), causal in (((-1, -1), False), ((-1, 0), True), ((20, 30), False)):
+        got = fn(q, k, v, do, 0.5, left, right, None)
+        want = attention_bwd_ref(q, k, v, do, 0.5, causal)
+        for a, b in zip(got, want):
+            assert np.max(np.abs(a - b)) <= tol, (left, right)
+
+
+def check_padding_is_inert(fn, tol=1e-13):
+    """K and V rows at or past a sequence's length change nothing; their dK
+    and dV are 0."""
+    q, k, v, do = _inputs((2, 2, 8, 3), 500)
+    lens = [5, 8]
+    got = fn(q, k, v, do, 0.7, 2, -1, lens)
+    k2, v2 = k.copy(), v.copy()
+    k2[0, :, 5:] = 1e3 * _rand(k2[0, :, 5:].shape, 1)
+    v2[0, :, 5:] = -7.0
+    got2 = fn(q, k2, v2, do, 0.7, 2, -1, lens)
+    for a, b in zip(got, got2):
+        assert np.max(np.abs(a - b)) <= tol
+    assert np.all(got[1][0, :, 5:] == 0.0) and np.all(got[2][0, :, 5:] == 0.0)
+
+
+MASKED_CHECKS = (check_masked_finite_differences, check_masked_against_torch, check_masked_reduces_to_unmasked,
+                 check_padding_is_inert)
+
+
+@pytest.mark.parametrize("check", MASKED_CHECKS, ids=lambda c: c.__name__)
+def test_masked_backward_oracle(check):
+    check(attention_bwd_ref_masked)
+
+
+MASKED_MUTANTS = {
+    # The left bound exclusive (one key fewer), and the key lengths ignored.
+    "left_bound_off_by_one": lambda q, k, v, do, s, l, r, lens: attention_bwd_ref_masked(
+        q, k, v, do, s, l - 1 if l > 0 else l, r, lens),
+    "padding_ignored": lambda q, k, v, do, s, l, r, lens: attention_bwd_ref_masked(q, k, v, do, s, l, r, None),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MASKED_MUTANTS))
+def test_masked_backward_pins_catch_planted_mistakes(mutant):
+    caught = 0
+    for check in MASKED_CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                check(MASKED_MUTANTS[mutant])
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"planted mistake {mutant} went unnoticed"
