@@ -26,7 +26,7 @@ FA2_ERR_HIP = 8
 FA2_ERR_TOO_LARGE = 9
 
 # Every symbol include/fa2.h declares.
-EXPORTED = ("fa2_fwd", "fa2_fwd_masked", "fa2_bwd", "fa2_bwd_noalloc", "fa2_status_string",
+EXPORTED = ("fa2_fwd", "fa2_fwd_masked", "fa2_bwd", "fa2_bwd_masked", "fa2_bwd_noalloc", "fa2_status_string",
             "fa2_launch_info")
 
 _lock = threading.Lock()
@@ -51,6 +51,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.fa2_fwd_masked.restype = ctypes.c_int
     lib.fa2_bwd.argtypes = [vp] * 10 + [i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
     lib.fa2_bwd.restype = ctypes.c_int
+    lib.fa2_bwd_masked.argtypes = [vp] * 10 + [i64, i64, i64, i64, ctypes.c_float, i64, i64, vp, ctypes.c_int, vp]
+    lib.fa2_bwd_masked.restype = ctypes.c_int
     lib.fa2_bwd_noalloc.argtypes = [vp] * 9 + [i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
     lib.fa2_bwd_noalloc.restype = ctypes.c_int
     lib.fa2_status_string.argtypes = [ctypes.c_int]
@@ -94,6 +96,14 @@ def fa2_bwd(Q: int, K: int, V: int, O: int, dO: int, LSE: int, dQ: int, dK: int,
     """Same arguments and status as the C function; pointers are integers."""
     return library().fa2_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, B, H, N, d, scale, int(is_causal),
                              int(dtype), stream)
+
+
+def fa2_bwd_masked(Q: int, K: int, V: int, O: int, dO: int, LSE: int, dQ: int, dK: int, dV: int, workspace: int,
+                   B: int, H: int, N: int, d: int, scale: float, window_left: int, window_right: int,
+                   key_lens: int | None, dtype: int, stream: int) -> int:
+    """Same arguments and status as the C function; pointers are integers (key_lens may be None)."""
+    return library().fa2_bwd_masked(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, B, H, N, d, scale,
+                                    int(window_left), int(window_right), key_lens, int(dtype), stream)
 
 
 def fa2_bwd_noalloc(Q: int, K: int, V: int, O: int, dO: int, LSE: int, dQ: int, dK: int, dV: int,

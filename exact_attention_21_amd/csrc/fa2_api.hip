@@ -355,12 +355,12 @@ fa2_status_t checked_launch(const void* Q, const void* K, const void* V, void* O
 // Waves per workgroup of the two backward kernels (32 rows each).
 constexpr int kBwdWaves = 4;
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, int MASK>
 hipError_t launch_bwd(const fa2::BwdParams& base, hipStream_t stream) {
-  using KQ = fa2::Fa2BwdQ<D, kBwdWaves, BF16, CAUSAL>;
-  using KKV = fa2::Fa2BwdKV<D, kBwdWaves, BF16, CAUSAL>;
-  auto kq = fa2::fa2_bwd_q_kernel<D, kBwdWaves, BF16, CAUSAL>;
-  auto kkv = fa2::fa2_bwd_kv_kernel<D, kBwdWaves, BF16, CAUSAL>;
+  using KQ = fa2::Fa2BwdQ<D, kBwdWaves, BF16, MASK>;
+  using KKV = fa2::Fa2BwdKV<D, kBwdWaves, BF16, MASK>;
+  auto kq = fa2::fa2_bwd_q_kernel<D, kBwdWaves, BF16, MASK>;
+  auto kkv = fa2::fa2_bwd_kv_kernel<D, kBwdWaves, BF16, MASK>;
   const KernelSetup sq = kernel_setup<KQ>((const void*)kq, KQ::THREADS, KQ::LDS_BYTES);
   if (sq.err != hipSuccess) return sq.err;
   const KernelSetup skv = kernel_setup<KKV>((const void*)kkv, KKV::THREADS, KKV::LDS_BYTES);
@@ -377,18 +377,27 @@ hipError_t launch_bwd(const fa2::BwdParams& base, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool BF16, bool CAUSAL>
+template <bool BF16, int MASK>
 hipError_t launch_bwd_d(int64_t d, const fa2::BwdParams& p, hipStream_t stream) {
-  return d == 64 ? launch_bwd<64, BF16, CAUSAL>(p, stream) : launch_bwd<128, BF16, CAUSAL>(p, stream);
+  return d == 64 ? launch_bwd<64, BF16, MASK>(p, stream) : launch_bwd<128, BF16, MASK>(p, stream);
+}
+
+template <bool BF16>
+hipError_t launch_bwd_mask(int mask, int64_t d, const fa2::BwdParams& p, hipStream_t stream) {
+  switch (mask) {
+    case fa2::kMaskNone: return launch_bwd_d<BF16, fa2::kMaskNone>(d, p, stream);
+    case fa2::kMaskCausal: return launch_bwd_d<BF16, fa2::kMaskCausal>(d, p, stream);
+    default: return launch_bwd_d<BF16, fa2::kMaskGeneral>(d, p, stream);
+  }
 }
 
 // Rows per workgroup of either backward kernel (the grid-size limit).
 constexpr int64_t kBwdRows = 32 * kBwdWaves;
-static_assert(fa2::Fa2BwdQ<64, kBwdWaves, false, false>::BQ == kBwdRows &&
-                  fa2::Fa2BwdKV<64, kBwdWaves, false, false>::BK == kBwdRows,
+static_assert(fa2::Fa2BwdQ<64, kBwdWaves, false, 0>::BQ == kBwdRows &&
+                  fa2::Fa2BwdKV<64, kBwdWaves, false, 0>::BK == kBwdRows,
               "backward tiles");
-static_assert(kBwdRows <= kPadRows && fa2::Fa2BwdQ<64, kBwdWaves, false, false>::BC <= kPadRows &&
-                  fa2::Fa2BwdKV<64, kBwdWaves, false, false>::BQ <= kPadRows,
+static_assert(kBwdRows <= kPadRows && fa2::Fa2BwdQ<64, kBwdWaves, false, 0>::BC <= kPadRows &&
+                  fa2::Fa2BwdKV<64, kBwdWaves, false, 0>::BQ <= kPadRows,
               "backward rows past N stay within the padded slice");
 
 fa2_status_t bwd_check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
@@ -440,7 +449,8 @@ float* scratch_workspace(int64_t floats, fa2_status_t* err) {
 // check has passed; otherwise `workspace` is the caller's.
 fa2_status_t bwd_checked_launch(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                                 const float* LSE, void* dQ, void* dK, void* dV, float* workspace, int64_t B,
-                                int64_t H, int64_t N, int64_t d, float scale, int is_causal, int dtype, void* stream,
+                                int64_t H, int64_t N, int64_t d, float scale, int mask, int64_t wl, int64_t wr,
+                                const int32_t* key_lens, int dtype, void* stream,
                                 float* (*get_scratch)(int64_t, fa2_status_t*)) {
   if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA2_ERR_NULL_POINTER;
   const fa2_status_t st = bwd_check_shape(B, H, N, d, dtype);
@@ -449,15 +459,15 @@ fa2_status_t bwd_checked_launch(const void* Q, const void* K, const void* V, con
   if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)dO | (uintptr_t)dQ | (uintptr_t)dK |
        (uintptr_t)dV) & 15u)
     return FA2_ERR_MISALIGNED;
-  if (((uintptr_t)LSE | (uintptr_t)workspace) & 3u) return FA2_ERR_MISALIGNED;
+  if (((uintptr_t)LSE | (uintptr_t)workspace | (uintptr_t)key_lens) & 3u) return FA2_ERR_MISALIGNED;
   const size_t tb = (size_t)(B * H * N * d) * 2;
   const size_t rb = (size_t)(B * H * N) * 4;
-  const void* ins[6] = {Q, K, V, O, dO, LSE};
-  const size_t in_bytes[6] = {tb, tb, tb, tb, tb, rb};
+  const void* ins[7] = {Q, K, V, O, dO, LSE, key_lens};
+  const size_t in_bytes[7] = {tb, tb, tb, tb, tb, rb, key_lens ? (size_t)B * 4 : 0};
   const void* outs[4] = {dQ, dK, dV, workspace};
   const size_t out_bytes[4] = {tb, tb, tb, workspace ? 2 * rb : 0};
   for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
+    for (int j = 0; j < 7; ++j)
       if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA2_ERR_OVERLAP;
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA2_ERR_OVERLAP;
@@ -483,12 +493,14 @@ fa2_status_t bwd_checked_launch(const void* Q, const void* K, const void* V, con
   p.n_tiles = 0;  // set per kernel
   p.scale = scale;
   p.c2 = scale * 1.4426950408889634f;
+  // A bound of N or more hides nothing (N < kNoBound by the size limits).
+  p.wl = (wl < 0 || wl >= N) ? fa2::kNoBound : (int)wl;
+  p.wr = (wr < 0 || wr >= N) ? fa2::kNoBound : (int)wr;
+  p.key_lens = key_lens;
+  p.heads = (int)H;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t err;
-  if (dtype == FA2_DTYPE_BF16)
-    err = is_causal ? launch_bwd_d<true, true>(d, p, s) : launch_bwd_d<true, false>(d, p, s);
-  else
-    err = is_causal ? launch_bwd_d<false, true>(d, p, s) : launch_bwd_d<false, false>(d, p, s);
+  const hipError_t err = dtype == FA2_DTYPE_BF16 ? launch_bwd_mask<true>(mask, d, p, s)
+                                                 : launch_bwd_mask<false>(mask, d, p, s);
   return err == hipSuccess ? FA2_OK : FA2_ERR_HIP;
 }
 
@@ -557,15 +569,34 @@ fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O,
                      void* dQ, void* dK, void* dV, float* workspace, int64_t B, int64_t H, int64_t N, int64_t d,
                      float scale, int is_causal, int dtype, void* stream) {
   if (!workspace) return FA2_ERR_NULL_POINTER;
-  return bwd_checked_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, B, H, N, d, scale, is_causal, dtype, stream,
-                            nullptr);
+  return bwd_checked_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, B, H, N, d, scale,
+                            is_causal ? fa2::kMaskCausal : fa2::kMaskNone, -1, is_causal ? 0 : -1, nullptr, dtype,
+                            stream, nullptr);
 }
 
 fa2_status_t fa2_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                              const float* LSE, void* dQ, void* dK, void* dV, int64_t B, int64_t H, int64_t N,
                              int64_t d, float scale, int is_causal, int dtype, void* stream) {
-  return bwd_checked_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, nullptr, B, H, N, d, scale, is_causal, dtype, stream,
-                            &scratch_workspace);
+  return bwd_checked_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, nullptr, B, H, N, d, scale,
+                            is_causal ? fa2::kMaskCausal : fa2::kMaskNone, -1, is_causal ? 0 : -1, nullptr, dtype,
+                            stream, &scratch_workspace);
+}
+
+fa2_status_t fa2_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                            const float* LSE, void* dQ, void* dK, void* dV, float* workspace, int64_t B, int64_t H,
+                            int64_t N, int64_t d, float scale, int64_t window_left, int64_t window_right,
+                            const int32_t* key_lens, int dtype, void* stream) {
+  if (!workspace) return FA2_ERR_NULL_POINTER;
+  // No window and no key lengths run the unmasked kernels, a window with no
+  // left bound and right bound 0 (no key lengths) the causal ones; anything
+  // else the general mask.
+  const bool no_left = window_left < 0 || window_left >= N;
+  const bool no_right = window_right < 0 || window_right >= N;
+  int mask = fa2::kMaskGeneral;
+  if (!key_lens && no_left && no_right) mask = fa2::kMaskNone;
+  if (!key_lens && no_left && window_right == 0) mask = fa2::kMaskCausal;
+  return bwd_checked_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, B, H, N, d, scale, mask, window_left,
+                            window_right, key_lens, dtype, stream, nullptr);
 }
 
 }  // extern "C"

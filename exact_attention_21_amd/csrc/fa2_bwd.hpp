@@ -51,6 +51,8 @@
 
 #include "fa2_kernel.hpp"
 
+#include <type_traits>
+
 namespace fa2 {
 
 struct BwdParams {
@@ -69,9 +71,27 @@ struct BwdParams {
   int n_tiles;  // stationary tiles per (batch*head) slice of the kernel launched
   float scale;  // softmax scale (any finite value)
   float c2;     // scale * log2(e): scores to the base-2 exponent domain
+  // General mask (the forward's): key j is visible to query i iff
+  // j < key_len(b), j >= i - wl and j <= i + wr (kNoBound: no bound).
+  int wl;
+  int wr;
+  const int* key_lens;  // B lengths (clamped to [0, N]) or null
+  int heads;            // H, to find the batch of a (batch*head) slice
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Calls f(std::integral_constant<int, I>{}) for I = B .. E-1 in order: the
+// pipelines below index their register arrays with these compile-time
+// values, which does not depend on the loop unroller's size limits (a loop
+// it left rolled would put the arrays in scratch memory).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Position of 16-byte chunk c of row r of a streamed tile: c ^ bwd_swz(r).
 // A tile is read two ways:
@@ -214,8 +234,10 @@ struct BwdBase {
 };
 
 // ---- dQ (and Delta): query rows stationary, key tiles streamed ----------
-template <int D, int NW, bool BF16, bool CAUSAL>
+template <int D, int NW, bool BF16, int MASK>
 struct Fa2BwdQ : BwdBase<D, BF16> {
+  static constexpr bool CAUSAL = MASK == kMaskCausal;
+  static constexpr bool GENERAL = MASK == kMaskGeneral;
   using Base = BwdBase<D, BF16>;
   using Base::CPR;
   using Base::DB;
@@ -248,8 +270,8 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
     const int h = lane >> 5;
     const int step = blockIdx.x / p.bh;
     const int bh = blockIdx.x - step * p.bh;
-    // Causal: the last query tiles (the most keys) first.
-    const int qtile = CAUSAL ? p.n_tiles - 1 - step : step;
+    // Under a mask the last query tiles (causal: the most keys) first.
+    const int qtile = MASK != kMaskNone ? p.n_tiles - 1 - step : step;
     const int n = p.n;
     const int q0 = qtile * BQ;
     const int qw0 = q0 + 32 * wave;
@@ -309,26 +331,49 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
       toff[db][1] = Base::tr_off(lane, db, 1);
     }
     const St st(tid);
-    const u32x4 wk = rsrc_words(p.k, slice * 2, bytes);
-    const u32x4 wv = rsrc_words(p.v, slice * 2, bytes);
+    // K and V are range-checked at the keys present (N, or the sequence's
+    // key length: rows past it may hold anything and are never read).
+    int klen = n, wl = kNoBound, wr = kNoBound;
+    if constexpr (GENERAL) {
+      if (p.key_lens) klen = min(max(p.key_lens[bh / p.heads], 0), n);
+      wl = p.wl;
+      wr = p.wr;
+    }
+    const u32x4 wk = rsrc_words(p.k, slice * 2, (uint32_t)klen * D * 2);
+    const u32x4 wv = rsrc_words(p.v, slice * 2, (uint32_t)klen * D * 2);
 
     f32x16 dq[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
 
-    // Key tiles [0, ntiles); those from `plain` on hold a key past N or past
-    // some row of the workgroup (causal) and take the per-element mask.
-    const int kend = CAUSAL ? min(n, q0 + BQ) : n;
-    const int ntiles = (kend + BC - 1) / BC;
-    const int plain = min(ntiles, CAUSAL ? min(n, q0 + 1) / BC : n / BC);
-    auto tile = [&](int t, auto masked_c) {
+    // Key tiles that some row of the workgroup sees: [tfirst, tend).  A tile
+    // takes the per-element mask when it holds a key past N (or the key
+    // length) or a key some row of the workgroup does not see.
+    int kbeg = 0, kend = n;
+    if constexpr (CAUSAL) kend = min(n, q0 + BQ);
+    if constexpr (GENERAL) {
+      kbeg = max(0, q0 - wl);
+      kend = min(klen, q0 + BQ + wr);  // q0 + BQ - 1 + wr + 1
+    }
+    const int tfirst = kbeg / BC;
+    const int tend = kend > kbeg ? (kend + BC - 1) / BC : tfirst;
+    // The masked tiles are a prefix [tfirst, m1) (keys before the last row's
+    // left bound) and a suffix [m2, tend) (keys past the key length, or
+    // after the first row's right bound; causal: after the first row).
+    const int lb = q0 + BQ - 1 - wl;  // tiles starting before this key are masked
+    const int m1 = min(tend, max(tfirst, GENERAL && lb > 0 ? (lb + BC - 1) / BC : tfirst));
+    int rcut = klen / BC;  // first tile holding a key at or past the key length
+    if constexpr (CAUSAL) rcut = min(rcut, (q0 + 1) / BC);
+    if constexpr (GENERAL) rcut = min(rcut, (int)(((int64_t)q0 + wr + 1) / BC));
+    const int m2 = min(tend, max(m1, rcut));
+    auto tile = [&](int t, auto masked_c) __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(masked_c)::value;
       Base::dma_wait();
       __syncthreads();
-      const lds_char* sk = lds + (t & 1) * SLOTB;
+      const lds_char* sk = lds + ((t - tfirst) & 1) * SLOTB;
       const lds_char* sv = sk + TILEB;
-      if (t + 1 < ntiles) {
-        const lds_char* nk = lds + ((t + 1) & 1) * SLOTB;
+      if (t + 1 < tend) {
+        const lds_char* nk = lds + ((t + 1 - tfirst) & 1) * SLOTB;
         st.stage(wk, nk, (t + 1) * BC);
         st.stage(wv, nk + TILEB, (t + 1) * BC);
       }
@@ -337,7 +382,7 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
       u32x4 b[2][2];        // packed dS^T of blocks of either parity
       // A operand of MFMA `pos` of the step that works on block j: S(j+1)
       // and dP(j+1) (K and V rows), then dQ(j-1) (K^T, transposed read).
-      auto frag = [&](int j, int pos) -> u32x4 {
+      auto frag = [&](int j, int pos) __attribute__((always_inline)) -> u32x4 {
         if (pos < NSD) {
           const int kb = j + 1, ks = pos / 2;
           return Base::lds16((pos % 2 ? sv : sk) + poff[ks] + kb * 32 * ROWB);
@@ -346,8 +391,8 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
         const int rows = (kb * 32 + 16 * u) * ROWB;
         return Base::tr_frag(sk, toff[db][0] + rows, toff[db][1] + rows);
       };
-      auto active = [&](int j, int pos) { return pos < NSD ? j + 1 < KB : j >= 1; };
-      auto issue = [&](int j, int pos, const u32x4& a) {
+      auto active = [&](int j, int pos) __attribute__((always_inline)) { return pos < NSD ? j + 1 < KB : j >= 1; };
+      auto issue = [&](int j, int pos, const u32x4& a) __attribute__((always_inline)) {
         if (pos < NSD) {
           const int kb = j + 1, ks = pos / 2;
           if (pos % 2 == 0)
@@ -361,7 +406,7 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
       };
       // VALU work of pair c of block j: registers 2c, 2c+1 (keys
       // kr0 + 8(r/4) + 4h + r%4 of row myq).
-      auto pair = [&](int j, int c) {
+      auto pair = [&](int j, int c) __attribute__((always_inline)) {
         float x[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -369,52 +414,64 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
           x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j % 2][r], p.c2, nl2));
           if constexpr (MASKED) {
             const int key = k0 + 32 * j + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key >= n || (CAUSAL && key > myq)) x[e] = 0.f;
+            const bool hide = GENERAL ? (key >= klen || key > myq + wr || key < myq - wl)
+                                      : (key >= n || (CAUSAL && key > myq));
+            if (hide) x[e] = 0.f;
           }
           x[e] *= dp[j % 2][r];
         }
         b[j % 2][c / 4][c % 4] = pack2<BF16>(x[0], x[1]);
       };
       // Prologue: S(0) and dP(0).
-#pragma unroll
-      for (int pos = 0; pos < NSD; ++pos) {
+      static_for<0, NSD>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int pos = decltype(pc)::value;
         const u32x4 a = frag(-1, pos);
         issue(-1, pos, a);
-      }
-#pragma unroll
-      for (int j = 0; j < KB; ++j) {
+      });
+      static_for<0, KB>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
         u32x4 fr[NPOS];
-#pragma unroll
-        for (int pos = 0; pos < PF && pos < NPOS; ++pos)
+        static_for<0, (PF < NPOS ? PF : NPOS)>([&](auto pc) __attribute__((always_inline)) {
+          constexpr int pos = decltype(pc)::value;
           if (active(j, pos)) fr[pos] = frag(j, pos);
-#pragma unroll
-        for (int pos = 0; pos < NPOS; ++pos) {
-          if (pos + PF < NPOS && active(j, pos + PF)) fr[pos + PF] = frag(j, pos + PF);
+        });
+        static_for<0, NPOS>([&](auto pc) __attribute__((always_inline)) {
+          constexpr int pos = decltype(pc)::value;
+          if constexpr (pos + PF < NPOS) {
+            if (active(j, pos + PF)) fr[pos + PF] = frag(j, pos + PF);
+          }
           if (active(j, pos)) issue(j, pos, fr[pos]);
-#pragma unroll
-          for (int c = pos * 8 / NPOS; c < (pos + 1) * 8 / NPOS; ++c) pair(j, c);
+          static_for<pos * 8 / NPOS, (pos + 1) * 8 / NPOS>(
+              [&](auto cc) __attribute__((always_inline)) { pair(j, decltype(cc)::value); });
           __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+        });
+      });
       // Epilogue: dQ(KB-1).
-#pragma unroll
-      for (int pos = NSD; pos < NPOS; ++pos) {
+      static_for<NSD, NPOS>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int pos = decltype(pc)::value;
         const u32x4 a = frag(KB, pos);
         issue(KB, pos, a);
-      }
+      });
     };
-    st.stage(wk, lds, 0);
-    st.stage(wv, lds + TILEB, 0);
-    int t = 0;
-    for (; t < plain; ++t) tile(t, std::false_type{});
-    for (; t < ntiles; ++t) tile(t, std::true_type{});
+    if (tend > tfirst) {
+      st.stage(wk, lds, tfirst * BC);
+      st.stage(wv, lds + TILEB, tfirst * BC);
+    }
+    int t = tfirst;
+    if constexpr (GENERAL) {
+      for (; t < m1; ++t) tile(t, std::true_type{});
+    }
+    for (; t < m2; ++t) tile(t, std::false_type{});
+    for (; t < tend; ++t) tile(t, std::true_type{});
     Base::store_grad(rdq, dq, myq, lane, p.scale);
   }
 };
 
 // ---- dK and dV: key rows stationary, query tiles streamed -----------------
-template <int D, int NW, bool BF16, bool CAUSAL>
+template <int D, int NW, bool BF16, int MASK>
 struct Fa2BwdKV : BwdBase<D, BF16> {
+  static constexpr bool CAUSAL = MASK == kMaskCausal;
+  static constexpr bool GENERAL = MASK == kMaskGeneral;
   using Base = BwdBase<D, BF16>;
   using Base::CPR;
   using Base::DB;
@@ -481,11 +538,20 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
     const int k0 = ktile * BK;
     const int kw0 = k0 + 32 * wave;
     const int mykey = kw0 + (lane & 31);
+    int klen = n, wl = kNoBound, wr = kNoBound;
+    if constexpr (CAUSAL) wr = 0;
+    if constexpr (GENERAL) {
+      if (p.key_lens) klen = min(max(p.key_lens[bh / p.heads], 0), n);
+      wl = p.wl;
+      wr = p.wr;
+    }
 
     const size_t slice = (size_t)bh * (size_t)n * D;
     const uint32_t bytes = (uint32_t)n * D * 2;
-    const auto rk = make_rsrc((const char*)p.k + slice * 2, bytes);
-    const auto rv = make_rsrc((const char*)p.v + slice * 2, bytes);
+    // K and V rows at or past the key length (padding) are never read; their
+    // dK and dV are 0 (every such key is hidden from every row).
+    const auto rk = make_rsrc((const char*)p.k + slice * 2, (uint32_t)klen * D * 2);
+    const auto rv = make_rsrc((const char*)p.v + slice * 2, (uint32_t)klen * D * 2);
     const auto rdk = make_rsrc((char*)p.dk + slice * 2, bytes);
     const auto rdv = make_rsrc((char*)p.dv + slice * 2, bytes);
 
@@ -511,7 +577,7 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
     const u32x4 wdo = rsrc_words(p.dout, slice * 2, bytes);
     // The row statistics the dQ kernel left in the workspace.
     const u32x4 wd = rsrc_words(p.delta, (size_t)bh * n * 4, (uint32_t)n * 4);
-    const u32x4 wl = rsrc_words(p.delta, ((size_t)p.bh + bh) * n * 4, (uint32_t)n * 4);
+    const u32x4 wl2 = rsrc_words(p.delta, ((size_t)p.bh + bh) * n * 4, (uint32_t)n * 4);
 
     f32x16 dv[DB], dk[DB];
 #pragma unroll
@@ -524,25 +590,42 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
       }
     }
 
-    // Query tiles that see some key of the workgroup: [tfirst, tend); those
-    // before `mask_end` hold a row before some key (causal) and take the
-    // per-element mask.  Rows past N load as zeros: Q, dO and both
-    // statistics 0, so P = 1 meets dO = 0 and dP - Delta = 0, and the row
-    // adds exactly nothing.
-    const int tfirst = CAUSAL ? k0 / BQ : 0;
-    const int tend = (n + BQ - 1) / BQ;
-    const int mask_end = CAUSAL ? min(tend, (k0 + BK - 1 + BQ - 1) / BQ) : tfirst;
-    auto stage = [&](int t, const lds_char* dst) {
+    // Query tiles with a row that sees some key of the workgroup: [tfirst,
+    // tend).  A tile takes the per-element mask when some (row, key) pair of
+    // it is hidden: a key past the key length, a key after a row's right
+    // bound (causal: after the row) or before its left bound.  Rows past N
+    // load as zeros: Q, dO and both statistics 0, so P = 1 meets dO = 0 and
+    // dP - Delta = 0, and the row adds exactly nothing.
+    int rbeg = 0, rend = n;
+    if constexpr (MASK != kMaskNone) {
+      rbeg = max(0, k0 - wr);
+      rend = min(n, k0 + BK + wl);  // k0 + BK - 1 + wl + 1
+      if (k0 >= klen) rend = rbeg;  // every key of the workgroup is padding
+    }
+    const int tfirst = rbeg / BQ;
+    const int tend = rend > rbeg ? (rend + BQ - 1) / BQ : tfirst;
+    // The masked tiles are a prefix [tfirst, m1) (rows before the last key's
+    // right bound: causal, rows before the last key) and a suffix [m2, tend)
+    // (rows past the first key's left bound); all of them when the
+    // workgroup holds a key past the key length.
+    int m1 = tfirst, m2 = tend;
+    if constexpr (MASK != kMaskNone) {
+      const int rb = k0 + BK - 1 - wr;  // tiles starting before this row are masked
+      m1 = min(tend, max(tfirst, rb > 0 ? (rb + BQ - 1) / BQ : tfirst));
+      m2 = min(tend, max(m1, (int)(((int64_t)k0 + wl + 1) / BQ)));
+      if (k0 + BK > klen) m1 = m2 = tend;
+    }
+    auto stage = [&](int t, const lds_char* dst) __attribute__((always_inline)) {
       st.stage(wq, dst, t * BQ);
       st.stage(wdo, dst + TILEB, t * BQ);
       // Wave 0: -LSE * log2(e) of the tile's rows; wave 1: -Delta.
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        if (wave == 0) Base::dma4(wl, dst + 2 * TILEB + half * 256, (t * BQ + 64 * half + lane) * 4);
+        if (wave == 0) Base::dma4(wl2, dst + 2 * TILEB + half * 256, (t * BQ + 64 * half + lane) * 4);
         if (wave == 1) Base::dma4(wd, dst + 2 * TILEB + BQ * 4 + half * 256, (t * BQ + 64 * half + lane) * 4);
       }
     };
-    auto tile = [&](int t, auto masked_c) {
+    auto tile = [&](int t, auto masked_c) __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(masked_c)::value;
       Base::dma_wait();
       __syncthreads();
@@ -556,7 +639,7 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
       u32x4 pb[2][2], sb[2][2]; // packed P and dS of blocks of either parity
       // Row statistics of block qb in accumulator order: register r holds
       // tile row 32qb + 8(r/4) + 4h + r%4, four 16-byte reads.
-      auto stats = [&](int qb, int which) -> f32x16 {
+      auto stats = [&](int qb, int which) __attribute__((always_inline)) -> f32x16 {
         f32x16 out;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -568,7 +651,7 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
       };
       f32x16 ndel;  // -Delta of the block whose dP is being accumulated
       // A operand of MFMA `pos` of the step that works on block j.
-      auto frag = [&](int j, int pos) -> u32x4 {
+      auto frag = [&](int j, int pos) __attribute__((always_inline)) -> u32x4 {
         if (pos < NG) {
           const int qb = j - 1, u = pos / (2 * DB), db = (pos % (2 * DB)) / 2;
           const int rows = (qb * 32 + 16 * u) * ROWB;
@@ -577,8 +660,8 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
         const int qb = j + 1, ks = (pos - NG) / 2;
         return Base::lds16(((pos - NG) % 2 ? sdo : sq) + poff[ks] + qb * 32 * ROWB);
       };
-      auto active = [&](int j, int pos) { return pos < NG ? j >= 1 : j + 1 < QBLK; };
-      auto issue = [&](int j, int pos, const u32x4& a) {
+      auto active = [&](int j, int pos) __attribute__((always_inline)) { return pos < NG ? j >= 1 : j + 1 < QBLK; };
+      auto issue = [&](int j, int pos, const u32x4& a) __attribute__((always_inline)) {
         if (pos < NG) {
           const int qb = j - 1, u = pos / (2 * DB), db = (pos % (2 * DB)) / 2;
           if (pos % 2 == 0)
@@ -595,14 +678,15 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
       };
       // VALU work of pair c of block j: registers 2c, 2c+1 (rows
       // q0 + 32j + 8(r/4) + 4h + r%4 against key mykey).
-      auto pair = [&](int j, int c) {
+      auto pair = [&](int j, int c) __attribute__((always_inline)) {
         float x[2], y[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * c + e;
           x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j % 2][r], p.c2, nl2[j % 2][r]));
           if constexpr (MASKED) {
-            if (mykey > q0 + 32 * j + 8 * (r >> 2) + 4 * h + (r & 3)) x[e] = 0.f;
+            const int row = q0 + 32 * j + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (mykey >= klen || mykey > row + wr || mykey < row - wl) x[e] = 0.f;
           }
           y[e] = x[e] * dp[j % 2][r];
         }
@@ -612,41 +696,49 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
       // Prologue: the statistics of block 0, S(0) and dP(0).
       nl2[0] = stats(0, 0);
       ndel = stats(0, 1);
-#pragma unroll
-      for (int pos = NG; pos < NPOS; ++pos) {
+      static_for<NG, NPOS>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int pos = decltype(pc)::value;
         const u32x4 a = frag(-1, pos);
         issue(-1, pos, a);
-      }
-#pragma unroll
-      for (int j = 0; j < QBLK; ++j) {
-        if (j + 1 < QBLK) {
+      });
+      static_for<0, QBLK>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j + 1 < QBLK) {
           nl2[(j + 1) % 2] = stats(j + 1, 0);
           ndel = stats(j + 1, 1);
         }
         u32x4 fr[NPOS];
-#pragma unroll
-        for (int pos = 0; pos < PF && pos < NPOS; ++pos)
+        static_for<0, (PF < NPOS ? PF : NPOS)>([&](auto pc) __attribute__((always_inline)) {
+          constexpr int pos = decltype(pc)::value;
           if (active(j, pos)) fr[pos] = frag(j, pos);
-#pragma unroll
-        for (int pos = 0; pos < NPOS; ++pos) {
-          if (pos + PF < NPOS && active(j, pos + PF)) fr[pos + PF] = frag(j, pos + PF);
+        });
+        static_for<0, NPOS>([&](auto pc) __attribute__((always_inline)) {
+          constexpr int pos = decltype(pc)::value;
+          if constexpr (pos + PF < NPOS) {
+            if (active(j, pos + PF)) fr[pos + PF] = frag(j, pos + PF);
+          }
           if (active(j, pos)) issue(j, pos, fr[pos]);
-#pragma unroll
-          for (int c = pos * 8 / NPOS; c < (pos + 1) * 8 / NPOS; ++c) pair(j, c);
+          static_for<pos * 8 / NPOS, (pos + 1) * 8 / NPOS>(
+              [&](auto cc) __attribute__((always_inline)) { pair(j, decltype(cc)::value); });
           __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+        });
+      });
       // Epilogue: dV(QBLK-1) and dK(QBLK-1).
-#pragma unroll
-      for (int pos = 0; pos < NG; ++pos) {
+      static_for<0, NG>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int pos = decltype(pc)::value;
         const u32x4 a = frag(QBLK, pos);
         issue(QBLK, pos, a);
-      }
+      });
     };
-    stage(tfirst, lds);
+    if (tend > tfirst) stage(tfirst, lds);
     int t = tfirst;
-    for (; t < mask_end; ++t) tile(t, std::true_type{});
-    for (; t < tend; ++t) tile(t, std::false_type{});
+    if constexpr (MASK != kMaskNone) {
+      for (; t < m1; ++t) tile(t, std::true_type{});
+    }
+    for (; t < m2; ++t) tile(t, std::false_type{});
+    if constexpr (GENERAL) {
+      for (; t < tend; ++t) tile(t, std::true_type{});
+    }
     settle_acc(dv, dk);
     Base::store_grad(rdv, dv, mykey, lane, 1.0f);
     Base::store_grad(rdk, dk, mykey, lane, p.scale);
@@ -655,18 +747,18 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
 
 // Two waves per SIMD (256 registers each), so that one wave's VALU work
 // issues beside the other's MFMAs.
-template <int D, int NW, bool BF16, bool CAUSAL>
+template <int D, int NW, bool BF16, int MASK>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
     fa2_bwd_q_kernel(const BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) char lds_generic[];
-  Fa2BwdQ<D, NW, BF16, CAUSAL>::run(
+  Fa2BwdQ<D, NW, BF16, MASK>::run(
       p, (__attribute__((address_space(3))) char*)(__attribute__((address_space(3))) void*)lds_generic);
 }
 
-template <int D, int NW, bool BF16, bool CAUSAL>
+template <int D, int NW, bool BF16, int MASK>
 __global__ void __launch_bounds__(NW * 64) fa2_bwd_kv_kernel(const BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) char lds_generic[];
-  Fa2BwdKV<D, NW, BF16, CAUSAL>::run(
+  Fa2BwdKV<D, NW, BF16, MASK>::run(
       p, (__attribute__((address_space(3))) char*)(__attribute__((address_space(3))) void*)lds_generic);
 }
 

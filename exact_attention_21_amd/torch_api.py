@@ -9,7 +9,8 @@ import math
 
 import torch
 
-from ._binding import FA2_DTYPE_BF16, FA2_DTYPE_FP16, FA2_OK, Fa2Error, fa2_bwd, fa2_fwd, fa2_fwd_masked
+from ._binding import (FA2_DTYPE_BF16, FA2_DTYPE_FP16, FA2_OK, Fa2Error, fa2_bwd, fa2_bwd_masked, fa2_fwd,
+                       fa2_fwd_masked)
 
 _DTYPES = {torch.float16: FA2_DTYPE_FP16, torch.bfloat16: FA2_DTYPE_BF16}
 
@@ -76,13 +77,16 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | No
 
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
              do: torch.Tensor, scale: float | None = None, causal: bool = False,
-             workspace: torch.Tensor | None = None, out: tuple | None = None):
+             workspace: torch.Tensor | None = None, out: tuple | None = None,
+             window: tuple[int, int] | None = None, key_lens: torch.Tensor | None = None):
     """Gradients (dQ, dK, dV) of the attention of ``forward`` given dO.
 
     q, k, v, o, do: [B, H, N, d] fp16/bf16 tensors of one dtype on one GPU
     (d = 64 or 128); o and lse are forward's outputs for the same q, k, v,
     scale and causal.  ``workspace`` (float32, 2*B*H*N elements) and ``out``
     (a (dq, dk, dv) tuple of tensors like q) may be given to reuse buffers.
+    ``window`` and ``key_lens`` are those of ``forward`` (through
+    ``fa2_bwd_masked``; o and lse must then come from the masked forward).
     The two kernels are enqueued on torch's current stream.
     """
     ts = (q, k, v, o, do)
@@ -110,11 +114,25 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if any(t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device
            for t in out):
         raise ValueError("out must be three contiguous tensors like q")
+    masked = window is not None or key_lens is not None
+    if masked:
+        left, right = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+        if causal:
+            right = 0 if right < 0 else min(right, 0)
+        lens_ptr = None
+        if key_lens is not None:
+            if key_lens.shape != (B,) or key_lens.dtype != torch.int32 or not key_lens.is_contiguous() \
+                    or key_lens.device != q.device:
+                raise ValueError("key_lens must be a contiguous int32 [B] tensor on q's device")
+            lens_ptr = key_lens.data_ptr()
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        st = fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                     B, H, N, d, float(scale), int(bool(causal)), _DTYPES[q.dtype], stream)
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr())
+        if masked:
+            st = fa2_bwd_masked(*ptrs, B, H, N, d, float(scale), left, right, lens_ptr, _DTYPES[q.dtype], stream)
+        else:
+            st = fa2_bwd(*ptrs, B, H, N, d, float(scale), int(bool(causal)), _DTYPES[q.dtype], stream)
     if st != FA2_OK:
-        raise Fa2Error(st, "fa2_bwd")
+        raise Fa2Error(st, "fa2_bwd_masked" if masked else "fa2_bwd")
     return dq, dk, dv

@@ -179,6 +179,25 @@ fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O,
                      int dtype, void* stream);
 
 /*
+ * fa2_bwd_masked - fa2_bwd for the attention of fa2_fwd_masked: the same
+ * window and key-length arguments, the same visibility of keys, and O and LSE
+ * from fa2_fwd_masked.  A row with no visible key (LSE = +inf) gets dQ = 0
+ * and adds nothing to dK and dV; keys at or past a sequence's length get
+ * dK = dV = 0 and their K and V rows are never read.  The gradients are
+ * those of the masked definition (the same chain rule with P the softmax
+ * over each row's visible keys; reading of the pages as for
+ * fa2_fwd_masked).  All other arguments, checks, limits and status codes
+ * are those of fa2_bwd (key_lens: as for fa2_fwd_masked, 4-byte aligned,
+ * not overlapping an output).  No window and no key lengths run fa2_bwd's
+ * unmasked kernels, window (<0, 0) without key lengths its causal ones.
+ */
+fa2_status_t fa2_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                            const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
+                            int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                            int64_t window_left, int64_t window_right, const int32_t* key_lens,
+                            int dtype, void* stream);
+
+/*
  * fa2_bwd_noalloc - fa2_bwd without the workspace argument, for callers that
  * cannot allocate device memory (code under HIP graph capture, serving loops,
  * harnesses that forbid hipMalloc).  The workspace is a scratch array inside

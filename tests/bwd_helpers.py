@@ -56,18 +56,39 @@ def make_case(B, H, N, d, dtype, seed, causal=False, scale=None, sigma=(1.0, 1.0
     return w, q, k, v, do
 
 
-def forward_inputs(q64, k64, v64, scale, causal, dtype):
+def forward_inputs(q64, k64, v64, scale, causal, dtype, mask=None):
     """O and LSE for the backward as a caller would pass them, from the oracle:
-    O rounded to the storage dtype, LSE to float32."""
-    from oracle import attention_ref
-    o, lse = attention_ref(q64, k64, v64, scale, causal)
+    O rounded to the storage dtype, LSE to float32.  ``mask`` = (window_left,
+    window_right, key_lens) selects the masked forward."""
+    from oracle import attention_ref, attention_ref_masked
+    if mask is None:
+        o, lse = attention_ref(q64, k64, v64, scale, causal)
+    else:
+        o, lse = attention_ref_masked(q64, k64, v64, scale, *mask)
     return wl.round_to_storage(o, dtype), lse.astype(np.float32)
 
 
-def grad_bounds(q64, k64, v64, do64, o_in64, lse_in64, scale, causal, dtype, heads=None):
+def visibility(n, causal=False, mask=None, b=0):
+    """[N, N] boolean: key j visible to query i (the definitions of the two
+    forward entry points, written out here)."""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    if mask is None:
+        return (j <= i) if causal else np.ones((n, n), dtype=bool)
+    left, right, lens = mask
+    vis = j < (n if lens is None else min(max(int(lens[b]), 0), n))
+    if 0 <= left < n:
+        vis = vis & (j >= i - left)
+    if 0 <= right < n:
+        vis = vis & (j <= i + right)
+    return vis
+
+
+def grad_bounds(q64, k64, v64, do64, o_in64, lse_in64, scale, causal, dtype, heads=None, mask=None):
     """The oracle's gradients and the error bound above, for the (b, h) pairs
-    in ``heads`` (all by default).  Returns dicts name -> [n_pairs, N, d]."""
-    from oracle import attention_bwd_ref, attention_ref
+    in ``heads`` (all by default); ``mask`` as for forward_inputs.  Returns
+    dicts name -> [n_pairs, N, d]."""
+    from oracle import attention_bwd_ref, attention_bwd_ref_masked, attention_ref, attention_ref_masked
     B, H, N, d = q64.shape
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     c = float(np.float32(scale))
@@ -78,11 +99,21 @@ def grad_bounds(q64, k64, v64, do64, o_in64, lse_in64, scale, causal, dtype, hea
     for b, h in pairs:
         sl = (slice(b, b + 1), slice(h, h + 1))
         q, k, v, do = (x[sl] for x in (q64, k64, v64, do64))
-        dq_r, dk_r, dv_r = attention_bwd_ref(q, k, v, do, scale, causal)
-        o_r, lse_r = attention_ref(q, k, v, scale, causal)
+        if mask is None:
+            dq_r, dk_r, dv_r = attention_bwd_ref(q, k, v, do, scale, causal)
+            o_r, lse_r = attention_ref(q, k, v, scale, causal)
+        else:
+            m = (mask[0], mask[1], None if mask[2] is None else [mask[2][b]])
+            dq_r, dk_r, dv_r = attention_bwd_ref_masked(q, k, v, do, scale, *m)
+            o_r, lse_r = attention_ref_masked(q, k, v, scale, *m)
         q, k, v, do, o_r, lse_r = q[0, 0], k[0, 0], v[0, 0], do[0, 0], o_r[0, 0], lse_r[0, 0]
         o_in, lse_in = o_in64[b, h], lse_in64[b, h]
-        vis = np.tril(np.ones((N, N))) if causal else np.ones((N, N))
+        vis = visibility(N, causal, mask, b).astype(np.float64)
+        seen = np.isfinite(lse_r)
+        # Rows that see no key have P = 0 (their LSE is +inf on both sides).
+        lse_r = np.where(seen, lse_r, 0.0)
+        lse_in = np.where(seen, lse_in, 0.0)
+        vis = vis * seen[:, None]
         p = np.exp(np.where(vis > 0, c * (q @ k.T) - lse_r[:, None], -np.inf))
         dp = do @ v.T
         delta = np.sum(do * o_r, axis=1)
@@ -120,7 +151,7 @@ def assert_grads_within(got, refs, bounds, label=""):
                               f"{float(bd[worst]):.3e} at {worst}")
 
 
-def simulate_kernel_rounding(q64, k64, v64, do64, o_in64, lse_in64, scale, causal, dtype):
+def simulate_kernel_rounding(q64, k64, v64, do64, o_in64, lse_in64, scale, causal, dtype, mask=None):
     """The kernels' rounding steps replayed in fp64 on the CPU (P and dS
     rounded to the storage dtype, Delta from the O given, outputs rounded):
     a check that the bound above covers what it claims to (it is not the
@@ -132,8 +163,9 @@ def simulate_kernel_rounding(q64, k64, v64, do64, o_in64, lse_in64, scale, causa
     for b in range(B):
         for h in range(H):
             q, k, v, do = q64[b, h], k64[b, h], v64[b, h], do64[b, h]
-            vis = np.tril(np.ones((N, N))) if causal else np.ones((N, N))
-            p = np.exp(np.where(vis > 0, c * (q @ k.T) - lse_in64[b, h][:, None], -np.inf))
+            vis = visibility(N, causal, mask, b) & np.isfinite(lse_in64[b, h])[:, None]
+            lse = np.where(np.isfinite(lse_in64[b, h]), lse_in64[b, h], 0.0)
+            p = np.exp(np.where(vis, c * (q @ k.T) - lse[:, None], -np.inf))
             delta = np.sum(do * o_in64[b, h], axis=1)
             ds = p * (do @ v.T - delta[:, None])
             out["dv"][b, h] = rnd(rnd(p).T @ do)

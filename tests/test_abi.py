@@ -255,3 +255,14 @@ def test_bwd_noalloc_checks_and_scratch_limit():
     assert fa.fa2_bwd_noalloc(**{**base, "dQ": 0}) == bd.FA2_ERR_NULL_POINTER
     assert fa.fa2_bwd_noalloc(**{**base, "d": 96}) == bd.FA2_ERR_UNSUPPORTED_HEAD_DIM
     assert fa.fa2_bwd_noalloc(**{**base, "dK": p[0]}) == bd.FA2_ERR_OVERLAP
+
+
+def test_bwd_masked_checks():
+    base = dict(Q=BQ_, K=BK_, V=BV_, O=BO_, dO=BDO_, LSE=BL_, dQ=BDQ_, dK=BDK_, dV=BDV_, workspace=BW_,
+                B=2, H=2, N=100, d=64, scale=0.125, window_left=16, window_right=0, key_lens=LENS,
+                dtype=0, stream=0)
+    assert fa.fa2_bwd_masked(**{**base, "workspace": 0}) == bd.FA2_ERR_NULL_POINTER
+    assert fa.fa2_bwd_masked(**{**base, "d": 96}) == bd.FA2_ERR_UNSUPPORTED_HEAD_DIM
+    assert fa.fa2_bwd_masked(**{**base, "key_lens": LENS + 2}) == bd.FA2_ERR_MISALIGNED
+    assert fa.fa2_bwd_masked(**{**base, "dQ": LENS}) == bd.FA2_ERR_OVERLAP
+    assert fa.fa2_bwd_masked(**{**base, "N": 0}) == bd.FA2_ERR_BAD_SHAPE

@@ -19,10 +19,10 @@ CASES = [
 ]
 
 
-def _case(B, H, N, d, dtype, causal, scale, sigma, seed=5):
+def _case(B, H, N, d, dtype, causal, scale, sigma, seed=5, mask=None):
     w, q, k, v, do = bh.make_case(B, H, N, d, dtype, seed, causal=causal, scale=scale, sigma=sigma)
     q64, k64, v64, do64 = (wl.to_float64(x, dtype) for x in (q, k, v, do))
-    o_in, lse_in = bh.forward_inputs(q64, k64, v64, w.softmax_scale(), causal, dtype)
+    o_in, lse_in = bh.forward_inputs(q64, k64, v64, w.softmax_scale(), causal, dtype, mask=mask)
     return w, q64, k64, v64, do64, wl.to_float64(o_in, dtype), lse_in.astype(np.float64)
 
 
@@ -55,3 +55,16 @@ def test_bound_rejects_wrong_gradients():
             got[name] = bad
         with pytest.raises(AssertionError):
             bh.assert_grads_within(got, refs, bounds, f"wrong {name}")
+
+
+MASKS = [(8, 0, None), (-1, -1, [40, 0]), (5, 3, [70, 33]), (-1, 0, [50, 17]), (0, 0, None)]
+
+
+@pytest.mark.parametrize("mask", MASKS, ids=str)
+def test_replayed_rounding_within_bound_masked(mask):
+    w, q64, k64, v64, do64, o_in, lse_in = _case(2, 1, 75, 64, wl.FP16, False, None, (1, 1, 1, 1), mask=mask)
+    refs, bounds = bh.grad_bounds(q64, k64, v64, do64, o_in, lse_in, w.softmax_scale(), False, w.dtype, mask=mask)
+    sim = bh.simulate_kernel_rounding(q64, k64, v64, do64, o_in, lse_in, w.softmax_scale(), False, w.dtype,
+                                      mask=mask)
+    got = {n: sim[n].reshape(refs[n].shape) for n in sim}
+    bh.assert_grads_within(got, refs, bounds, f"replayed rounding {mask}")

@@ -18,28 +18,41 @@ from tests.gpu_helpers import to_device
 pytestmark = pytest.mark.gpu
 
 
-def _run(case_args, device, heads=None, seed=3, chained=False, stream=None):
+def _run(case_args, device, heads=None, seed=3, chained=False, stream=None, mask=None):
+    """One backward case; ``mask`` = (window_left, window_right, key_lens)
+    runs fa2_bwd_masked (the forward inputs from the masked oracle), with the
+    GPU's K and V rows at or past each key length set to NaN (the kernels
+    must never read them)."""
     B, H, N, d, dtype, causal, scale, sigma = case_args
     w, q, k, v, do = bh.make_case(B, H, N, d, dtype, seed, causal=causal, scale=scale, sigma=sigma)
     sc = w.softmax_scale()
-    print(f"case {w.name} causal={causal} scale={sc} sigma={sigma} chained={chained}", flush=True)
+    print(f"case {w.name} causal={causal} scale={sc} sigma={sigma} chained={chained} mask={mask}", flush=True)
     q64, k64, v64, do64 = (wl.to_float64(x, dtype) for x in (q, k, v, do))
     tq, tk, tv, tdo = (to_device(x, dtype, device) for x in (q, k, v, do))
+    kw = {}
+    if mask is not None:
+        kw["window"] = (mask[0], mask[1])
+        if mask[2] is not None:
+            kw["key_lens"] = torch.tensor(mask[2], dtype=torch.int32, device=device)
+            if not chained:
+                for b, n_b in enumerate(mask[2]):
+                    tk[b, :, max(n_b, 0):] = float("nan")
+                    tv[b, :, max(n_b, 0):] = float("nan")
     if chained:
-        o_t, lse_t = forward(tq, tk, tv, scale=sc, causal=causal)
+        o_t, lse_t = forward(tq, tk, tv, scale=sc, causal=causal, **kw)
     else:
-        o_in, lse_in = bh.forward_inputs(q64, k64, v64, sc, causal, dtype)
+        o_in, lse_in = bh.forward_inputs(q64, k64, v64, sc, causal, dtype, mask=mask)
         o_t = to_device(o_in, dtype, device)
         lse_t = torch.from_numpy(lse_in).to(device)
     if stream is None:
-        dq, dk, dv = backward(tq, tk, tv, o_t, lse_t, tdo, scale=sc, causal=causal)
+        dq, dk, dv = backward(tq, tk, tv, o_t, lse_t, tdo, scale=sc, causal=causal, **kw)
     else:
         with torch.cuda.stream(stream):
-            dq, dk, dv = backward(tq, tk, tv, o_t, lse_t, tdo, scale=sc, causal=causal)
+            dq, dk, dv = backward(tq, tk, tv, o_t, lse_t, tdo, scale=sc, causal=causal, **kw)
     torch.cuda.synchronize(device)
     o_in64 = bh.to_np(o_t)
     lse_in64 = lse_t.cpu().numpy().astype(np.float64)
-    refs, bounds = bh.grad_bounds(q64, k64, v64, do64, o_in64, lse_in64, sc, causal, dtype, heads=heads)
+    refs, bounds = bh.grad_bounds(q64, k64, v64, do64, o_in64, lse_in64, sc, causal, dtype, heads=heads, mask=mask)
     got = {}
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         g = bh.to_np(t)
@@ -150,3 +163,42 @@ def test_bwd_random_shapes(gpu_device, case):
     dim, dtype, scale of either sign and mask: every element of dQ, dK, dV
     within the rounding bound."""
     _run(case, gpu_device, seed=case[2] + case[3])
+
+
+
+# (B, H, N, d, dtype) with (window_left, window_right, key_lens): two-sided,
+# left-only and right-only windows, key lengths with a fully padded sequence
+# (and rows that see no key), the causal window with lengths, a window wider
+# than N.
+MASKED = [
+    ((1, 2, 300, 64, wl.FP16), (40, 7, None)),
+    ((2, 1, 257, 128, wl.BF16), (-1, -1, [200, 0])),
+    ((2, 2, 333, 64, wl.BF16), (64, 0, [333, 90])),
+    ((1, 1, 500, 128, wl.FP16), (-1, 0, [311])),
+    ((2, 1, 190, 128, wl.FP16), (5, 3, [100, 40])),
+    ((1, 2, 700, 64, wl.FP16), (129, -1, None)),
+    ((1, 1, 260, 64, wl.BF16), (1000, 1000, None)),
+    ((3, 1, 150, 64, wl.FP16), (0, 0, [150, 1, 77])),
+]
+
+
+@pytest.mark.parametrize("shape,mask", MASKED, ids=[f"{s[2]}d{s[3]}{s[4]}-{m}" for s, m in MASKED])
+def test_bwd_masked(gpu_device, shape, mask):
+    """fa2_bwd_masked against the masked oracle's gradients, every element;
+    keys past a length get dK = dV = 0 and rows that see no key dQ = 0,
+    exactly."""
+    B, H, N, d, dtype = shape
+    tq, tk, tv, o_t, lse_t, tdo, dq, dk, dv = _run((B, H, N, d, dtype, False, None, ONE), gpu_device, mask=mask)
+    lens = mask[2]
+    if lens is not None:
+        for b, n_b in enumerate(lens):
+            assert torch.count_nonzero(dk[b, :, n_b:]).item() == 0 and torch.count_nonzero(dv[b, :, n_b:]).item() == 0
+    hidden = torch.isinf(lse_t)
+    assert torch.count_nonzero(dq[hidden]).item() == 0
+
+
+@pytest.mark.parametrize("case", [(2, 2, 400, 64, wl.FP16, False, None, ONE),
+                                  (1, 2, 300, 128, wl.BF16, False, None, ONE)],
+                         ids=["d64_fp16", "d128_bf16"])
+def test_bwd_masked_chained_after_gpu_forward(gpu_device, case):
+    _run(case, gpu_device, chained=True, mask=(100, 0, [400, 250][:case[0]]))
