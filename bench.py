@@ -9,8 +9,9 @@ average kernel time used for the roofline figure.
 
 Prints one JSON line.  ``--workload NAME`` times one of the other seeded
 workloads instead (for the design notes; the default line is the headline one).
-``--pass bwd`` times the backward pass (fa2_bwd: dQ, dK, dV from the
-forward's O and LSE and a seeded N(0,1) dO) on d = 64 or 128 workloads.
+``--pass bwd`` times the backward pass (fa2_bwd or fa2_bwd_masked: dQ, dK,
+dV from the forward's O and LSE and a seeded N(0,1) dO) on d = 64 or 128
+workloads.
 """
 from __future__ import annotations
 
@@ -210,17 +211,17 @@ def main() -> int:
 
     bwd = args.pass_ == "bwd"
     if bwd:
-        if w.masked or w.d not in (64, 128):
-            print(f"--pass bwd supports unmasked d = 64 and 128 workloads, not {w.name}", file=sys.stderr)
+        if w.d not in (64, 128):
+            print(f"--pass bwd supports d = 64 and 128 workloads, not {w.name}", file=sys.stderr)
             return 2
         do = wl.make_grad_output(w, seed=0)
         tdo = to_dev(do)
-        forward(tq, tk, tv, scale=scale, causal=w.causal, out=out, lse=lse)
+        forward(tq, tk, tv, scale=scale, causal=w.causal, out=out, lse=lse, **mask_kw)
         grads = (torch.empty_like(tq), torch.empty_like(tq), torch.empty_like(tq))
         ws = torch.empty((2, w.B, w.H, w.N), dtype=torch.float32, device=dev)
 
         def step():
-            backward(tq, tk, tv, out, lse, tdo, scale=scale, causal=w.causal, workspace=ws, out=grads)
+            backward(tq, tk, tv, out, lse, tdo, scale=scale, causal=w.causal, workspace=ws, out=grads, **mask_kw)
     else:
         def step():
             forward(tq, tk, tv, scale=scale, causal=w.causal, out=out, lse=lse, **mask_kw)

@@ -49,12 +49,13 @@ def main() -> int:
     if w.key_lens is not None:
         mask_kw["key_lens"] = torch.tensor(w.key_lens, dtype=torch.int32, device=dev)
     if args.pass_ == "bwd":
-        forward(tq, tk, tv, scale=w.softmax_scale(), causal=w.causal, out=out, lse=lse)
+        forward(tq, tk, tv, scale=w.softmax_scale(), causal=w.causal, out=out, lse=lse, **mask_kw)
         tdo = to_dev(wl.make_grad_output(w, seed=0))
         grads = (torch.empty_like(tq), torch.empty_like(tq), torch.empty_like(tq))
         ws = torch.empty((2, w.B, w.H, w.N), dtype=torch.float32, device=dev)
         for _ in range(args.launches):
-            backward(tq, tk, tv, out, lse, tdo, scale=w.softmax_scale(), causal=w.causal, workspace=ws, out=grads)
+            backward(tq, tk, tv, out, lse, tdo, scale=w.softmax_scale(), causal=w.causal, workspace=ws, out=grads,
+                     **mask_kw)
     else:
         for _ in range(args.launches):
             forward(tq, tk, tv, scale=w.softmax_scale(), causal=w.causal, out=out, lse=lse, **mask_kw)
