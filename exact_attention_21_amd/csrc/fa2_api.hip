@@ -352,6 +352,26 @@ fa2_status_t checked_launch(const void* Q, const void* K, const void* V, void* O
 }
 
 // ---- backward ----------------------------------------------------------
+// Slices per group of the backward work order (fa2::bwd_work_item): 8 (one
+// per XCD) times the number of a slice's tiles that fill one round of an
+// XCD's resident workgroups, at least 8; all slices when that is no fewer.
+// Groups are taken under a mask with 128 slices or more (16 per XCD); the
+// plain order (heads fastest over all slices, the longest tiles of every
+// slice first) otherwise.  Measured, same-process A/B against the plain
+// order: masked with 128 to 256 slices +1% to +6% (padded causal d = 128
+// +5.7%, causal B8 H16 N4096 d = 128 +5.5%); causal with 32 slices -2% to
+// -3%; no mask with 128 slices -2% (d = 128) to +2% (d = 64); 4 or 8
+// slices unchanged.
+#ifndef FA2_BWD_GROUPS
+#define FA2_BWD_GROUPS 1
+#endif
+int bwd_slice_group(int bh, int n_tiles, int wgs_per_cu, int mask) {
+  if (!FA2_BWD_GROUPS || mask == fa2::kMaskNone || bh < 16 * kXcds) return bh;
+  const int64_t resident = (int64_t)std::max(1, device_cus() / kXcds) * std::max(1, wgs_per_cu);
+  const int64_t group = kXcds * std::max<int64_t>(1, resident / std::max(1, n_tiles));
+  return group >= bh ? bh : (int)group;
+}
+
 // Waves per workgroup of the two backward kernels (32 rows each).
 constexpr int kBwdWaves = 4;
 
@@ -368,10 +388,12 @@ hipError_t launch_bwd(const fa2::BwdParams& base, hipStream_t stream) {
   // dQ and Delta first: the dK/dV kernel reads Delta.
   fa2::BwdParams p = base;
   p.n_tiles = (p.n + KQ::BQ - 1) / KQ::BQ;
+  p.group = bwd_slice_group(p.bh, p.n_tiles, sq.per_cu, MASK);
   hipLaunchKernelGGL(kq, dim3((unsigned)((int64_t)p.n_tiles * p.bh)), dim3(KQ::THREADS), KQ::LDS_BYTES, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   p.n_tiles = (p.n + KKV::BK - 1) / KKV::BK;
+  p.group = bwd_slice_group(p.bh, p.n_tiles, skv.per_cu, MASK);
   hipLaunchKernelGGL(kkv, dim3((unsigned)((int64_t)p.n_tiles * p.bh)), dim3(KKV::THREADS), KKV::LDS_BYTES, stream,
                      p);
   return hipGetLastError();

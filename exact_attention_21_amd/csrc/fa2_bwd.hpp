@@ -69,6 +69,7 @@ struct BwdParams {
   int n;        // sequence length N
   int bh;       // B * H
   int n_tiles;  // stationary tiles per (batch*head) slice of the kernel launched
+  int group;    // slices per group of the work order (bwd_work_item)
   float scale;  // softmax scale (any finite value)
   float c2;     // scale * log2(e): scores to the base-2 exponent domain
   // General mask (the forward's): key j is visible to query i iff
@@ -80,6 +81,26 @@ struct BwdParams {
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Work item of workgroup wg: its (batch*head) slice and its step (tile
+// index, counted from the longest tile under a mask).  The slices are taken
+// in groups of p.group, every tile of a group before the next group, the step
+// varying slowest inside a group: with a group of (a multiple of) 8 slices
+// each XCD (workgroups are dealt to the 8 XCDs round robin) runs the tiles of
+// the same few slices together, so the tiles they stream (K and V, or Q and
+// dO) are read from its L2 instead of HBM (the forward's order, work_item).
+struct BwdItem {
+  int bh;
+  int step;
+};
+__device__ __forceinline__ BwdItem bwd_work_item(const BwdParams& p, int wg) {
+  const int span = p.group * p.n_tiles;
+  const int g = wg / span;
+  const int r = wg - g * span;
+  const int size = min(p.group, p.bh - g * p.group);
+  const int step = r / size;
+  return {g * p.group + (r - step * size), step};
+}
 
 // Calls f(std::integral_constant<int, I>{}) for I = B .. E-1 in order: the
 // pipelines below index their register arrays with these compile-time
@@ -268,8 +289,9 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int h = lane >> 5;
-    const int step = blockIdx.x / p.bh;
-    const int bh = blockIdx.x - step * p.bh;
+    const BwdItem item = bwd_work_item(p, blockIdx.x);
+    const int step = item.step;
+    const int bh = item.bh;
     // Under a mask the last query tiles (causal: the most keys) first.
     const int qtile = MASK != kMaskNone ? p.n_tiles - 1 - step : step;
     const int n = p.n;
@@ -532,8 +554,9 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
     const int wave = tid >> 6;
     const int h = lane >> 5;
     // Causal: the first key tiles (the most queries) first.
-    const int ktile = blockIdx.x / p.bh;
-    const int bh = blockIdx.x - ktile * p.bh;
+    const BwdItem item = bwd_work_item(p, blockIdx.x);
+    const int ktile = item.step;
+    const int bh = item.bh;
     const int n = p.n;
     const int k0 = ktile * BK;
     const int kw0 = k0 + 32 * wave;

@@ -202,3 +202,25 @@ def test_bwd_masked(gpu_device, shape, mask):
                          ids=["d64_fp16", "d128_bf16"])
 def test_bwd_masked_chained_after_gpu_forward(gpu_device, case):
     _run(case, gpu_device, chained=True, mask=(100, 0, [400, 250][:case[0]]))
+
+
+def test_bwd_grouped_work_order(gpu_device):
+    """Masked grids of 128 slices or more take the work in XCD-sized slice
+    groups: every element of dQ, dK, dV is written (the outputs start as
+    NaN) and sampled heads from several groups match the oracle."""
+    B, H, N, d, dtype = 8, 16, 1100, 64, wl.FP16
+    w, q, k, v, do = bh.make_case(B, H, N, d, dtype, 9, causal=True)
+    sc = w.softmax_scale()
+    q64, k64, v64, do64 = (wl.to_float64(x, dtype) for x in (q, k, v, do))
+    tq, tk, tv, tdo = (to_device(x, dtype, gpu_device) for x in (q, k, v, do))
+    o_t, lse_t = forward(tq, tk, tv, scale=sc, causal=True)
+    out = tuple(torch.full_like(tq, float("nan")) for _ in range(3))
+    dq, dk, dv = backward(tq, tk, tv, o_t, lse_t, tdo, scale=sc, causal=True, out=out)
+    torch.cuda.synchronize(gpu_device)
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all().item()), "an output tile was not written"
+    heads = [(0, 0), (2, 9), (5, 3), (7, 15)]
+    refs, bounds = bh.grad_bounds(q64, k64, v64, do64, bh.to_np(o_t), lse_t.cpu().numpy().astype(np.float64), sc,
+                                  True, dtype, heads=heads)
+    got = {name: np.stack([bh.to_np(t)[b, h] for b, h in heads]) for name, t in (("dq", dq), ("dk", dk), ("dv", dv))}
+    bh.assert_grads_within(got, refs, bounds, "grouped work order")
