@@ -1,9 +1,10 @@
 // FlashAttention-2 backward kernels for gfx950 (CDNA4), wave64 MFMA.
 //
 // What they compute (per batch b, head h), given the forward's O and LSE and
-// the output gradient dO, with S = scale * Q K^T (causal: key j hidden from
-// query i when j > i) and P = exp(S - LSE) (the forward's probabilities,
-// recomputed):
+// the output gradient dO, with S = scale * Q K^T over the keys each query
+// sees (all, j <= i under the causal mask, or the forward's general mask: a
+// sliding window below a per-sequence key length) and P = exp(S - LSE) (the
+// forward's probabilities, recomputed; 0 for hidden keys):
 //   dV = P^T dO
 //   dP = dO V^T,   Delta_i = sum_d dO[i,d] O[i,d],   dS = P * (dP - Delta)
 //   dQ = scale * dS K,   dK = scale * dS^T Q
@@ -39,6 +40,14 @@
 //     per row (bwd_swz) so that both reads are free of LDS bank conflicts.
 //   * The dP accumulators start at -Delta instead of 0, so the product gives
 //     dP - Delta and dS = P (dP - Delta) is one multiply per element.
+//   * Tiles that hold a hidden (row, key) pair run their own instantiation
+//     of the tile body, with the per-element mask; they are a prefix and a
+//     suffix of each workgroup's tile range (window edges, causal diagonal,
+//     key length, ragged N), the tiles between carry no mask arithmetic.
+//   * Each wave runs a software pipeline: step j issues the MFMAs of the next
+//     block's score products and of the previous block's gradient products
+//     one at a time, each followed by a share of block j's exponentials, dS
+//     and packing.
 //   * Rows past N load as zeros from range-checked buffer resources and
 //     contribute exactly zero; out-of-range stores are dropped by the same
 //     check.
