@@ -129,7 +129,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 //    must fall in distinct 16-byte bank groups of the 256-byte LDS line;
 //  * transposed (ds_read_b64_tr_b16): 32 lanes read 4 consecutive rows 4a+e
 //    (e = 0..3) at one aligned group of 4 chunks, so those 16 chunks must too.
-// d = 64 (8 chunks, two rows per line, the line half given by r%2): bits 0-1
+// d = 32 (4 chunks, four rows per line, the line quarter given by r%4): the
+// XOR follows r/4 % 4, so the four rows of 16 that share a line quarter take
+// four different chunk positions; a transposed read covers whole rows, one
+// per line quarter.  d = 64 (8 chunks, two rows per line, the line half given by r%2): bits 0-1
 // of the XOR walk the four aligned 4-row groups of 16 rows and bit 2 follows
 // r/2 % 2, which puts rows 4a and 4a+2 (same line half) in different 4-chunk
 // halves.  d = 128 (16 chunks, one row per line): bits 2-3 follow r%4 (the
@@ -138,7 +141,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 // depend on r only through r%16.
 template <int D>
 __device__ __forceinline__ int bwd_swz(int row) {
-  static_assert(D == 64 || D == 128, "backward head dims");
+  static_assert(D == 32 || D == 64 || D == 128, "backward head dims");
+  if constexpr (D == 32) return (row >> 2) & 3;
   if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
   return ((row & 3) << 2) | ((row >> 2) & 3);
 }
@@ -276,9 +280,9 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
   using typename Base::lds_char;
   static constexpr int THREADS = NW * 64;
   static constexpr int BQ = NW * 32;  // query rows per workgroup (32 per wave)
-  // Keys per streamed tile: 128 at d = 64, 64 at d = 128 (two tiles in LDS,
-  // 64 KiB, so that two workgroups share a CU).
-  static constexpr int BC = D == 64 ? 128 : 64;
+  // Keys per streamed tile: 128 at d = 32 and 64, 64 at d = 128 (two tiles in
+  // LDS, 64 KiB, so that two workgroups share a CU).
+  static constexpr int BC = D <= 64 ? 128 : 64;
   static constexpr int KB = BC / 32;
   static constexpr int TILEB = BC * ROWB;
   static constexpr int SLOTB = 2 * TILEB;  // one K tile and one V tile

@@ -82,8 +82,10 @@ typedef enum {
  *   LSE       device pointer to a [B, H, N] float32 tensor (written).
  *   B, H, N   batch, heads, sequence length; each >= 1.  Limits, with R the
  *             query rows per workgroup (256 for d = 64 and 128, 128 for
- *             d = 32, 96, 256 and 512, 64 for d = 1024; fa2_launch_info
- *             reports it):
+ *             d = 32, 96, 256 and 512, 64 for d = 1024; d = 128 takes a
+ *             128-row form on grids of at most one 256-row workgroup per
+ *             compute unit, which fa2_launch_info reports, and the limit
+ *             below uses 256):
  *             (N + 256) * d * 2 < 2^31 (one head's slice, with the rows past
  *             N that the last query tile and the last key tiles touch, is
  *             addressed with signed 32-bit byte offsets) and
@@ -159,8 +161,8 @@ fa2_status_t fa2_fwd_masked(const void* Q, const void* K, const void* V, void* O
  *             owned by the caller; its contents on entry do not matter.  When
  *             the call's work has run it holds -Delta of every row ([B, H, N])
  *             followed by -LSE * log2(e) of every row ([B, H, N]).
- *   B, H, N, scale, is_causal, dtype, stream: as for fa2_fwd, with d = 64
- *             or 128 only, and ceil(N / 128) * H * B < 2^31.
+ *   B, H, N, scale, is_causal, dtype, stream: as for fa2_fwd, with d = 32,
+ *             64 or 128 only, and ceil(N / 128) * H * B < 2^31.
  *
  * Numerics: S, dP, Delta and the accumulators are fp32; P and dS are rounded
  * to `dtype` (to nearest even) before the products that take them, and the
@@ -171,7 +173,7 @@ fa2_status_t fa2_fwd_masked(const void* Q, const void* K, const void* V, void* O
  * (first dQ and the row statistics, then dK and dV), allocates nothing and does not
  * synchronise.  Errors: as for fa2_fwd; FA2_ERR_OVERLAP when dQ, dK, dV or
  * the workspace overlaps an input or one another; FA2_ERR_UNSUPPORTED_HEAD_DIM
- * for d other than 64 and 128.
+ * for d other than 32, 64 and 128.
  */
 fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                      const float* LSE, void* dQ, void* dK, void* dV, float* workspace,
