@@ -141,7 +141,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // depend on r only through r%16.
 template <int D>
 __device__ __forceinline__ int bwd_swz(int row) {
-  static_assert(D == 32 || D == 64 || D == 128, "backward head dims");
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "backward head dims");
   if constexpr (D == 32) return (row >> 2) & 3;
   if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
   return ((row & 3) << 2) | ((row >> 2) & 3);
@@ -238,6 +238,39 @@ struct BwdBase {
     }
   };
 
+  // Gradient accumulators in AGPRs (AGPR = true: wide head dims, one wave per
+  // SIMD, the arch VGPRs hold the rest) go through the forward's inline-asm
+  // MFMA, under its rules: A and B are never written by VALU just before it
+  // (the B operands are packed a step earlier), the two MFMAs of one
+  // accumulator in a step are other MFMAs apart, and compiler-issued reads
+  // of the accumulators come only after settle().
+  template <bool AGPR>
+  static __device__ __forceinline__ void acc_zero(f32x16 (&x)[DB]) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      x[db] = f32x16{};
+      if constexpr (AGPR) asm volatile("" : "+a"(x[db]));
+    }
+  }
+  template <bool AGPR>
+  static __device__ __forceinline__ void acc_mfma(f32x16& c, const u32x4& a, const u32x4& b) {
+    if constexpr (AGPR)
+      mfma32_acc_agpr<BF16>(c, a, b);
+    else
+      c = mfma32<BF16>(a, b, c);
+  }
+  // Wait states between the last inline-asm MFMA of an accumulator and a
+  // compiler-issued read of it (a 32x32 MFMA's result is readable 18 passes
+  // after issue); the pins keep the reads behind the wait.
+  template <bool AGPR>
+  static __device__ __forceinline__ void settle(f32x16 (&x)[DB]) {
+    if constexpr (AGPR) {
+      asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
+#pragma unroll
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(x[db]));
+    }
+  }
+
   // Registers 8u..8u+7 of a score accumulator, rounded and packed: the B
   // operand of a gradient product for k-step u.
   static __device__ __forceinline__ void pack_operand(const float (&x)[16], u32x4 (&b)[2]) {
@@ -281,8 +314,10 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
   static constexpr int THREADS = NW * 64;
   static constexpr int BQ = NW * 32;  // query rows per workgroup (32 per wave)
   // Keys per streamed tile: 128 at d = 32 and 64, 64 at d = 128 (two tiles in
-  // LDS, 64 KiB, so that two workgroups share a CU).
+  // LDS, 64 KiB, so that two workgroups share a CU) and 256 (128 KiB).
   static constexpr int BC = D <= 64 ? 128 : 64;
+  // dQ accumulators in AGPRs at d = 256 (one wave per SIMD).
+  static constexpr bool ACC_AGPR = D >= 256;
   static constexpr int KB = BC / 32;
   static constexpr int TILEB = BC * ROWB;
   static constexpr int SLOTB = 2 * TILEB;  // one K tile and one V tile
@@ -378,8 +413,7 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
     const u32x4 wv = rsrc_words(p.v, slice * 2, (uint32_t)klen * D * 2);
 
     f32x16 dq[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+    Base::template acc_zero<ACC_AGPR>(dq);
 
     // Key tiles that some row of the workgroup sees: [tfirst, tend).  A tile
     // takes the per-element mask when it holds a key past N (or the key
@@ -436,7 +470,7 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
             dp[kb % 2] = mfma32<BF16>(a, df[ks], ks == 0 ? dp0 : dp[kb % 2]);
         } else {
           const int kb = j - 1, u = (pos - NSD) / DB, db = (pos - NSD) % DB;
-          dq[db] = mfma32<BF16>(a, b[kb % 2][u], dq[db]);
+          Base::template acc_mfma<ACC_AGPR>(dq[db], a, b[kb % 2][u]);
         }
       };
       // VALU work of pair c of block j: registers 2c, 2c+1 (keys
@@ -498,6 +532,7 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
     }
     for (; t < m2; ++t) tile(t, std::false_type{});
     for (; t < tend; ++t) tile(t, std::true_type{});
+    Base::template settle<ACC_AGPR>(dq);
     Base::store_grad(rdq, dq, myq, lane, p.scale);
   }
 };
@@ -515,21 +550,17 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
   using typename Base::lds_char;
   static constexpr int THREADS = NW * 64;
   static constexpr int BK = NW * 32;  // key rows per workgroup (32 per wave)
-  static constexpr int BQ = 128;      // query rows per streamed tile
+  static constexpr int BQ = D >= 256 ? 64 : 128;  // query rows per streamed tile (LDS: two slots)
   static constexpr int QBLK = BQ / 32;
   static constexpr int TILEB = BQ * ROWB;
   // Slot: Q tile, dO tile, then -LSE * log2(e) and -Delta of its rows (BQ
   // floats each).
   static constexpr int SLOTB = 2 * TILEB + 2 * BQ * 4;
   static constexpr int LDS_BYTES = 2 * SLOTB;
-  static_assert(BQ == 128 && NW >= 2, "the row statistics of a tile are two 64-lane dword copies each");
+  static_assert(BQ % 64 == 0 && NW >= 2, "the row statistics of a tile are 64-lane dword copies");
   using St = typename Base::template Stager<BQ, THREADS>;
-  // dV and dK accumulators in AGPRs at d = 128 (one wave per SIMD: the arch
-  // VGPRs hold the rest), through the inline-asm MFMA of the forward's output
-  // product and under the same rules: its A and B operands are never written
-  // by VALU just before it (the B operands are packed a step earlier), the
-  // two MFMAs of one accumulator in a step are 2 DB - 1 MFMAs apart, and the
-  // epilogue reads the accumulators only after settle_acc.
+  // dV and dK accumulators in AGPRs from d = 128 (one wave per SIMD: the
+  // arch VGPRs hold the rest; see BwdBase::acc_mfma).
   static constexpr bool ACC_AGPR = D >= 128;
   // Software pipeline over the QBLK 32-row blocks of a tile: step j issues
   // the MFMAs of dV(j-1) and dK(j-1) (NG, u = 0 first), then of S(j+1) and
@@ -539,27 +570,7 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
   static constexpr int NG = 4 * DB;
   static constexpr int NSD = 2 * DK;
   static constexpr int NPOS = NG + NSD;
-  static constexpr int PF = 3;  // positions between a fragment's LDS read and its MFMA
-
-  static __device__ __forceinline__ void acc_mfma(f32x16& c, const u32x4& a, const u32x4& b) {
-    if constexpr (ACC_AGPR)
-      mfma32_acc_agpr<BF16>(c, a, b);
-    else
-      c = mfma32<BF16>(a, b, c);
-  }
-  // Wait states between the last inline-asm MFMA of an accumulator and a
-  // compiler-issued read of it (a 32x32 MFMA's result is readable 18 passes
-  // after issue); the pins keep the reads behind the wait.
-  static __device__ __forceinline__ void settle_acc(f32x16 (&x)[DB], f32x16 (&y)[DB]) {
-    if constexpr (ACC_AGPR) {
-      asm volatile("s_nop 7\n s_nop 7\n s_nop 3");
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        asm volatile("" : "+a"(x[db]));
-        asm volatile("" : "+a"(y[db]));
-      }
-    }
-  }
+  static constexpr int PF = D >= 256 ? 2 : 3;  // positions between a fragment's LDS read and its MFMA
 
   static __device__ __forceinline__ void run(const BwdParams& p, lds_char* lds) {
     const int tid = threadIdx.x;
@@ -616,15 +627,8 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
     const u32x4 wl2 = rsrc_words(p.delta, ((size_t)p.bh + bh) * n * 4, (uint32_t)n * 4);
 
     f32x16 dv[DB], dk[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      dv[db] = f32x16{};
-      dk[db] = f32x16{};
-      if constexpr (ACC_AGPR) {
-        asm volatile("" : "+a"(dv[db]));
-        asm volatile("" : "+a"(dk[db]));
-      }
-    }
+    Base::template acc_zero<ACC_AGPR>(dv);
+    Base::template acc_zero<ACC_AGPR>(dk);
 
     // Query tiles with a row that sees some key of the workgroup: [tfirst,
     // tend).  A tile takes the per-element mask when some (row, key) pair of
@@ -656,7 +660,7 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
       st.stage(wdo, dst + TILEB, t * BQ);
       // Wave 0: -LSE * log2(e) of the tile's rows; wave 1: -Delta.
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      for (int half = 0; half < BQ / 64; ++half) {
         if (wave == 0) Base::dma4(wl2, dst + 2 * TILEB + half * 256, (t * BQ + 64 * half + lane) * 4);
         if (wave == 1) Base::dma4(wd, dst + 2 * TILEB + BQ * 4 + half * 256, (t * BQ + 64 * half + lane) * 4);
       }
@@ -701,9 +705,9 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
         if (pos < NG) {
           const int qb = j - 1, u = pos / (2 * DB), db = (pos % (2 * DB)) / 2;
           if (pos % 2 == 0)
-            acc_mfma(dv[db], a, pb[qb % 2][u]);
+            Base::template acc_mfma<ACC_AGPR>(dv[db], a, pb[qb % 2][u]);
           else
-            acc_mfma(dk[db], a, sb[qb % 2][u]);
+            Base::template acc_mfma<ACC_AGPR>(dk[db], a, sb[qb % 2][u]);
         } else {
           const int qb = j + 1, ks = (pos - NG) / 2;
           if ((pos - NG) % 2 == 0)
@@ -775,16 +779,17 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
     if constexpr (GENERAL) {
       for (; t < tend; ++t) tile(t, std::true_type{});
     }
-    settle_acc(dv, dk);
+    Base::template settle<ACC_AGPR>(dv);
+    Base::template settle<ACC_AGPR>(dk);
     Base::store_grad(rdv, dv, mykey, lane, 1.0f);
     Base::store_grad(rdk, dk, mykey, lane, p.scale);
   }
 };
 
-// Two waves per SIMD (256 registers each), so that one wave's VALU work
-// issues beside the other's MFMAs.
+// Two waves per SIMD (256 registers each) up to d = 128, so that one wave's
+// VALU work issues beside the other's MFMAs; one at d = 256.
 template <int D, int NW, bool BF16, int MASK>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
     fa2_bwd_q_kernel(const BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) char lds_generic[];
   Fa2BwdQ<D, NW, BF16, MASK>::run(

@@ -82,6 +82,9 @@ SMALL = [
     (2, 2, 333, 32, wl.FP16, False, None, ONE),
     (1, 3, 515, 32, wl.BF16, True, None, ONE),
     (1, 1, 1, 32, wl.BF16, False, None, ONE),
+    (1, 2, 300, 256, wl.BF16, False, None, ONE),
+    (2, 1, 257, 256, wl.FP16, True, None, ONE),
+    (1, 1, 70, 256, wl.BF16, True, 0.2, (3.0, 3.0, 1.0, 1.0)),
 ]
 
 
@@ -146,7 +149,7 @@ def test_bwd_on_a_side_stream(gpu_device):
 
 def _draw_bwd_case(i):
     rng = np.random.default_rng(5000 + i)
-    d = int(rng.choice((32, 64, 128)))
+    d = int(rng.choice((32, 64, 128, 256)))
     B, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
     N = int(rng.integers(1, 700))
     dtype = wl.FP16 if rng.random() < 0.5 else wl.BF16
@@ -183,6 +186,7 @@ MASKED = [
     ((1, 1, 260, 64, wl.BF16), (1000, 1000, None)),
     ((3, 1, 150, 64, wl.FP16), (0, 0, [150, 1, 77])),
     ((2, 2, 280, 32, wl.BF16), (50, 10, [280, 99])),
+    ((2, 1, 300, 256, wl.BF16), (70, 0, [300, 130])),
 ]
 
 
