@@ -403,6 +403,7 @@ template <bool BF16, int MASK>
 hipError_t launch_bwd_d(int64_t d, const fa2::BwdParams& p, hipStream_t stream) {
   return d == 32    ? launch_bwd<32, BF16, MASK>(p, stream)
          : d == 64  ? launch_bwd<64, BF16, MASK>(p, stream)
+         : d == 96  ? launch_bwd<96, BF16, MASK>(p, stream)
          : d == 128 ? launch_bwd<128, BF16, MASK>(p, stream)
                     : launch_bwd<256, BF16, MASK>(p, stream);
 }
@@ -427,7 +428,7 @@ static_assert(kBwdRows <= kPadRows && fa2::Fa2BwdQ<64, kBwdWaves, false, 0>::BC 
 
 fa2_status_t bwd_check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_UNSUPPORTED_DTYPE;
-  if (d != 32 && d != 64 && d != 128 && d != 256) return FA2_ERR_UNSUPPORTED_HEAD_DIM;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA2_ERR_UNSUPPORTED_HEAD_DIM;
   if (B < 1 || H < 1 || N < 1) return FA2_ERR_BAD_SHAPE;
   if ((N + kPadRows) * d * 2 >= (int64_t(1) << 31)) return FA2_ERR_BAD_SHAPE;
   if (B > (int64_t(1) << 31) / H) return FA2_ERR_BAD_SHAPE;

@@ -37,7 +37,7 @@
 //   * Streamed tiles go from global memory straight into a 2-slot LDS ring
 //     (buffer_load ... lds), one barrier per tile.  A streamed tile is read
 //     both as plain rows and transposed; its 16-byte chunks are permuted
-//     per row (bwd_swz) so that both reads are free of LDS bank conflicts.
+//     per row (bwd_pos) so that both reads are free of LDS bank conflicts.
 //   * The dP accumulators start at -Delta instead of 0, so the product gives
 //     dP - Delta and dS = P (dP - Delta) is one multiply per element.
 //   * Tiles that hold a hidden (row, key) pair run their own instantiation
@@ -123,8 +123,8 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Position of 16-byte chunk c of row r of a streamed tile: c ^ bwd_swz(r).
-// A tile is read two ways:
+// Position of 16-byte chunk c of row r of a streamed tile (bwd_pos), and the
+// chunk held at position p (bwd_chunk, its inverse).  A tile is read two ways:
 //  * plain: 16 lanes read 16 consecutive rows at one chunk, so the 16 chunks
 //    must fall in distinct 16-byte bank groups of the 256-byte LDS line;
 //  * transposed (ds_read_b64_tr_b16): 32 lanes read 4 consecutive rows 4a+e
@@ -132,19 +132,29 @@ __device__ __forceinline__ void static_for(F&& f) {
 // d = 32 (4 chunks, four rows per line, the line quarter given by r%4): the
 // XOR follows r/4 % 4, so the four rows of 16 that share a line quarter take
 // four different chunk positions; a transposed read covers whole rows, one
-// per line quarter.  d = 64 (8 chunks, two rows per line, the line half given by r%2): bits 0-1
-// of the XOR walk the four aligned 4-row groups of 16 rows and bit 2 follows
-// r/2 % 2, which puts rows 4a and 4a+2 (same line half) in different 4-chunk
-// halves.  d = 128 (16 chunks, one row per line): bits 2-3 follow r%4 (the
-// four rows of a transposed read in four different 4-chunk groups) and bits
-// 0-1 follow r/4 % 4, so 16 consecutive rows take 16 distinct values.  Both
-// depend on r only through r%16.
+// per line quarter.  d = 64 (8 chunks, two rows per line, the line half given
+// by r%2): bits 0-1 of the XOR walk the four aligned 4-row groups of 16 rows
+// and bit 2 follows r/2 % 2, which puts rows 4a and 4a+2 (same line half) in
+// different 4-chunk halves.  d = 128 and 256 (16 or 32 chunks, whole lines):
+// bits 2-3 follow r%4 (the four rows of a transposed read in four different
+// 4-chunk groups) and bits 0-1 follow r/4 % 4, so 16 consecutive rows take 16
+// distinct values.  d = 96 (12 chunks, rows starting at bank groups 12r mod
+// 16, which repeat every 4 rows): the chunks rotate by r/4 % 4 within the
+// row, which separates rows 4 apart for the plain read; the four rows of a
+// transposed read already start 12 groups apart.  (Every rule was checked
+// exhaustively for both reads.)  All depend on r only through r%16.
 template <int D>
-__device__ __forceinline__ int bwd_swz(int row) {
-  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "backward head dims");
-  if constexpr (D == 32) return (row >> 2) & 3;
-  if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-  return ((row & 3) << 2) | ((row >> 2) & 3);
+__device__ __forceinline__ int bwd_pos(int row, int c) {
+  static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "backward head dims");
+  if constexpr (D == 32) return c ^ ((row >> 2) & 3);
+  if constexpr (D == 64) return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  if constexpr (D == 96) return (c + ((row >> 2) & 3)) % 12;
+  return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
+}
+template <int D>
+__device__ __forceinline__ int bwd_chunk(int row, int p) {
+  if constexpr (D == 96) return (p + 12 - ((row >> 2) & 3)) % 12;
+  return bwd_pos<D>(row, p);  // the XOR rules are involutions
 }
 
 template <int D, bool BF16>
@@ -171,7 +181,7 @@ struct BwdBase {
   // the swizzle).
   static __device__ __forceinline__ int plain_off(int lane, int ks) {
     const int row = lane & 31;
-    return row * ROWB + (((2 * ks + (lane >> 5)) ^ bwd_swz<D>(row)) << 4);
+    return row * ROWB + (bwd_pos<D>(row, 2 * ks + (lane >> 5)) << 4);
   }
   // Transposed read of dims 32db.. of 16 rows: lane group g = L/16 serves A
   // rows (dims) 16(g%2) + L%16; as a source, lane 16g + 4e + u reads row
@@ -183,7 +193,7 @@ struct BwdBase {
     const int g = lane >> 4;
     const int row = 4 * (g >> 1) + ((lane >> 2) & 3) + 8 * second;
     const int c = 4 * db + 2 * (g & 1) + ((lane & 3) >> 1);
-    return row * ROWB + ((c ^ bwd_swz<D>(row)) << 4) + 8 * (lane & 1);
+    return row * ROWB + (bwd_pos<D>(row, c) << 4) + 8 * (lane & 1);
   }
   static __device__ __forceinline__ u32x4 tr_frag(const lds_char* base, int off0, int off1) {
     const s16x4 a = tr16(base + off0);
@@ -214,7 +224,7 @@ struct BwdBase {
 
   // Staging of a ROWS-row tile by T threads: thread t copies linear LDS slots
   // t + T j; slot s is row s / CPR at position s % CPR, which holds chunk
-  // (s % CPR) ^ bwd_swz(row) of that row (the XOR is an involution).
+  // bwd_chunk(row, s % CPR) of that row.
   template <int ROWS, int T>
   struct Stager {
     static constexpr int CPT = ROWS * CPR / T;
@@ -226,7 +236,7 @@ struct BwdBase {
       for (int j = 0; j < CPT; ++j) {
         const int s = tid + T * j;
         const int row = s / CPR;
-        const int c = (s % CPR) ^ bwd_swz<D>(row);
+        const int c = bwd_chunk<D>(row, s % CPR);
         goff[j] = (row * D + c * 8) * 2;
       }
       lds0 = (tid & ~63) * 16;
@@ -559,9 +569,9 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
   static constexpr int LDS_BYTES = 2 * SLOTB;
   static_assert(BQ % 64 == 0 && NW >= 2, "the row statistics of a tile are 64-lane dword copies");
   using St = typename Base::template Stager<BQ, THREADS>;
-  // dV and dK accumulators in AGPRs from d = 128 (one wave per SIMD: the
+  // dV and dK accumulators in AGPRs from d = 96 (one wave per SIMD: the
   // arch VGPRs hold the rest; see BwdBase::acc_mfma).
-  static constexpr bool ACC_AGPR = D >= 128;
+  static constexpr bool ACC_AGPR = D >= 96;
   // Software pipeline over the QBLK 32-row blocks of a tile: step j issues
   // the MFMAs of dV(j-1) and dK(j-1) (NG, u = 0 first), then of S(j+1) and
   // dP(j+1) (NSD, alternating), one at a time, each followed by its share of

@@ -82,7 +82,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     """Gradients (dQ, dK, dV) of the attention of ``forward`` given dO.
 
     q, k, v, o, do: [B, H, N, d] fp16/bf16 tensors of one dtype on one GPU
-    (d = 32, 64, 128 or 256); o and lse are forward's outputs for the same q, k, v,
+    (d = 32, 64, 96, 128 or 256); o and lse are forward's outputs for the same q, k, v,
     scale and causal.  ``workspace`` (float32, 2*B*H*N elements) and ``out``
     (a (dq, dk, dv) tuple of tensors like q) may be given to reuse buffers.
     ``window`` and ``key_lens`` are those of ``forward`` (through

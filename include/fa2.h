@@ -162,7 +162,7 @@ fa2_status_t fa2_fwd_masked(const void* Q, const void* K, const void* V, void* O
  *             the call's work has run it holds -Delta of every row ([B, H, N])
  *             followed by -LSE * log2(e) of every row ([B, H, N]).
  *   B, H, N, scale, is_causal, dtype, stream: as for fa2_fwd, with d = 32,
- *             64, 128 or 256 only, and ceil(N / 128) * H * B < 2^31.
+ *             64, 96, 128 or 256 only, and ceil(N / 128) * H * B < 2^31.
  *
  * Numerics: S, dP, Delta and the accumulators are fp32; P and dS are rounded
  * to `dtype` (to nearest even) before the products that take them, and the
@@ -173,7 +173,7 @@ fa2_status_t fa2_fwd_masked(const void* Q, const void* K, const void* V, void* O
  * (first dQ and the row statistics, then dK and dV), allocates nothing and does not
  * synchronise.  Errors: as for fa2_fwd; FA2_ERR_OVERLAP when dQ, dK, dV or
  * the workspace overlaps an input or one another; FA2_ERR_UNSUPPORTED_HEAD_DIM
- * for d other than 32, 64, 128 and 256.
+ * for d other than 32, 64, 96, 128 and 256.
  */
 fa2_status_t fa2_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                      const float* LSE, void* dQ, void* dK, void* dV, float* workspace,

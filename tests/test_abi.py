@@ -219,7 +219,7 @@ def test_bwd_bad_shape(kw):
     assert call_bwd(**kw) == bd.FA2_ERR_BAD_SHAPE
 
 
-@pytest.mark.parametrize("d", [0, 16, 48, 96, 512, 1024])
+@pytest.mark.parametrize("d", [0, 16, 48, 80, 512, 1024])
 def test_bwd_unsupported_head_dim(d):
     assert call_bwd(d=d) == bd.FA2_ERR_UNSUPPORTED_HEAD_DIM
 
@@ -253,7 +253,7 @@ def test_bwd_noalloc_checks_and_scratch_limit():
                 B=1, H=64, N=(1 << 21) // 64 + 1, d=64, scale=0.125, is_causal=0, dtype=0, stream=0)
     assert fa.fa2_bwd_noalloc(**base) == bd.FA2_ERR_TOO_LARGE
     assert fa.fa2_bwd_noalloc(**{**base, "dQ": 0}) == bd.FA2_ERR_NULL_POINTER
-    assert fa.fa2_bwd_noalloc(**{**base, "d": 96}) == bd.FA2_ERR_UNSUPPORTED_HEAD_DIM
+    assert fa.fa2_bwd_noalloc(**{**base, "d": 80}) == bd.FA2_ERR_UNSUPPORTED_HEAD_DIM
     assert fa.fa2_bwd_noalloc(**{**base, "dK": p[0]}) == bd.FA2_ERR_OVERLAP
 
 
@@ -262,7 +262,7 @@ def test_bwd_masked_checks():
                 B=2, H=2, N=100, d=64, scale=0.125, window_left=16, window_right=0, key_lens=LENS,
                 dtype=0, stream=0)
     assert fa.fa2_bwd_masked(**{**base, "workspace": 0}) == bd.FA2_ERR_NULL_POINTER
-    assert fa.fa2_bwd_masked(**{**base, "d": 96}) == bd.FA2_ERR_UNSUPPORTED_HEAD_DIM
+    assert fa.fa2_bwd_masked(**{**base, "d": 80}) == bd.FA2_ERR_UNSUPPORTED_HEAD_DIM
     assert fa.fa2_bwd_masked(**{**base, "key_lens": LENS + 2}) == bd.FA2_ERR_MISALIGNED
     assert fa.fa2_bwd_masked(**{**base, "dQ": LENS}) == bd.FA2_ERR_OVERLAP
     assert fa.fa2_bwd_masked(**{**base, "N": 0}) == bd.FA2_ERR_BAD_SHAPE

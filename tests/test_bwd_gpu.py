@@ -85,6 +85,8 @@ SMALL = [
     (1, 2, 300, 256, wl.BF16, False, None, ONE),
     (2, 1, 257, 256, wl.FP16, True, None, ONE),
     (1, 1, 70, 256, wl.BF16, True, 0.2, (3.0, 3.0, 1.0, 1.0)),
+    (2, 2, 301, 96, wl.FP16, False, None, ONE),
+    (1, 2, 257, 96, wl.BF16, True, -0.15, ONE),
 ]
 
 
@@ -149,7 +151,7 @@ def test_bwd_on_a_side_stream(gpu_device):
 
 def _draw_bwd_case(i):
     rng = np.random.default_rng(5000 + i)
-    d = int(rng.choice((32, 64, 128, 256)))
+    d = int(rng.choice((32, 64, 96, 128, 256)))
     B, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
     N = int(rng.integers(1, 700))
     dtype = wl.FP16 if rng.random() < 0.5 else wl.BF16
@@ -187,6 +189,7 @@ MASKED = [
     ((3, 1, 150, 64, wl.FP16), (0, 0, [150, 1, 77])),
     ((2, 2, 280, 32, wl.BF16), (50, 10, [280, 99])),
     ((2, 1, 300, 256, wl.BF16), (70, 0, [300, 130])),
+    ((1, 3, 222, 96, wl.FP16), (-1, 20, [150])),
 ]
 
 
