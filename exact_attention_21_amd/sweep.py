@@ -11,7 +11,8 @@ N(0, 1) fp16 (or bf16) tensors made on the GPU.
 
 prints one markdown table row per (d, causal, N): time per call and TFLOP/s
 (4 B H N^2 d, halved for causal) as a share of the 2516.6 TFLOP/s dense
-fp16/bf16 MFMA peak.
+fp16/bf16 MFMA peak.  ``--pass bwd`` sweeps the backward (fa2_bwd on the
+forward's O and LSE and a seeded dO; 10 B H N^2 d FLOPs, halved for causal).
 """
 from __future__ import annotations
 
@@ -55,10 +56,11 @@ def main() -> int:
     ap.add_argument("--dims", default="64,128,256")
     ap.add_argument("--dtype", default="fp16", choices=("fp16", "bf16"))
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd")
     args = ap.parse_args()
 
     import torch
-    from exact_attention_21_amd import forward
+    from exact_attention_21_amd import backward, forward
 
     dev = torch.device("cuda:0")
     dt = torch.float16 if args.dtype == "fp16" else torch.bfloat16
@@ -75,8 +77,18 @@ def main() -> int:
                 o = torch.empty_like(q)
                 lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
                 scale = d ** -0.5
-                ms = time_call(lambda: forward(q, k, v, scale=scale, causal=causal, out=o, lse=lse), stream)
                 flops = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
+                if args.pass_ == "bwd":
+                    forward(q, k, v, scale=scale, causal=causal, out=o, lse=lse)
+                    do = torch.randn(B, H, N, d, generator=g, device=dev).to(dt)
+                    grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+                    ws = torch.empty((2, B, H, N), dtype=torch.float32, device=dev)
+                    ms = time_call(lambda: backward(q, k, v, o, lse, do, scale=scale, causal=causal, workspace=ws,
+                                                    out=grads), stream)
+                    flops *= 2.5
+                    del do, grads, ws
+                else:
+                    ms = time_call(lambda: forward(q, k, v, scale=scale, causal=causal, out=o, lse=lse), stream)
                 tf = flops / ms / 1e9
                 print(f"| {d} | {causal} | {N} | {B} | {H} | {ms:.4f} | {tf:.1f} | {100 * tf / PEAK_TFLOPS:.1f} |",
                       flush=True)
