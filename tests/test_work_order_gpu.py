@@ -10,9 +10,16 @@ of 16 query tiles at d = 128, no mask (groups of 16 and 5); 36 slices of 8 at
 d = 64, no mask (32 and 4); 136 causal slices of 4 at d = 64 (64, 64, 8); 132
 padded causal slices of 5 at d = 96 (48, 48, 36); 36 slices of 8 at d = 64
 under a window bounded on both sides, which is grouped like no mask (32 and
-4).  O and LSE start as NaN, so
-a tile that no workgroup writes fails, and every element is compared with the
-fp64 oracle.
+4).
+
+Causal grids of more than one round of resident workgroups and at most two
+(one workgroup per compute unit: 256 < grid <= 512), whose second round
+takes the short query tiles: 20 slices of 16 tiles at d = 128, 40 of 8 at
+d = 64 (split-KV), 17 of 17 at d = 128 (an odd count), 14 of 22 at d = 256
+and 5 of 63 at d = 1024.
+
+O and LSE start as NaN, so a tile that no workgroup writes fails, and every
+element is compared with the fp64 oracle.
 """
 import numpy as np
 import pytest
@@ -30,6 +37,11 @@ CASES = [
     (8, 17, 1024, 64, wl.BF16, True, None),
     (4, 33, 640, 96, wl.FP16, False, (-1, 0, [640, 401, 77, 639])),
     (4, 9, 2048, 64, wl.FP16, False, (100, 20, None)),
+    (1, 20, 4096, 128, wl.BF16, True, None),
+    (1, 40, 2048, 64, wl.FP16, True, None),
+    (1, 17, 4300, 128, wl.BF16, True, None),
+    (1, 14, 2800, 256, wl.FP16, True, None),
+    (1, 5, 4000, 1024, wl.BF16, True, None),
 ]
 
 
