@@ -195,9 +195,9 @@ struct BwdBase {
     const int c = 4 * db + 2 * (g & 1) + ((lane & 3) >> 1);
     return row * ROWB + (bwd_pos<D>(row, c) << 4) + 8 * (lane & 1);
   }
-  static __device__ __forceinline__ u32x4 tr_frag(const lds_char* base, int off0, int off1) {
-    const s16x4 a = tr16(base + off0);
-    const s16x4 b = tr16(base + off1);
+  static __device__ __forceinline__ u32x4 tr_frag(const lds_char* p0, const lds_char* p1) {
+    const s16x4 a = tr16(p0);
+    const s16x4 b = tr16(p1);
     u32x4 r;
     r[0] = __builtin_bit_cast(u32x2, a)[0];
     r[1] = __builtin_bit_cast(u32x2, a)[1];
@@ -205,6 +205,61 @@ struct BwdBase {
     r[3] = __builtin_bit_cast(u32x2, b)[1];
     return r;
   }
+
+  // x ^ k, issued where it is used: the asm keeps the compiler from holding
+  // one register per constant k through the loop (it would hoist the XORs of
+  // a loop-invariant x) or from merging equal ones.
+  static __device__ __forceinline__ int xor_at(int x, int k) {
+    if (k == 0) return x;
+    int r;
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(k), "v"(x));
+    return r;
+  }
+
+  // LDS pointer of a byte address.
+  static __device__ __forceinline__ const lds_char* at(int addr) { return (const lds_char*)(uintptr_t)(uint32_t)addr; }
+  // LDS byte address of a pointer.
+  static __device__ __forceinline__ int addr_of(const lds_char* p) { return (int)(uint32_t)(uintptr_t)p; }
+
+  // Addresses of the fragment reads of a tile at LDS byte address `base` (a
+  // multiple of ROWB: the slots sit at multiples of ROWB from the start of
+  // the kernels' dynamic LDS, address 0, as they declare no static LDS).  Under the XOR chunk permutations (every head dim but
+  // 96) chunk c of a row sits at byte 16 (c ^ f) = 16 c ^ 16 f of it, below
+  // ROWB (a power of two), so the plain read of k-step ks is
+  // plain_off(lane, 0) ^ 32 ks and the transposed read of dims 32 db.. is
+  // tr_off(lane, 0, s) ^ 64 db, each plus the base: three lane offsets and
+  // one XOR at each read, where one register per read offset held through
+  // the loop made the d = 256 kernels spill (and each spill reload waited
+  // for the tile loads in flight).  Narrower head dims keep one offset per
+  // read: they fit their registers, and the XORs cost issue slots that their
+  // two waves per SIMD need for the softmax (measured 2.5% to 5% slower).
+  struct FragOff {
+    static constexpr bool XOR = D >= 256;
+    int p0, t0, t1;
+    int pk[XOR ? 1 : DK], tk[XOR ? 1 : DB][2];
+    __device__ __forceinline__ explicit FragOff(int lane) {
+      p0 = plain_off(lane, 0);
+      t0 = tr_off(lane, 0, 0);
+      t1 = tr_off(lane, 0, 1);
+      if constexpr (!XOR) {
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) pk[ks] = plain_off(lane, ks);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          tk[db][0] = tr_off(lane, db, 0);
+          tk[db][1] = tr_off(lane, db, 1);
+        }
+      }
+    }
+    __device__ __forceinline__ int plain(int base, int ks) const {
+      if constexpr (XOR) return xor_at(p0 + base, 32 * ks);
+      return pk[ks] + base;
+    }
+    __device__ __forceinline__ int tr(int base, int db, int second) const {
+      if constexpr (XOR) return xor_at((second ? t1 : t0) + base, 64 * db);
+      return tk[db][second] + base;
+    }
+  };
 
   // Global -> LDS copies that bypass the VGPRs: lane L of the wave writes its
   // 16 (or 4) bytes at the LDS address `dst` + 16 L (4 L).  Written as inline
@@ -224,16 +279,25 @@ struct BwdBase {
 
   // Staging of a ROWS-row tile by T threads: thread t copies linear LDS slots
   // t + T j; slot s is row s / CPR at position s % CPR, which holds chunk
-  // bwd_chunk(row, s % CPR) of that row.
+  // bwd_chunk(row, s % CPR) of that row.  At d = 256 (T a multiple of CPR)
+  // slot j of a thread is RJ = T / CPR rows below slot 0, and as the chunk
+  // permutations depend on the row only through r % 16, the offsets repeat
+  // every PER = 16 / gcd(16, RJ) slots up to whole rows: PER lane offsets,
+  // each made opaque at every staging so that the compiler adds the row
+  // terms there instead of holding one register per slot (which spilled).
+  // Narrower head dims keep one offset per slot.
   template <int ROWS, int T>
   struct Stager {
     static constexpr int CPT = ROWS * CPR / T;
     static_assert(CPT >= 1 && (ROWS * CPR) % T == 0, "staging split");
-    int goff[CPT];  // global byte offset within the tile
+    static constexpr int RJ = D >= 256 && T % CPR == 0 ? T / CPR : 0;
+    static constexpr int PER0 = RJ == 0 ? CPT : RJ % 16 == 0 ? 1 : RJ % 8 == 0 ? 2 : RJ % 4 == 0 ? 4 : RJ % 2 == 0 ? 8 : 16;
+    static constexpr int PER = PER0 < CPT ? PER0 : CPT;
+    int goff[PER];  // global byte offset within the tile of slots 0 .. PER-1
     int lds0;       // this wave's first slot (bytes)
     __device__ __forceinline__ Stager(int tid) {
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) {
+      for (int j = 0; j < PER; ++j) {
         const int s = tid + T * j;
         const int row = s / CPR;
         const int c = bwd_chunk<D>(row, s % CPR);
@@ -241,10 +305,18 @@ struct BwdBase {
       }
       lds0 = (tid & ~63) * 16;
     }
-    // Tile of rows r0.. into LDS at dst.
+    // Tile of rows r0.. into LDS at dst.  The row term stays in the VGPR
+    // offset: the range check that zero-fills rows past the end covers it.
     __device__ __forceinline__ void stage(const u32x4& rsrc, const lds_char* dst, int r0) const {
+      int g[PER];
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) dma16(rsrc, dst + lds0 + T * 16 * j, goff[j] + r0 * ROWB);
+      for (int i = 0; i < PER; ++i) {
+        g[i] = goff[i];
+        if constexpr (RJ != 0) asm volatile("" : "+v"(g[i]));
+      }
+#pragma unroll
+      for (int j = 0; j < CPT; ++j)
+        dma16(rsrc, dst + lds0 + T * 16 * j, g[j % PER] + (r0 + (j - j % PER) * RJ) * ROWB);
     }
   };
 
@@ -333,6 +405,7 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
   static constexpr int SLOTB = 2 * TILEB;  // one K tile and one V tile
   static constexpr int LDS_BYTES = 2 * SLOTB;
   using St = typename Base::template Stager<BC, THREADS>;
+  static_assert(!Base::FragOff::XOR || SLOTB % ROWB == 0, "slot bases keep the fragment offsets' XOR bits");
   // Software pipeline over the KB 32-key blocks of a tile: step j issues the
   // MFMAs of S(j+1) and dP(j+1) (NSD, S and dP alternating) and of
   // dQ += K^T dS(j-1) (NQ), one at a time, each followed by its share of the
@@ -402,14 +475,7 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
     for (int r = 0; r < 16; ++r) dp0[r] = ndelta;
 
     // Lane-constant LDS offsets.
-    int poff[DK], toff[DB][2];
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) poff[ks] = Base::plain_off(lane, ks);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      toff[db][0] = Base::tr_off(lane, db, 0);
-      toff[db][1] = Base::tr_off(lane, db, 1);
-    }
+    const typename Base::FragOff fo(lane);
     const St st(tid);
     // K and V are range-checked at the keys present (N, or the sequence's
     // key length: rows past it may hold anything and are never read).
@@ -449,8 +515,7 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
       constexpr bool MASKED = decltype(masked_c)::value;
       Base::dma_wait();
       __syncthreads();
-      const lds_char* sk = lds + ((t - tfirst) & 1) * SLOTB;
-      const lds_char* sv = sk + TILEB;
+      const int slot = Base::addr_of(lds) + ((t - tfirst) & 1) * SLOTB;
       if (t + 1 < tend) {
         const lds_char* nk = lds + ((t + 1 - tfirst) & 1) * SLOTB;
         st.stage(wk, nk, (t + 1) * BC);
@@ -464,11 +529,11 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
       auto frag = [&](int j, int pos) __attribute__((always_inline)) -> u32x4 {
         if (pos < NSD) {
           const int kb = j + 1, ks = pos / 2;
-          return Base::lds16((pos % 2 ? sv : sk) + poff[ks] + kb * 32 * ROWB);
+          return Base::lds16(Base::at(fo.plain(slot, ks)) + (pos % 2 ? TILEB : 0) + kb * 32 * ROWB);
         }
         const int kb = j - 1, u = (pos - NSD) / DB, db = (pos - NSD) % DB;
         const int rows = (kb * 32 + 16 * u) * ROWB;
-        return Base::tr_frag(sk, toff[db][0] + rows, toff[db][1] + rows);
+        return Base::tr_frag(Base::at(fo.tr(slot, db, 0)) + rows, Base::at(fo.tr(slot, db, 1)) + rows);
       };
       auto active = [&](int j, int pos) __attribute__((always_inline)) { return pos < NSD ? j + 1 < KB : j >= 1; };
       auto issue = [&](int j, int pos, const u32x4& a) __attribute__((always_inline)) {
@@ -569,6 +634,7 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
   static constexpr int LDS_BYTES = 2 * SLOTB;
   static_assert(BQ % 64 == 0 && NW >= 2, "the row statistics of a tile are 64-lane dword copies");
   using St = typename Base::template Stager<BQ, THREADS>;
+  static_assert(!Base::FragOff::XOR || SLOTB % ROWB == 0, "slot bases keep the fragment offsets' XOR bits");
   // dV and dK accumulators in AGPRs from d = 96 (one wave per SIMD: the
   // arch VGPRs hold the rest; see BwdBase::acc_mfma).
   static constexpr bool ACC_AGPR = D >= 96;
@@ -621,14 +687,7 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
       vf[ks] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     }
 
-    int poff[DK], toff[DB][2];
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) poff[ks] = Base::plain_off(lane, ks);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      toff[db][0] = Base::tr_off(lane, db, 0);
-      toff[db][1] = Base::tr_off(lane, db, 1);
-    }
+    const typename Base::FragOff fo(lane);
     const St st(tid);
     const u32x4 wq = rsrc_words(p.q, slice * 2, bytes);
     const u32x4 wdo = rsrc_words(p.dout, slice * 2, bytes);
@@ -679,9 +738,8 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
       constexpr bool MASKED = decltype(masked_c)::value;
       Base::dma_wait();
       __syncthreads();
-      const lds_char* sq = lds + ((t - tfirst) & 1) * SLOTB;
-      const lds_char* sdo = sq + TILEB;
-      const lds_char* sst = sq + 2 * TILEB;
+      const int slot = Base::addr_of(lds) + ((t - tfirst) & 1) * SLOTB;
+      const lds_char* sst = Base::at(slot) + 2 * TILEB;
       if (t + 1 < tend) stage(t + 1, lds + ((t + 1 - tfirst) & 1) * SLOTB);
       const int q0 = t * BQ;
       f32x16 sc[2], dp[2];      // S and dP - Delta of blocks of either parity
@@ -704,11 +762,11 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
       auto frag = [&](int j, int pos) __attribute__((always_inline)) -> u32x4 {
         if (pos < NG) {
           const int qb = j - 1, u = pos / (2 * DB), db = (pos % (2 * DB)) / 2;
-          const int rows = (qb * 32 + 16 * u) * ROWB;
-          return Base::tr_frag(pos % 2 ? sq : sdo, toff[db][0] + rows, toff[db][1] + rows);
+          const int rows = (pos % 2 ? 0 : TILEB) + (qb * 32 + 16 * u) * ROWB;
+          return Base::tr_frag(Base::at(fo.tr(slot, db, 0)) + rows, Base::at(fo.tr(slot, db, 1)) + rows);
         }
         const int qb = j + 1, ks = (pos - NG) / 2;
-        return Base::lds16(((pos - NG) % 2 ? sdo : sq) + poff[ks] + qb * 32 * ROWB);
+        return Base::lds16(Base::at(fo.plain(slot, ks)) + ((pos - NG) % 2 ? TILEB : 0) + qb * 32 * ROWB);
       };
       auto active = [&](int j, int pos) __attribute__((always_inline)) { return pos < NG ? j >= 1 : j + 1 < QBLK; };
       auto issue = [&](int j, int pos, const u32x4& a) __attribute__((always_inline)) {

@@ -9,9 +9,11 @@ construction (the packing of P is pinned well before the output MFMAs; an
 explicit `s_nop 7; s_nop 7; s_nop 3` precedes every compiler-issued read of
 the AGPR accumulators).  This module finds violations in the assembly text:
 
-* `valu_write_before_asm_mfma`: a VALU instruction writes a VGPR that an
-  inline-asm MFMA reads as its A or B operand within the few instructions
-  before it;
+* `valu_write_before_asm_mfma`: a VALU instruction (compiler-issued or
+  inline asm) writes a VGPR that an inline-asm MFMA reads as its A or B
+  operand within the few instructions before it, and no load into that
+  register comes in between (a load's result, which the MFMA then reads,
+  is awaited by a memory-counter wait, not by wait states);
 * `agpr_read_after_asm_mfma`: an instruction the compiler issued (VALU,
   `v_accvgpr_read/mov`, an MFMA reading its C operand, a store) reads an AGPR
   that an inline-asm MFMA writes, with fewer than `required` wait states in
@@ -36,6 +38,7 @@ REQUIRED_AFTER_MFMA = 19
 # register as an operand.
 REQUIRED_BEFORE_MFMA = 4
 STORE_PREFIXES = ("buffer_store", "scratch_store")
+LOAD_PREFIXES = ("ds_read", "ds_load", "buffer_load", "global_load", "flat_load", "scratch_load")
 
 
 def regs(operand: str, kind: str) -> set:
@@ -85,6 +88,13 @@ class Instr:
 
     def vgpr_writes(self) -> set:
         if not self.mnem.startswith("v_") or not self.ops:
+            return set()
+        return regs(self.ops[0], "v")
+
+    def load_writes(self) -> set:
+        """VGPRs a memory load writes (none for loads straight into LDS,
+        whose first operand is an address)."""
+        if not self.mnem.startswith(LOAD_PREFIXES) or not self.ops or re.search(r"\blds\s*$", self.text):
             return set()
         return regs(self.ops[0], "v")
 
@@ -171,6 +181,36 @@ def walk_back(blocks, preds, b, i, limit, hit):
     return best
 
 
+def valu_write_distance(blocks, preds, b, i, srcs, limit):
+    """Smallest wait-state distance, over the paths backwards from
+    instruction i of block b, to a VALU write of one of the registers `srcs`
+    that no later load on the path overwrites; None when there is none
+    within `limit`."""
+    best = None
+    stack = [(b, i, 0, frozenset(srcs))]
+    seen = {}
+    while stack:
+        blk, idx, acc, live = stack.pop()
+        while idx > 0 and live:
+            idx -= 1
+            ins = blocks[blk][idx]
+            if ins.mnem.startswith("v_") and not ins.mnem.startswith(("v_mfma", "v_smfmac")) and \
+                    ins.vgpr_writes() & live:
+                best = acc if best is None else min(best, acc)
+                break
+            live = live - ins.load_writes()
+            acc += ins.waits
+            if acc >= limit:
+                break
+        else:
+            if live:
+                for p in preds[blk]:
+                    if seen.get((p, live), limit + 1) > acc:
+                        seen[(p, live)] = acc
+                        stack.append((p, len(blocks[p]), acc, live))
+    return best
+
+
 def check_kernel(items):
     """List of (kind, message) violations in one kernel."""
     blocks, preds = cfg(items)
@@ -183,10 +223,7 @@ def check_kernel(items):
                 srcs = regs(mf.group(2), "v") | regs(mf.group(3), "v")
                 src_c = regs(mf.group(4), "a")
 
-                def valu_hit(x, srcs=srcs):
-                    return (not x.asm and x.mnem.startswith("v_") and not x.mnem.startswith(("v_mfma", "v_smfmac"))
-                            and bool(x.vgpr_writes() & srcs))
-                d = walk_back(blocks, preds, b, i, REQUIRED_BEFORE_MFMA, valu_hit)
+                d = valu_write_distance(blocks, preds, b, i, srcs, REQUIRED_BEFORE_MFMA)
                 if d is not None:
                     found.append(("valu_write_before_asm_mfma", f"{ins.text} ({d} wait states after a VALU write)"))
 

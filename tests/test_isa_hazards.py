@@ -112,3 +112,21 @@ def test_checker_flags_operand_writes_before_asm_mfma():
     assert _kinds("\tv_cvt_pk_f16_f32 v7, v1, v2\n" + ASM_MFMA) == ["valu_write_before_asm_mfma"]
     assert _kinds("\tv_accvgpr_write_b32 a4, v1\n\ts_nop 0\n" + ASM_MFMA) == ["agpr_write_before_asm_mfma"]
     assert _kinds("\tv_cvt_pk_f16_f32 v7, v1, v2\n\ts_nop 4\n" + ASM_MFMA) == []
+
+
+def test_checker_operand_write_superseded_by_a_load():
+    # A VALU write of an operand register that a load then overwrites: the
+    # MFMA reads the load's result (awaited by s_waitcnt), not the VALU's.
+    load = "\tds_read_b64 v[2:3], v2\n\ts_waitcnt lgkmcnt(0)\n"
+    assert _kinds("\tv_add_u32_e32 v2, 0, v2\n" + load + ASM_MFMA) == []
+    # The load covers v2 and v3 only: a write of v4 still counts.
+    assert _kinds("\tv_add_u32_e32 v4, 0, v4\n" + load + ASM_MFMA) == ["valu_write_before_asm_mfma"]
+    # A load straight into LDS writes no VGPR (its first operand is an address).
+    assert _kinds("\tv_add_u32_e32 v2, 0, v2\n\tbuffer_load_dword v2, s[0:3], 0 offen lds\n" + ASM_MFMA) == \
+        ["valu_write_before_asm_mfma"]
+
+
+def test_checker_flags_inline_asm_valu_writes():
+    asm_xor = "\t;;#ASMSTART\n\tv_xor_b32 v6, s1, v6\n\t;;#ASMEND\n"
+    assert _kinds(asm_xor + ASM_MFMA) == ["valu_write_before_asm_mfma"]
+    assert _kinds(asm_xor + "\tds_read_b128 v[6:9], v6\n\ts_waitcnt lgkmcnt(0)\n" + ASM_MFMA) == []
