@@ -91,6 +91,7 @@ struct BwdParams {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+
 // Work item of workgroup wg: its (batch*head) slice and its step (tile
 // index, counted from the longest tile under a mask).  The slices are taken
 // in groups of p.group, every tile of a group before the next group, the step
@@ -229,15 +230,16 @@ struct BwdBase {
   // plain_off(lane, 0) ^ 32 ks and the transposed read of dims 32 db.. is
   // tr_off(lane, 0, s) ^ 64 db, each plus the base: three lane offsets and
   // one XOR at each read, where one register per read offset held through
-  // the loop made the d = 256 kernels spill (and each spill reload waited
-  // for the tile loads in flight).  Narrower head dims keep one offset per
-  // read: they fit their registers, and the XORs cost issue slots that their
-  // two waves per SIMD need for the softmax (measured 2.5% to 5% slower).
-  struct FragOff {
-    static constexpr bool XOR = D >= 256;
+  // the loop made the d = 256 dK/dV kernel spill (and each spill reload
+  // waited for the tile loads in flight).  XOR_ = false keeps one offset per
+  // read, for the kernels that fit their registers: there the XORs only cost
+  // issue slots (measured 2.5% to 5% slower at d <= 128).
+  template <bool XOR_>
+  struct FragOffT {
+    static constexpr bool XOR = XOR_ && D != 96;
     int p0, t0, t1;
     int pk[XOR ? 1 : DK], tk[XOR ? 1 : DB][2];
-    __device__ __forceinline__ explicit FragOff(int lane) {
+    __device__ __forceinline__ explicit FragOffT(int lane) {
       p0 = plain_off(lane, 0);
       t0 = tr_off(lane, 0, 0);
       t1 = tr_off(lane, 0, 1);
@@ -279,18 +281,18 @@ struct BwdBase {
 
   // Staging of a ROWS-row tile by T threads: thread t copies linear LDS slots
   // t + T j; slot s is row s / CPR at position s % CPR, which holds chunk
-  // bwd_chunk(row, s % CPR) of that row.  At d = 256 (T a multiple of CPR)
+  // bwd_chunk(row, s % CPR) of that row.  PERIODIC (T a multiple of CPR):
   // slot j of a thread is RJ = T / CPR rows below slot 0, and as the chunk
   // permutations depend on the row only through r % 16, the offsets repeat
   // every PER = 16 / gcd(16, RJ) slots up to whole rows: PER lane offsets,
   // each made opaque at every staging so that the compiler adds the row
-  // terms there instead of holding one register per slot (which spilled).
-  // Narrower head dims keep one offset per slot.
-  template <int ROWS, int T>
+  // terms there instead of holding one register per slot (used at d = 256,
+  // where those registers spilled).  Otherwise one offset per slot.
+  template <int ROWS, int T, bool PERIODIC>
   struct Stager {
     static constexpr int CPT = ROWS * CPR / T;
     static_assert(CPT >= 1 && (ROWS * CPR) % T == 0, "staging split");
-    static constexpr int RJ = D >= 256 && T % CPR == 0 ? T / CPR : 0;
+    static constexpr int RJ = PERIODIC && T % CPR == 0 ? T / CPR : 0;
     static constexpr int PER0 = RJ == 0 ? CPT : RJ % 16 == 0 ? 1 : RJ % 8 == 0 ? 2 : RJ % 4 == 0 ? 4 : RJ % 2 == 0 ? 8 : 16;
     static constexpr int PER = PER0 < CPT ? PER0 : CPT;
     int goff[PER];  // global byte offset within the tile of slots 0 .. PER-1
@@ -404,8 +406,15 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
   static constexpr int TILEB = BC * ROWB;
   static constexpr int SLOTB = 2 * TILEB;  // one K tile and one V tile
   static constexpr int LDS_BYTES = 2 * SLOTB;
-  using St = typename Base::template Stager<BC, THREADS>;
-  static_assert(!Base::FragOff::XOR || SLOTB % ROWB == 0, "slot bases keep the fragment offsets' XOR bits");
+  // Fragment and staging addresses (FragOffT, Stager): one register per
+  // fragment read (the XOR at each read measured 4% to 5% slower at d = 256,
+  // where this kernel does not spill either way); staging offsets kept to the
+  // permutation's period at d = 256.
+  static constexpr bool XOR_ADDR = false;
+  static constexpr bool PERIODIC_STAGE = D >= 256;
+  using FragOff = typename Base::template FragOffT<XOR_ADDR>;
+  using St = typename Base::template Stager<BC, THREADS, PERIODIC_STAGE>;
+  static_assert(!FragOff::XOR || SLOTB % ROWB == 0, "slot bases keep the fragment offsets' XOR bits");
   // Software pipeline over the KB 32-key blocks of a tile: step j issues the
   // MFMAs of S(j+1) and dP(j+1) (NSD, S and dP alternating) and of
   // dQ += K^T dS(j-1) (NQ), one at a time, each followed by its share of the
@@ -475,7 +484,7 @@ struct Fa2BwdQ : BwdBase<D, BF16> {
     for (int r = 0; r < 16; ++r) dp0[r] = ndelta;
 
     // Lane-constant LDS offsets.
-    const typename Base::FragOff fo(lane);
+    const FragOff fo(lane);
     const St st(tid);
     // K and V are range-checked at the keys present (N, or the sequence's
     // key length: rows past it may hold anything and are never read).
@@ -633,8 +642,14 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
   static constexpr int SLOTB = 2 * TILEB + 2 * BQ * 4;
   static constexpr int LDS_BYTES = 2 * SLOTB;
   static_assert(BQ % 64 == 0 && NW >= 2, "the row statistics of a tile are 64-lane dword copies");
-  using St = typename Base::template Stager<BQ, THREADS>;
-  static_assert(!Base::FragOff::XOR || SLOTB % ROWB == 0, "slot bases keep the fragment offsets' XOR bits");
+  // Fragment and staging addresses (FragOffT, Stager): at d = 256 the
+  // XOR at each read and the periodic staging offsets (with one register
+  // per read offset this kernel spills 80 to 104 bytes inside the loop).
+  static constexpr bool XOR_ADDR = D >= 256;
+  static constexpr bool PERIODIC_STAGE = D >= 256;
+  using FragOff = typename Base::template FragOffT<XOR_ADDR>;
+  using St = typename Base::template Stager<BQ, THREADS, PERIODIC_STAGE>;
+  static_assert(!FragOff::XOR || SLOTB % ROWB == 0, "slot bases keep the fragment offsets' XOR bits");
   // dV and dK accumulators in AGPRs from d = 96 (one wave per SIMD: the
   // arch VGPRs hold the rest; see BwdBase::acc_mfma).
   static constexpr bool ACC_AGPR = D >= 96;
@@ -687,7 +702,7 @@ struct Fa2BwdKV : BwdBase<D, BF16> {
       vf[ks] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     }
 
-    const typename Base::FragOff fo(lane);
+    const FragOff fo(lane);
     const St st(tid);
     const u32x4 wq = rsrc_words(p.q, slice * 2, bytes);
     const u32x4 wdo = rsrc_words(p.dout, slice * 2, bytes);
