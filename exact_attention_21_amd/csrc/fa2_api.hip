@@ -372,6 +372,17 @@ int bwd_slice_group(int bh, int n_tiles, int wgs_per_cu, int mask) {
   return group >= bh ? bh : (int)group;
 }
 
+// Steps per phase of the backward work order (fa2::bwd_work_item): two
+// phases when the slices are grouped and carry key lengths, whose work then
+// differs from slice to slice, so that the grouped order's last groups do not
+// start their long tiles at the end of the launch; one phase otherwise.
+// Measured, same-process A/B: padded causal d = 128 (128 slices) +7.8%;
+// plain causal grids of 128 and 256 slices, where every group has the same
+// work, -1.3% to +0.7%, which one phase keeps.
+int bwd_phase_tiles(int n_tiles, int group, int bh, const int* key_lens) {
+  return key_lens && group < bh ? (n_tiles + 1) / 2 : n_tiles;
+}
+
 // Waves per workgroup of the two backward kernels (32 rows each).
 constexpr int kBwdWaves = 4;
 
@@ -389,11 +400,13 @@ hipError_t launch_bwd(const fa2::BwdParams& base, hipStream_t stream) {
   fa2::BwdParams p = base;
   p.n_tiles = (p.n + KQ::BQ - 1) / KQ::BQ;
   p.group = bwd_slice_group(p.bh, p.n_tiles, sq.per_cu, MASK);
+  p.phase_tiles = bwd_phase_tiles(p.n_tiles, p.group, p.bh, p.key_lens);
   hipLaunchKernelGGL(kq, dim3((unsigned)((int64_t)p.n_tiles * p.bh)), dim3(KQ::THREADS), KQ::LDS_BYTES, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   p.n_tiles = (p.n + KKV::BK - 1) / KKV::BK;
   p.group = bwd_slice_group(p.bh, p.n_tiles, skv.per_cu, MASK);
+  p.phase_tiles = bwd_phase_tiles(p.n_tiles, p.group, p.bh, p.key_lens);
   hipLaunchKernelGGL(kkv, dim3((unsigned)((int64_t)p.n_tiles * p.bh)), dim3(KKV::THREADS), KKV::LDS_BYTES, stream,
                      p);
   return hipGetLastError();

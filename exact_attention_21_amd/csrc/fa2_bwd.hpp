@@ -77,8 +77,9 @@ struct BwdParams {
   void* dv;
   int n;        // sequence length N
   int bh;       // B * H
-  int n_tiles;  // stationary tiles per (batch*head) slice of the kernel launched
-  int group;    // slices per group of the work order (bwd_work_item)
+  int n_tiles;      // stationary tiles per (batch*head) slice of the kernel launched
+  int group;        // slices per group of the work order (bwd_work_item)
+  int phase_tiles;  // steps per phase of the work order (bwd_work_item; n_tiles: one phase)
   float scale;  // softmax scale (any finite value)
   float c2;     // scale * log2(e): scores to the base-2 exponent domain
   // General mask (the forward's): key j is visible to query i iff
@@ -93,23 +94,31 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 
 // Work item of workgroup wg: its (batch*head) slice and its step (tile
-// index, counted from the longest tile under a mask).  The slices are taken
-// in groups of p.group, every tile of a group before the next group, the step
-// varying slowest inside a group: with a group of (a multiple of) 8 slices
-// each XCD (workgroups are dealt to the 8 XCDs round robin) runs the tiles of
-// the same few slices together, so the tiles they stream (K and V, or Q and
-// dO) are read from its L2 instead of HBM (the forward's order, work_item).
+// index, counted from the longest tile under a mask).  The steps are taken in
+// phases of p.phase_tiles (the last may be shorter), every step of a phase
+// before the next phase; inside a phase the slices are taken in groups of
+// p.group, every step of a group before the next group, the step varying
+// slowest inside a group: with a group of (a multiple of) 8 slices each XCD
+// (workgroups are dealt to the 8 XCDs round robin) runs the tiles of the same
+// few slices together, so the tiles they stream (K and V, or Q and dO) are
+// read from its L2 instead of HBM (the forward's order, work_item).  Two
+// phases put the long steps of every group before the short ones, so that
+// the last groups' long tiles do not start at the end of the launch.
 struct BwdItem {
   int bh;
   int step;
 };
 __device__ __forceinline__ BwdItem bwd_work_item(const BwdParams& p, int wg) {
-  const int span = p.group * p.n_tiles;
+  const int phase = wg / (p.bh * p.phase_tiles);
+  const int step0 = phase * p.phase_tiles;
+  wg -= step0 * p.bh;
+  const int steps = min(p.phase_tiles, p.n_tiles - step0);
+  const int span = p.group * steps;
   const int g = wg / span;
   const int r = wg - g * span;
   const int size = min(p.group, p.bh - g * p.group);
   const int step = r / size;
-  return {g * p.group + (r - step * size), step};
+  return {g * p.group + (r - step * size), step0 + step};
 }
 
 // Calls f(std::integral_constant<int, I>{}) for I = B .. E-1 in order: the
@@ -222,18 +231,20 @@ struct BwdBase {
   // LDS byte address of a pointer.
   static __device__ __forceinline__ int addr_of(const lds_char* p) { return (int)(uint32_t)(uintptr_t)p; }
 
-  // Addresses of the fragment reads of a tile at LDS byte address `base` (a
-  // multiple of ROWB: the slots sit at multiples of ROWB from the start of
-  // the kernels' dynamic LDS, address 0, as they declare no static LDS).  Under the XOR chunk permutations (every head dim but
-  // 96) chunk c of a row sits at byte 16 (c ^ f) = 16 c ^ 16 f of it, below
-  // ROWB (a power of two), so the plain read of k-step ks is
-  // plain_off(lane, 0) ^ 32 ks and the transposed read of dims 32 db.. is
-  // tr_off(lane, 0, s) ^ 64 db, each plus the base: three lane offsets and
-  // one XOR at each read, where one register per read offset held through
-  // the loop made the d = 256 dK/dV kernel spill (and each spill reload
-  // waited for the tile loads in flight).  XOR_ = false keeps one offset per
-  // read, for the kernels that fit their registers: there the XORs only cost
-  // issue slots (measured 2.5% to 5% slower at d <= 128).
+  // Addresses of the fragment reads of a tile at LDS byte address `base`, a
+  // multiple of ROWB (the slots sit at multiples of ROWB from the start of
+  // the kernels' dynamic LDS, address 0: they declare no static LDS).
+  // Under the XOR chunk permutations (every head dim but 96) chunk c of a row
+  // sits at byte 16 (c ^ f) = 16 c ^ 16 f of it, below ROWB (a power of
+  // two), so the plain read of k-step ks is plain_off(lane, 0) ^ 32 ks and
+  // the transposed read of dims 32 db.. is tr_off(lane, 0, s) ^ 64 db, each
+  // plus the base.  XOR_ = true: three lane offsets and one XOR at each
+  // read, for the d = 256 dK/dV kernel, which spilled with one register per
+  // read offset held through the loop (and each spill reload waited for the
+  // tile loads in flight).  XOR_ = false: one offset per read, for the
+  // kernels that fit their registers, where the XORs only cost issue slots
+  // (measured 2.5% to 5% slower at d <= 128, 4% to 5% in the d = 256 dQ
+  // kernel).
   template <bool XOR_>
   struct FragOffT {
     static constexpr bool XOR = XOR_ && D != 96;
