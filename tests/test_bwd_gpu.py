@@ -215,29 +215,37 @@ def test_bwd_masked_chained_after_gpu_forward(gpu_device, case):
     _run(case, gpu_device, chained=True, mask=(100, 0, [400, 250][:case[0]]))
 
 
-@pytest.mark.parametrize("padded", [False, True], ids=["causal", "causal_key_lens"])
-def test_bwd_grouped_work_order(gpu_device, padded):
+# (B, H, N, d, key lengths or None, sampled (b, h) pairs)
+GROUPED = [
+    (8, 16, 1100, 64, None, [(0, 0), (2, 9), (5, 3), (7, 15)]),
+    (8, 16, 1100, 64, [1100, 700, 1, 1099, 0, 256, 900, 129], [(0, 0), (2, 9), (5, 3), (7, 15)]),
+    (10, 13, 700, 32, [700, 5, 699, 0, 333, 128, 129, 650, 1, 512], [(0, 0), (4, 7), (9, 11), (9, 12)]),
+]
+
+
+@pytest.mark.parametrize("case", GROUPED, ids=["causal", "causal_key_lens", "key_lens_last_group_of_2"])
+def test_bwd_grouped_work_order(gpu_device, case):
     """Masked grids of 128 slices or more take the work in XCD-sized slice
-    groups, and with key lengths in two phases of steps (9 tiles per slice
-    here: phases of 5 and 4): every element of dQ, dK, dV is written (the
-    outputs start as NaN) and sampled heads from several groups match the
-    oracle."""
-    B, H, N, d, dtype = 8, 16, 1100, 64, wl.FP16
+    groups (8 slices; 130 slices leave a last group of 2), and with key
+    lengths in two phases of steps (9 tiles per slice at N = 1100: phases of
+    5 and 4; 6 at N = 700: 3 and 3): every element of dQ, dK, dV is written
+    (the outputs start as NaN) and sampled heads, from the first and the
+    last groups among others, match the oracle."""
+    B, H, N, d, lens, heads = case
+    dtype = wl.FP16
     w, q, k, v, do = bh.make_case(B, H, N, d, dtype, 9, causal=True)
     sc = w.softmax_scale()
     q64, k64, v64, do64 = (wl.to_float64(x, dtype) for x in (q, k, v, do))
     tq, tk, tv, tdo = (to_device(x, dtype, gpu_device) for x in (q, k, v, do))
-    lens = [1100, 700, 1, 1099, 0, 256, 900, 129]
-    mask = (-1, 0, lens) if padded else None
-    kw = dict(window=(-1, 0), key_lens=torch.tensor(lens, dtype=torch.int32, device=gpu_device)) if padded else \
-        dict(causal=True)
+    mask = (-1, 0, lens) if lens is not None else None
+    kw = dict(window=(-1, 0), key_lens=torch.tensor(lens, dtype=torch.int32, device=gpu_device)) \
+        if lens is not None else dict(causal=True)
     o_t, lse_t = forward(tq, tk, tv, scale=sc, **kw)
     out = tuple(torch.full_like(tq, float("nan")) for _ in range(3))
     dq, dk, dv = backward(tq, tk, tv, o_t, lse_t, tdo, scale=sc, out=out, **kw)
     torch.cuda.synchronize(gpu_device)
     for t in (dq, dk, dv):
         assert bool(torch.isfinite(t.float()).all().item()), "an output tile was not written"
-    heads = [(0, 0), (2, 9), (5, 3), (7, 15)]
     refs, bounds = bh.grad_bounds(q64, k64, v64, do64, bh.to_np(o_t), lse_t.cpu().numpy().astype(np.float64), sc,
                                   True, dtype, heads=heads, mask=mask)
     got = {name: np.stack([bh.to_np(t)[b, h] for b, h in heads]) for name, t in (("dq", dq), ("dk", dk), ("dv", dv))}
