@@ -154,7 +154,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // transposed read already start 12 groups apart.  (Every rule was checked
 // exhaustively for both reads.)  All depend on r only through r%16.
 template <int D>
-__device__ __forceinline__ int bwd_pos(int row, int c) {
+constexpr int bwd_pos(int row, int c) {
   static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "backward head dims");
   if constexpr (D == 32) return c ^ ((row >> 2) & 3);
   if constexpr (D == 64) return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
@@ -162,7 +162,7 @@ __device__ __forceinline__ int bwd_pos(int row, int c) {
   return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
 }
 template <int D>
-__device__ __forceinline__ int bwd_chunk(int row, int p) {
+constexpr int bwd_chunk(int row, int p) {
   if constexpr (D == 96) return (p + 12 - ((row >> 2) & 3)) % 12;
   return bwd_pos<D>(row, p);  // the XOR rules are involutions
 }
@@ -189,7 +189,7 @@ struct BwdBase {
   // .. +7): the A operand [32 rows x 16 dims] of a score product.  Rows of
   // later 32-row blocks are added as immediates (multiples of 16 rows keep
   // the swizzle).
-  static __device__ __forceinline__ int plain_off(int lane, int ks) {
+  static constexpr int plain_off(int lane, int ks) {
     const int row = lane & 31;
     return row * ROWB + (bwd_pos<D>(row, 2 * ks + (lane >> 5)) << 4);
   }
@@ -199,7 +199,7 @@ struct BwdBase {
   // The two reads give the A operand [32 dims x 16 rows] with its k index
   // ordered rows {4h + e, 8 + 4h + e} for lane half h, the order of
   // registers 8u..8u+7 of a score accumulator.
-  static __device__ __forceinline__ int tr_off(int lane, int db, int second) {
+  static constexpr int tr_off(int lane, int db, int second) {
     const int g = lane >> 4;
     const int row = 4 * (g >> 1) + ((lane >> 2) & 3) + 8 * second;
     const int c = 4 * db + 2 * (g & 1) + ((lane & 3) >> 1);
@@ -245,9 +245,21 @@ struct BwdBase {
   // kernels that fit their registers, where the XORs only cost issue slots
   // (measured 2.5% to 5% slower at d <= 128, 4% to 5% in the d = 256 dQ
   // kernel).
+  // The XOR forms, for every lane (checked at compile time where used).
+  static constexpr bool xor_forms_hold() {
+    for (int lane = 0; lane < 64; ++lane) {
+      for (int ks = 0; ks < DK; ++ks)
+        if (plain_off(lane, ks) != (plain_off(lane, 0) ^ (32 * ks))) return false;
+      for (int db = 0; db < DB; ++db)
+        for (int s = 0; s < 2; ++s)
+          if (tr_off(lane, db, s) != (tr_off(lane, 0, s) ^ (64 * db))) return false;
+    }
+    return 32 * (DK - 1) < ROWB && 64 * (DB - 1) < ROWB;
+  }
   template <bool XOR_>
   struct FragOffT {
     static constexpr bool XOR = XOR_ && D != 96;
+    static_assert(!XOR || xor_forms_hold(), "fragment offsets are a lane base XOR a constant");
     int p0, t0, t1;
     int pk[XOR ? 1 : DK], tk[XOR ? 1 : DB][2];
     __device__ __forceinline__ explicit FragOffT(int lane) {
@@ -308,14 +320,22 @@ struct BwdBase {
     static constexpr int PER = PER0 < CPT ? PER0 : CPT;
     int goff[PER];  // global byte offset within the tile of slots 0 .. PER-1
     int lds0;       // this wave's first slot (bytes)
+    static constexpr int slot_off(int tid, int j) {
+      const int s = tid + T * j;
+      const int row = s / CPR;
+      return (row * D + bwd_chunk<D>(row, s % CPR) * 8) * 2;
+    }
+    // The period, for every thread (checked at compile time).
+    static constexpr bool period_holds() {
+      for (int tid = 0; tid < T; ++tid)
+        for (int j = 0; j < CPT; ++j)
+          if (slot_off(tid, j) != slot_off(tid, j % PER) + (j - j % PER) * RJ * ROWB) return false;
+      return true;
+    }
+    static_assert(RJ == 0 || period_holds(), "staging offsets repeat every PER slots up to whole rows");
     __device__ __forceinline__ Stager(int tid) {
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int s = tid + T * j;
-        const int row = s / CPR;
-        const int c = bwd_chunk<D>(row, s % CPR);
-        goff[j] = (row * D + c * 8) * 2;
-      }
+      for (int j = 0; j < PER; ++j) goff[j] = slot_off(tid, j);
       lds0 = (tid & ~63) * 16;
     }
     // Tile of rows r0.. into LDS at dst.  The row term stays in the VGPR
