@@ -176,7 +176,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the forward pass has no cross-GPU step in this build)", file=sys.stderr)
+              "(the library runs on one GPU: a larger job would give each GPU its own heads, "
+              "with no exchange between GPUs)", file=sys.stderr)
         return 2
 
     import torch
