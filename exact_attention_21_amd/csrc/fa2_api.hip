@@ -45,8 +45,11 @@ struct TileCfg {
 // Two waves per SIMD let one wave's softmax issue beside the other's MFMAs.
 // d = 32, 64 and 128 have two forms.  The 8-wave form runs one workgroup per
 // CU (two waves per SIMD): at d = 32 and 64 in two split-KV groups of 4
-// waves, at d = 128 as 8 waves of 32 rows on one K/V stream (64 rows per
-// wave, 4 waves, measured 8% slower).  The 4-wave form runs two workgroups
+// waves, at d = 128 as 8 waves of 32 rows on one K/V stream, except without
+// a mask, where 4 waves of 64 rows (two query blocks per wave, one wave per
+// SIMD, the same 256 rows) share each K/V fragment between two blocks:
+// +2% to +3% on unmasked grids of one and two rounds, -1% to +0.4% causal,
+// -1.4% on the padded batch (same-process A/B).  The 4-wave form runs two workgroups
 // per CU on one K/V stream each, which hide each other's prologue and
 // epilogue (choose_eight picks by grid size).  At d = 32 and 64 both forms
 // cover the same rows; the 4-wave form of d = 128 covers 128 rows instead of
@@ -56,11 +59,11 @@ struct TileCfg {
 // (96 KiB) fits the LDS.
 constexpr bool has_two_forms(int64_t d) { return d == 32 || d == 64 || d == 128; }
 
-constexpr TileCfg cfg_for(int64_t d, bool eight = true) {
+constexpr TileCfg cfg_for(int64_t d, bool eight = true, bool unmasked = false) {
   return d == 32    ? (eight ? TileCfg{64, 8, 1, 2} : TileCfg{64, 4, 1, 1})
          : d == 64  ? (eight ? TileCfg{32, 8, 2, 2} : TileCfg{32, 4, 2, 1})
          : d == 96  ? TileCfg{64, 4, 1, 1}
-         : d == 128 ? (eight ? TileCfg{32, 8, 1, 1} : TileCfg{32, 4, 1, 1})
+         : d == 128 ? (eight ? (unmasked ? TileCfg{32, 4, 2, 1} : TileCfg{32, 8, 1, 1}) : TileCfg{32, 4, 1, 1})
                     : TileCfg{32, 4, 1, 1};
 }
 
@@ -69,6 +72,13 @@ using KernelFor = fa2::Fa2Fwd<D, cfg_for(D, EIGHT).bc, cfg_for(D, EIGHT).nw, cfg
                               cfg_for(D, EIGHT).kvg, false, false>;
 static_assert(KernelFor<32, false>::BR == KernelFor<32>::BR && KernelFor<64, false>::BR == KernelFor<64>::BR,
               "both forms of d = 32 and 64 cover the same rows");
+// The unmasked 8-wave-grid form of d = 128 covers the rows, and takes the
+// LDS, of the 8-wave form.
+using KernelFor128Unmasked = fa2::Fa2Fwd<128, cfg_for(128, true, true).bc, cfg_for(128, true, true).nw,
+                                         cfg_for(128, true, true).qb, cfg_for(128, true, true).kvg, false, false>;
+static_assert(KernelFor128Unmasked::BR == KernelFor<128>::BR &&
+                  KernelFor128Unmasked::LDS_BYTES == KernelFor<128>::LDS_BYTES,
+              "both forms of the d = 128 8-wave grid cover the same rows in the same LDS");
 // Head dims 512 and 1024 run the chunked kernel (fa2_wide.hpp).
 template <int D>
 using WideFor = fa2::Fa2Wide<D, false, fa2::kMaskNone>;
@@ -88,8 +98,8 @@ constexpr int lds_bytes_for(int64_t d, bool eight = true) {
          : d == 256 ? KernelFor<256>::LDS_BYTES : d == 512 ? WideFor<512>::LDS_BYTES : WideFor<1024>::LDS_BYTES;
 }
 
-constexpr int threads_for(int64_t d, bool eight = true) {
-  return d == 512 ? WideFor<512>::THREADS : d == 1024 ? WideFor<1024>::THREADS : cfg_for(d, eight).nw * 64;
+constexpr int threads_for(int64_t d, bool eight = true, bool unmasked = false) {
+  return d == 512 ? WideFor<512>::THREADS : d == 1024 ? WideFor<1024>::THREADS : cfg_for(d, eight, unmasked).nw * 64;
 }
 
 // Compute units of the current device (256, MI355X's count, when no device
@@ -124,7 +134,8 @@ int device_cus() {
 //   d = 128 (8-wave grid in workgroups per CU): no mask, the 4-wave form +27%
 //     at 0.5, -6% at 1 (three shapes) and -5% at 2; causal, +16% to +38% at
 //     0.5 and 1 (four shapes), -1% at 1.5, -6% at 2.  The general mask keeps
-//     the 8-wave form (not measured).
+//     the 8-wave form (not measured).  (Without a mask the 8-wave choice runs
+//     the 64-row-wave form, see cfg_for; these figures predate it.)
 bool choose_eight(int64_t d, int64_t grid, int mask, int dtype) {
   if (!has_two_forms(d)) return true;
   if (d == 128) {
@@ -239,7 +250,7 @@ KernelSetup kernel_setup(const void* kern, int threads, int lds) {
 template <int D, int BC, int NW, int QB, int KVG, bool BF16, int MASK>
 hipError_t launch(const fa2::Params& p, int64_t grid, hipStream_t stream) {
   constexpr int lds = fa2::Fa2Fwd<D, BC, NW, QB, KVG, BF16, MASK>::LDS_BYTES;
-  static_assert(lds == lds_bytes_for(D, NW == 8 || !has_two_forms(D)), "LDS size");
+  static_assert(lds == lds_bytes_for(D, true) || lds == lds_bytes_for(D, false), "LDS size");
   auto kern = fa2::fa2_fwd_kernel<D, BC, NW, QB, KVG, BF16, MASK>;
   const KernelSetup k = kernel_setup<fa2::Fa2Fwd<D, BC, NW, QB, KVG, BF16, MASK>>((const void*)kern, NW * 64, lds);
   if (k.err != hipSuccess) return k.err;
@@ -269,7 +280,7 @@ hipError_t launch_d(const fa2::Params& p, int64_t grid, hipStream_t stream, bool
   } else if constexpr (D >= 512) {
     return launch_wide<D, BF16, MASK>(p, grid, stream);
   } else if constexpr (has_two_forms(D)) {
-    constexpr TileCfg s = cfg_for(D, true), u = cfg_for(D, false);
+    constexpr TileCfg s = cfg_for(D, true, MASK == fa2::kMaskNone), u = cfg_for(D, false);
     return eight ? launch<D, s.bc, s.nw, s.qb, s.kvg, BF16, MASK>(p, grid, stream)
                  : launch<D, u.bc, u.nw, u.qb, u.kvg, BF16, MASK>(p, grid, stream);
   } else {
@@ -571,10 +582,10 @@ fa2_status_t fa2_launch_info(int64_t B, int64_t H, int64_t N, int64_t d, int is_
   const fa2_status_t st = check_shape(B, H, N, d, dtype, &grid);
   if (st != FA2_OK) return st;
   const bool eight = choose_eight(d, grid, is_causal ? fa2::kMaskCausal : fa2::kMaskNone, dtype);
-  const TileCfg c = cfg_for(d, eight);
+  const TileCfg c = cfg_for(d, eight, !is_causal);
   grid = (N + ::rows_per_wg(d, eight) - 1) / ::rows_per_wg(d, eight) * (B * H);
   if (workgroups) *workgroups = grid;
-  if (threads) *threads = threads_for(d, eight);
+  if (threads) *threads = threads_for(d, eight, !is_causal);
   if (rows_per_wg) *rows_per_wg = ::rows_per_wg(d, eight);
   if (keys_per_tile) *keys_per_tile = c.bc;
   if (lds_bytes) *lds_bytes = lds_bytes_for(d, eight);

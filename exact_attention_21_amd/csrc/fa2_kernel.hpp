@@ -237,8 +237,9 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 //                      0: the checked pipeline only.
 //   FA2_SPLIT_KV       1: two split-KV wave groups at d = 32 and 64 (host side);
 //                      0: one group of 4 waves.
-//   FA2_W4_TWO_PER_SIMD 1: the 4-wave forms of d = 64 and 128 held to two
-//                      waves per SIMD (256 registers); 0: no register bound.
+//   FA2_W4_TWO_PER_SIMD 1: the 4-wave forms of d = 64 and of d = 128 with one
+//                      query block per wave held to two waves per SIMD (256
+//                      registers); 0: no register bound.
 //   FA2_XCD_GROUPS     1: slices taken in groups whose query tiles fill one
 //                      round of an XCD's resident workgroups (host side, see
 //                      work_item); k: k rounds; 0: one group of all slices.
@@ -1366,7 +1367,7 @@ struct Fa2Fwd {
 // workgroup (8 waves, or LDS- and register-bound d = 96 and 256).
 template <int D, int BC, int NW, int QB, int KVG, bool BF16, int MASK>
 __global__ void __launch_bounds__(NW * 64)
-    __attribute__((amdgpu_waves_per_eu((FA2_W4_TWO_PER_SIMD && NW == 4 && (D == 64 || D == 128)) ? 2 : 1)))
+    __attribute__((amdgpu_waves_per_eu((FA2_W4_TWO_PER_SIMD && NW == 4 && (D == 64 || (D == 128 && QB == 1))) ? 2 : 1)))
     fa2_fwd_kernel(const Params p) {
   extern __shared__ __attribute__((aligned(16))) char lds_generic[];
   Fa2Fwd<D, BC, NW, QB, KVG, BF16, MASK>::run(

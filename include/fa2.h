@@ -226,10 +226,11 @@ const char* fa2_status_string(int status);
  * launching.  Writes the number of workgroups, threads per workgroup, query
  * rows per workgroup, keys per tile and LDS bytes per workgroup.  Returns the
  * status fa2_fwd would return from its argument checks (pointers are not
- * examined).  Any output pointer may be NULL.  For d = 32 and 64 the form of
- * the launch (threads, LDS bytes) depends on how many workgroups the grid
- * gives each compute unit of the current device (queried once per device;
- * 256 compute units are assumed when no device can be queried).
+ * examined).  Any output pointer may be NULL.  For d = 32, 64 and 128 the
+ * form of the launch (threads, rows, LDS bytes) depends on how many
+ * workgroups the grid gives each compute unit of the current device (queried
+ * once per device; 256 compute units are assumed when no device can be
+ * queried), and at d = 128 also on the mask.
  */
 fa2_status_t fa2_launch_info(int64_t B, int64_t H, int64_t N, int64_t d, int is_causal, int dtype,
                              int64_t* workgroups, int* threads, int* rows_per_wg,

@@ -110,32 +110,33 @@ def test_launch_info_headline_shape():
 # the library assumes 256 compute units, so the grid sizes below are 1, 2 and
 # 3 workgroups per CU (256 query rows per workgroup at d = 64, 128 at d = 32)
 # and, for d = 128, 0.5 to 4 workgroups of the 8-wave form per CU (256 rows).
+# (B, H, N, d, is_causal, dtype), threads, query rows per workgroup
 FORM_CHOICES = [
-    ((1, 8, 8192, 64, 0, 0), 512),  # no mask, one per CU: split-KV
-    ((2, 8, 8192, 64, 0, 0), 256),  # no mask, two per CU: 4-wave
-    ((2, 8, 8192, 64, 0, 1), 256),
-    ((2, 8, 8192, 64, 1, 0), 512),  # fp16 causal d = 64 keeps split-KV at two per CU
-    ((3, 8, 8192, 64, 1, 0), 256),  # and takes the 4-wave form from three
-    ((1, 8, 8192, 64, 1, 1), 256),  # bf16 d = 64 under a mask: 4-wave at every grid size
-    ((1, 2, 300, 64, 1, 1), 256),
-    ((1, 8, 4096, 32, 1, 0), 512),  # d = 32 causal, one per CU: split-KV
-    ((2, 8, 4096, 32, 1, 0), 256),  # two per CU: 4-wave
-    ((4, 8, 8192, 128, 1, 1), 512),  # d = 128, four 8-wave workgroups per CU: 8 waves
-    ((1, 8, 8192, 128, 0, 0), 512),  # no mask, one per CU: 8 waves
-    ((1, 16, 4096, 128, 1, 1), 256),  # causal, one per CU: 4 waves
-    ((1, 32, 1024, 128, 0, 0), 256),  # no mask, half a round: 4 waves
-    ((2, 16, 4096, 128, 1, 0), 512),  # causal, two per CU: 8 waves
+    ((1, 8, 8192, 64, 0, 0), 512, 256),  # no mask, one per CU: split-KV
+    ((2, 8, 8192, 64, 0, 0), 256, 256),  # no mask, two per CU: 4-wave
+    ((2, 8, 8192, 64, 0, 1), 256, 256),
+    ((2, 8, 8192, 64, 1, 0), 512, 256),  # fp16 causal d = 64 keeps split-KV at two per CU
+    ((3, 8, 8192, 64, 1, 0), 256, 256),  # and takes the 4-wave form from three
+    ((1, 8, 8192, 64, 1, 1), 256, 256),  # bf16 d = 64 under a mask: 4-wave at every grid size
+    ((1, 2, 300, 64, 1, 1), 256, 256),
+    ((1, 8, 4096, 32, 1, 0), 512, 128),  # d = 32 causal, one per CU: split-KV
+    ((2, 8, 4096, 32, 1, 0), 256, 128),  # two per CU: 4-wave
+    ((4, 8, 8192, 128, 1, 1), 512, 256),  # d = 128 causal, four 8-wave workgroups per CU: 8 waves
+    ((1, 8, 8192, 128, 0, 0), 256, 256),  # no mask, one per CU: 4 waves of 64 rows
+    ((4, 8, 8192, 128, 0, 1), 256, 256),  # no mask, four per CU: 4 waves of 64 rows
+    ((1, 16, 4096, 128, 1, 1), 256, 128),  # causal, one per CU: 4 waves of 32 rows
+    ((1, 32, 1024, 128, 0, 0), 256, 128),  # no mask, half a round: 4 waves of 32 rows
+    ((2, 16, 4096, 128, 1, 0), 512, 256),  # causal, two per CU: 8 waves
 ]
 
 
-@pytest.mark.parametrize("args,threads", FORM_CHOICES, ids=[str(a) for a, _ in FORM_CHOICES])
-def test_launch_form_choice_without_gpu(args, threads):
+@pytest.mark.parametrize("args,threads,rows", FORM_CHOICES, ids=[str(a) for a, _, _ in FORM_CHOICES])
+def test_launch_form_choice_without_gpu(args, threads, rows):
     info = fa.fa2_launch_info(*args)
     assert info["threads"] == threads
+    assert info["rows_per_wg"] == rows
     B, H, N = args[:3]
     assert info["workgroups"] == B * H * math.ceil(N / info["rows_per_wg"])
-    if args[3] == 128:  # the 4-wave form of d = 128 covers 128 rows
-        assert info["rows_per_wg"] == (256 if threads == 512 else 128)
 
 
 @pytest.mark.parametrize("d", [32, 64, 96, 128, 256, 512, 1024])

@@ -241,19 +241,20 @@ D128_FORMS = [(c, dt) for c in (False, True) for dt in (wl.FP16, wl.BF16)]
                          ids=[f"{dt}-{'causal' if c else 'full'}" for c, dt in D128_FORMS])
 def test_d128_both_forms(gpu_device, causal, dtype):
     """d = 128 runs 4 waves of 32 rows (128 rows, two workgroups per CU) on
-    grids of at most one 8-wave workgroup per CU, and 8 waves (256 rows)
-    beyond: parity of both forms, every element on the small grid, sampled
-    rows on the large one."""
+    grids of at most one 8-wave workgroup per CU, and 256 rows beyond: 8
+    waves of 32 rows under a mask, 4 waves of 64 rows without one.  Parity
+    of every form, every element on the small grid, sampled rows on the
+    large one."""
     import exact_attention_21_amd as fa
     dt = 1 if dtype == wl.BF16 else 0
-    for B, H, N, threads in ((1, 4, 700, 256), (4, 32, 2000, 512)):
+    for B, H, N, threads, rows_per_wg in ((1, 4, 700, 256, 128), (4, 32, 2000, 512 if causal else 256, 256)):
         info = fa.fa2_launch_info(B, H, N, 128, int(causal), dt)
-        assert info["threads"] == threads, (B, H, N, info)
+        assert (info["threads"], info["rows_per_wg"]) == (threads, rows_per_wg), (B, H, N, info)
         w = wl.Workload("f128", B, H, N, 128, dtype, causal)
         q, k, v = wl.make_inputs(w, seed=23)
         o, lse = run_gpu(q, k, v, dtype, w.softmax_scale(), causal, gpu_device)
-        rows = np.arange(N) if threads == 256 else sampled_rows(N, seed=5, edge=32, inner=32)
+        rows = np.arange(N) if rows_per_wg == 128 else sampled_rows(N, seed=5, edge=32, inner=32)
         o_ref, lse_ref = attention_ref(*(wl.to_float64(x, dtype) for x in (q, k, v)), w.softmax_scale(), causal,
                                        rows=rows)
         assert_close(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, dtype,
-                     f"d128 {threads // 64}-wave form {dtype} causal={causal}")
+                     f"d128 {threads // 64}-wave {rows_per_wg}-row form {dtype} causal={causal}")
