@@ -17,7 +17,7 @@
 #include "fa2_kernel.hpp"
 #include "fa2_wide.hpp"
 
-// Head dims compiled into this build: a bit mask (bit 0: d = 32, then 64, 96,
+// Head dims compiled into the library: a bit mask (bit 0: d = 32, then 64, 96,
 // 128, 256, 512, 1024), all of them unless FA2_DIMS says otherwise.  Builds of
 // the library with a design switch flipped, made to measure that switch,
 // compile only the head dims they are measured on; a head dim left out is
